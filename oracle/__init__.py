@@ -1,0 +1,133 @@
+"""Float64 CPU oracle for Kimi Delta Attention (test infrastructure only).
+
+TEST INFRASTRUCTURE: only tests/, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The HIP library never loads it and
+shares no code with it.  See kda_oracle.c for the recurrence it computes and
+where it comes from (fireworks.ai, "Kimi K3 on Fireworks: Fast RL at frontier
+scale", section on Kimi Delta Attention).
+
+Pins: every function here is checked in tests/test_oracle_pins.py against
+facts that do not come from this code (closed forms, brute-force products of
+explicit transition matrices, invariants, finite differences, autograd).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH, extra=()) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-std=c99", *extra, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.kda_oracle_fwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, ctypes.c_double, P, P, P, I, I]
+    lib.kda_oracle_fwd.restype = I
+    lib.kda_oracle_bwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, ctypes.c_double, P, P,
+                                   P, P, P, P, P, P, P, I, I]
+    lib.kda_oracle_bwd.restype = I
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle; build it only if it is not there."""
+    global _lib
+    if path is not None:
+        return _bind(path)
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _units(units):
+    if units is None:
+        return None, 0
+    u = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+    return u, u.shape[0]
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def kda_fwd(q, k, v, log_alpha, beta, cu_seqlens, init_state=None, scale=None,
+            units=None, nthreads=None, lib=None):
+    """o[n_tok,H,dv], final_state[N,H,dk,dv] in float64.
+
+    q,k,log_alpha [n_tok,H,dk]; v [n_tok,H,dv]; beta [n_tok,H]; cu_seqlens [N+1].
+    scale=None means dk**-0.5.  units: iterable of (seq, head) to compute (others stay NaN).
+    """
+    lib = lib or load()
+    q, k, v, log_alpha, beta, init_state = map(_f64, (q, k, v, log_alpha, beta, init_state))
+    n_tok, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ns = cu.shape[0] - 1
+    if scale is None:
+        scale = dk ** -0.5
+    out = np.full((n_tok, H, dv), np.nan)
+    fin = np.full((ns, H, dk, dv), np.nan)
+    u, nu = _units(units)
+    rc = lib.kda_oracle_fwd(H, dk, dv, ns, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                            _ptr(init_state), float(scale), _ptr(out), _ptr(fin), _ptr(u), nu,
+                            nthreads or default_threads())
+    if rc:
+        raise RuntimeError(f"kda_oracle_fwd failed: {rc}")
+    return out, fin
+
+
+def kda_bwd(q, k, v, log_alpha, beta, cu_seqlens, d_out, init_state=None, d_final_state=None,
+            scale=None, units=None, nthreads=None, lib=None):
+    """Gradients (dq, dk, dv, dlog_alpha, dbeta, d_init_state) in float64."""
+    lib = lib or load()
+    q, k, v, log_alpha, beta, init_state, d_out, d_final_state = map(
+        _f64, (q, k, v, log_alpha, beta, init_state, d_out, d_final_state))
+    n_tok, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ns = cu.shape[0] - 1
+    if scale is None:
+        scale = dk ** -0.5
+    dq = np.full((n_tok, H, dk), np.nan)
+    dkk = np.full((n_tok, H, dk), np.nan)
+    dvv = np.full((n_tok, H, dv), np.nan)
+    dla = np.full((n_tok, H, dk), np.nan)
+    db = np.full((n_tok, H), np.nan)
+    dinit = np.full((ns, H, dk, dv), np.nan)
+    u, nu = _units(units)
+    rc = lib.kda_oracle_bwd(H, dk, dv, ns, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                            _ptr(init_state), float(scale), _ptr(d_out), _ptr(d_final_state),
+                            _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dla), _ptr(db), _ptr(dinit), _ptr(u), nu,
+                            nthreads or default_threads())
+    if rc:
+        raise RuntimeError(f"kda_oracle_bwd failed: {rc}")
+    return dq, dkk, dvv, dla, db, dinit

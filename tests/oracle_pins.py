@@ -1,0 +1,328 @@
+"""Pins for the float64 oracle: facts that hold independently of its code.
+
+Each pin takes a loaded oracle library (so the mutation test can run the same
+pins against deliberately broken builds of the oracle) and raises
+AssertionError when the oracle disagrees with the fact.
+
+The recurrence being pinned (fireworks.ai, "Kimi K3 on Fireworks", section on
+Kimi Delta Attention; channel-wise gated delta rule):
+    S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,  o_t = scale S_t^T q_t.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+RNG_SEED = 20261202
+
+
+def _rand_case(rng, lengths, H, dk, dv, unit_k=True, gate=(2.0, 1.0), init_sd=0.5):
+    n = int(sum(lengths))
+    q = rng.standard_normal((n, H, dk))
+    k = rng.standard_normal((n, H, dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((n, H, dv))
+    x = rng.normal(gate[0], gate[1], (n, H, dk))
+    la = -np.logaddexp(0.0, -x)
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((n, H))))
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    init = rng.standard_normal((len(lengths), H, dk, dv)) * init_sd
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, cu_seqlens=cu, init_state=init)
+
+
+def _fwd(lib, c, **kw):
+    args = dict(c)
+    args.update(kw)
+    return oracle.kda_fwd(args["q"], args["k"], args["v"], args["log_alpha"], args["beta"], args["cu_seqlens"],
+                          init_state=args.get("init_state"), scale=args.get("scale"), nthreads=2, lib=lib)
+
+
+def _close(a, b, tol, what):
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    ref = max(np.max(np.abs(b)) if b.size else 0.0, 1e-300)
+    assert err <= tol * max(ref, 1.0), f"{what}: max err {err:.3e} (ref max {ref:.3e})"
+
+
+# ---------------------------------------------------------------------------
+# forward pins
+# ---------------------------------------------------------------------------
+def pin_identity_when_no_write_no_decay(lib):
+    """beta=0 and alpha=1: the state never changes, o_t = scale S_0^T q_t."""
+    rng = np.random.default_rng(RNG_SEED)
+    c = _rand_case(rng, [7, 0, 12], H=2, dk=5, dv=3)
+    c["beta"][:] = 0.0
+    c["log_alpha"][:] = 0.0
+    o, fin = _fwd(lib, c, scale=0.7)
+    _close(fin, c["init_state"], 1e-14, "final_state")
+    cu = c["cu_seqlens"]
+    for s in range(len(cu) - 1):
+        for t in range(cu[s], cu[s + 1]):
+            for h in range(2):
+                ref = 0.7 * c["init_state"][s, h].T @ c["q"][t, h]
+                _close(o[t, h], ref, 1e-14, "output")
+
+
+def pin_unit_key_replaces_component(lib):
+    """alpha=1, beta=1, one unit key: k^T S_1 = v^T and u^T S_1 = u^T S_0 for u orthogonal to k."""
+    rng = np.random.default_rng(RNG_SEED + 1)
+    dk, dv = 6, 4
+    c = _rand_case(rng, [1], H=1, dk=dk, dv=dv)
+    c["beta"][:] = 1.0
+    c["log_alpha"][:] = 0.0
+    _, fin = _fwd(lib, c)
+    S1, S0 = fin[0, 0], c["init_state"][0, 0]
+    kk = c["k"][0, 0]
+    _close(kk @ S1, c["v"][0, 0], 1e-13, "k^T S_1")
+    for _ in range(3):
+        u = rng.standard_normal(dk)
+        u -= (u @ kk) * kk
+        _close(u @ S1, u @ S0, 1e-13, "u^T S_1")
+
+
+def _brute_force(c, scale):
+    """Unrolled products of explicit dk x dk transition matrices."""
+    q, k, v, la, beta, cu, init = (c[x] for x in ("q", "k", "v", "log_alpha", "beta", "cu_seqlens", "init_state"))
+    n, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((n, H, dv))
+    fin = np.zeros((len(cu) - 1, H, dk, dv))
+    I = np.eye(dk)
+    for s in range(len(cu) - 1):
+        for h in range(H):
+            ts = list(range(cu[s], cu[s + 1]))
+            Ms = [(I - beta[t, h] * np.outer(k[t, h], k[t, h])) @ np.diag(np.exp(la[t, h])) for t in ts]
+            for i in range(len(ts) + 1):
+                # S after i tokens = (M_i ... M_1) S_0 + sum_{j<=i} (M_i ... M_{j+1}) b_j k_j v_j^T
+                prod = I.copy()
+                for M in Ms[:i]:
+                    prod = M @ prod
+                S = prod @ init[s, h]
+                for j in range(i):
+                    tail = I.copy()
+                    for M in Ms[j + 1:i]:
+                        tail = M @ tail
+                    t = ts[j]
+                    S = S + tail @ (beta[t, h] * np.outer(k[t, h], v[t, h]))
+                if i > 0:
+                    o[ts[i - 1], h] = scale * S.T @ q[ts[i - 1], h]
+                if i == len(ts):
+                    fin[s, h] = S
+    return o, fin
+
+
+def pin_brute_force_products(lib):
+    """T<=8: oracle == explicit products of (I - b k k^T) Diag(a), unnormalised keys, dk != dv."""
+    rng = np.random.default_rng(RNG_SEED + 2)
+    c = _rand_case(rng, [8, 3, 1], H=2, dk=5, dv=3, unit_k=False, gate=(0.5, 1.0))
+    o, fin = _fwd(lib, c, scale=0.37)
+    ob, fb = _brute_force(c, 0.37)
+    _close(o, ob, 1e-12, "outputs")
+    _close(fin, fb, 1e-12, "final_state")
+
+
+def pin_pure_decay(lib):
+    """beta=0: S_t = Diag(exp(sum_{s<=t} log a_s)) S_0 exactly (up to rounding)."""
+    rng = np.random.default_rng(RNG_SEED + 3)
+    c = _rand_case(rng, [40], H=1, dk=4, dv=3, gate=(1.0, 2.0))
+    c["beta"][:] = 0.0
+    o, fin = _fwd(lib, c)
+    g = np.cumsum(c["log_alpha"][:, 0, :], axis=0)
+    S0 = c["init_state"][0, 0]
+    for t in range(40):
+        St = np.exp(g[t])[:, None] * S0
+        _close(o[t, 0], 0.5 * St.T @ c["q"][t, 0], 1e-12, "decay output")
+    _close(fin[0, 0], np.exp(g[-1])[:, None] * S0, 1e-12, "decay final")
+
+
+def pin_orthonormal_keys_projection(lib):
+    """alpha=1, beta=1, orthonormal keys: S_T = (I - sum k k^T) S_0 + sum k v^T."""
+    rng = np.random.default_rng(RNG_SEED + 4)
+    dk, dv, T = 8, 5, 6
+    c = _rand_case(rng, [T], H=1, dk=dk, dv=dv)
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    c["k"][:, 0, :] = Qm[:, :T].T
+    c["beta"][:] = 1.0
+    c["log_alpha"][:] = 0.0
+    _, fin = _fwd(lib, c)
+    K = c["k"][:, 0, :]
+    ref = (np.eye(dk) - K.T @ K) @ c["init_state"][0, 0] + K.T @ c["v"][:, 0, :]
+    _close(fin[0, 0], ref, 1e-13, "projection")
+
+
+def pin_linearity(lib):
+    """(S_0, V) -> (o, S_T) is linear for fixed q, k, alpha, beta."""
+    rng = np.random.default_rng(RNG_SEED + 5)
+    c1 = _rand_case(rng, [9, 4], H=2, dk=4, dv=3)
+    c2 = dict(c1)
+    c2["v"] = rng.standard_normal(c1["v"].shape)
+    c2["init_state"] = rng.standard_normal(c1["init_state"].shape)
+    a, b = 0.3, -1.7
+    c3 = dict(c1)
+    c3["v"] = a * c1["v"] + b * c2["v"]
+    c3["init_state"] = a * c1["init_state"] + b * c2["init_state"]
+    o1, f1 = _fwd(lib, c1)
+    o2, f2 = _fwd(lib, c2)
+    o3, f3 = _fwd(lib, c3)
+    _close(o3, a * o1 + b * o2, 1e-12, "linear outputs")
+    _close(f3, a * f1 + b * f2, 1e-12, "linear state")
+
+
+def pin_value_columns_separate(lib):
+    """Each value column (and state column) evolves on its own."""
+    rng = np.random.default_rng(RNG_SEED + 6)
+    c = _rand_case(rng, [11], H=1, dk=4, dv=5)
+    o, f = _fwd(lib, c)
+    cols = [0, 3]
+    c2 = dict(c)
+    c2["v"] = np.ascontiguousarray(c["v"][:, :, cols])
+    c2["init_state"] = np.ascontiguousarray(c["init_state"][..., cols])
+    o2, f2 = _fwd(lib, c2)
+    _close(o2, o[:, :, cols], 1e-13, "column outputs")
+    _close(f2, f[..., cols], 1e-13, "column state")
+
+
+def pin_chaining(lib):
+    """Running [0,t) then [t,T) from the carried state equals one run."""
+    rng = np.random.default_rng(RNG_SEED + 7)
+    c = _rand_case(rng, [23], H=2, dk=4, dv=3)
+    o, f = _fwd(lib, c)
+    t = 9
+    a = {k_: (v_[:t] if k_ in ("q", "k", "v", "log_alpha", "beta") else v_) for k_, v_ in c.items()}
+    a["cu_seqlens"] = np.array([0, t], np.int32)
+    oa, fa = _fwd(lib, a)
+    b = {k_: (v_[t:] if k_ in ("q", "k", "v", "log_alpha", "beta") else v_) for k_, v_ in c.items()}
+    b["cu_seqlens"] = np.array([0, 23 - t], np.int32)
+    b["init_state"] = fa
+    ob, fb = _fwd(lib, b)
+    _close(np.concatenate([oa, ob]), o, 1e-13, "chained outputs")
+    _close(fb, f, 1e-13, "chained state")
+
+
+def pin_varlen_is_separate_runs(lib):
+    """A packed batch equals each sequence run alone (zero-length keeps its init)."""
+    rng = np.random.default_rng(RNG_SEED + 8)
+    lens = [5, 0, 13, 1]
+    c = _rand_case(rng, lens, H=2, dk=4, dv=3)
+    o, f = _fwd(lib, c)
+    cu = c["cu_seqlens"]
+    for s in range(len(lens)):
+        sl = slice(cu[s], cu[s + 1])
+        one = {k_: (v_[sl] if k_ in ("q", "k", "v", "log_alpha", "beta") else v_) for k_, v_ in c.items()}
+        one["cu_seqlens"] = np.array([0, lens[s]], np.int32)
+        one["init_state"] = c["init_state"][s:s + 1]
+        os_, fs = _fwd(lib, one)
+        _close(os_, o[sl], 1e-14, f"seq {s} outputs")
+        _close(fs[0], f[s], 1e-14, f"seq {s} state")
+    _close(f[1], c["init_state"][1], 0.0, "zero-length sequence keeps init")
+
+
+def pin_non_expansive(lib):
+    """Unit keys, beta in [0,1], alpha<=1: ||S_T||_F <= ||S_0||_F + sum_t b_t ||v_t||."""
+    rng = np.random.default_rng(RNG_SEED + 9)
+    c = _rand_case(rng, [200], H=2, dk=6, dv=4, gate=(0.0, 3.0), init_sd=2.0)
+    for T in (1, 17, 200):
+        cc = {k_: (v_[:T] if k_ in ("q", "k", "v", "log_alpha", "beta") else v_) for k_, v_ in c.items()}
+        cc["cu_seqlens"] = np.array([0, T], np.int32)
+        _, f = _fwd(lib, cc)
+        for h in range(2):
+            bound = np.linalg.norm(c["init_state"][0, h]) + np.sum(
+                c["beta"][:T, h] * np.linalg.norm(c["v"][:T, h], axis=-1))
+            assert np.linalg.norm(f[0, h]) <= bound * (1 + 1e-12), "state norm grew beyond the bound"
+
+
+FORWARD_PINS = [pin_identity_when_no_write_no_decay, pin_unit_key_replaces_component, pin_brute_force_products,
+                pin_pure_decay, pin_orthonormal_keys_projection, pin_linearity, pin_value_columns_separate,
+                pin_chaining, pin_varlen_is_separate_runs, pin_non_expansive]
+
+
+# ---------------------------------------------------------------------------
+# backward pins
+# ---------------------------------------------------------------------------
+def _loss(lib, c, dO, dS, scale):
+    o, f = oracle.kda_fwd(c["q"], c["k"], c["v"], c["log_alpha"], c["beta"], c["cu_seqlens"],
+                          init_state=c["init_state"], scale=scale, nthreads=1, lib=lib)
+    return float(np.sum(o * dO) + np.sum(f * dS))
+
+
+def pin_backward_finite_differences(lib):
+    """Every gradient equals central differences of L = <dO, o> + <dS_final, S_T>."""
+    rng = np.random.default_rng(RNG_SEED + 10)
+    c = _rand_case(rng, [6, 0, 4], H=2, dk=3, dv=2, unit_k=False, gate=(1.0, 1.0))
+    scale = 0.6
+    dO = rng.standard_normal(c["v"].shape)
+    dS = rng.standard_normal(c["init_state"].shape)
+    g = oracle.kda_bwd(c["q"], c["k"], c["v"], c["log_alpha"], c["beta"], c["cu_seqlens"], dO,
+                       init_state=c["init_state"], d_final_state=dS, scale=scale, nthreads=2, lib=lib)
+    names = ["q", "k", "v", "log_alpha", "beta", "init_state"]
+    eps = 1e-6
+    for name, grad in zip(names, g):
+        x = c[name]
+        fd = np.zeros_like(x)
+        flat = x.reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = _loss(lib, c, dO, dS, scale)
+            flat[i] = old - eps
+            lm = _loss(lib, c, dO, dS, scale)
+            flat[i] = old
+            fd.reshape(-1)[i] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(fd - grad))
+        assert err <= 1e-7 * max(1.0, np.max(np.abs(fd))), f"d{name}: finite-difference mismatch {err:.3e}"
+
+
+def pin_backward_autograd(lib):
+    """Every gradient equals torch float64 autograd through a naive token loop."""
+    import torch
+
+    rng = np.random.default_rng(RNG_SEED + 11)
+    c = _rand_case(rng, [70, 5], H=2, dk=4, dv=3, gate=(1.5, 1.0))
+    scale = 0.45
+    dO = rng.standard_normal(c["v"].shape)
+    dS = rng.standard_normal(c["init_state"].shape)
+    names = ["q", "k", "v", "log_alpha", "beta", "init_state"]
+    tt = {n: torch.tensor(c[n], dtype=torch.float64, requires_grad=True) for n in names}
+    cu = c["cu_seqlens"]
+    outs = []
+    fins = []
+    for s in range(len(cu) - 1):
+        fh = []
+        for h in range(c["q"].shape[1]):
+            S = tt["init_state"][s, h]
+            for t in range(cu[s], cu[s + 1]):
+                a = torch.exp(tt["log_alpha"][t, h])
+                kk = tt["k"][t, h]
+                # S_t = (I - b k k^T) Diag(a) S + b k v^T, written as matrices
+                M = torch.eye(kk.shape[0], dtype=torch.float64) - tt["beta"][t, h] * torch.outer(kk, kk)
+                S = M @ (a[:, None] * S) + tt["beta"][t, h] * torch.outer(kk, tt["v"][t, h])
+                outs.append(((t, h), scale * S.T @ tt["q"][t, h]))
+            fh.append(S)
+        fins.append(torch.stack(fh))
+    L = sum((o * torch.tensor(dO[t, h])).sum() for (t, h), o in outs)
+    L = L + (torch.stack(fins) * torch.tensor(dS)).sum()
+    L.backward()
+    g = oracle.kda_bwd(c["q"], c["k"], c["v"], c["log_alpha"], c["beta"], cu, dO,
+                       init_state=c["init_state"], d_final_state=dS, scale=scale, nthreads=2, lib=lib)
+    for name, grad in zip(names, g):
+        _close(grad, tt[name].grad.numpy(), 1e-11, f"d{name} vs autograd")
+
+
+def pin_backward_without_final_grad(lib):
+    """d_final_state omitted means zero: equals passing explicit zeros."""
+    rng = np.random.default_rng(RNG_SEED + 12)
+    c = _rand_case(rng, [70], H=1, dk=3, dv=2)
+    dO = rng.standard_normal(c["v"].shape)
+    a = oracle.kda_bwd(c["q"], c["k"], c["v"], c["log_alpha"], c["beta"], c["cu_seqlens"], dO,
+                       init_state=c["init_state"], d_final_state=None, lib=lib)
+    b = oracle.kda_bwd(c["q"], c["k"], c["v"], c["log_alpha"], c["beta"], c["cu_seqlens"], dO,
+                       init_state=c["init_state"], d_final_state=np.zeros_like(c["init_state"]), lib=lib)
+    for x, y in zip(a, b):
+        _close(x, y, 0.0, "zero final grad")
+
+
+BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_autograd, pin_backward_without_final_grad]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS
