@@ -1,0 +1,201 @@
+"""Kimi Delta Attention on MI355X (gfx950): Python binding of libkda.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkda.so (see include/kda.h for the C ABI).  PyTorch supplies
+device memory and the current stream.  If the library is not built this
+module raises on use; there is no fallback implementation.
+
+    o, S_T = fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None)
+    dq, dk, dv, dlog_alpha, dbeta, d_init = bwd(q, k, v, log_alpha, beta, d_out, ...)
+
+Shapes: q, k, log_alpha [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H]; all of
+one dtype (torch.float32 or torch.bfloat16), contiguous, on the GPU.  States
+are float32 [N, H, dk, dv] with N = B, or N = len(cu_seqlens) - 1 for a packed
+varlen batch (then B must be 1 and cu_seqlens is int32 on the GPU).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fwd", "bwd", "workspace_bytes", "KdaError", "lib_path", "load_library", "status_string"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+KDA_F32, KDA_BF16 = 0, 1
+
+
+class kda_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: str | None = None):
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libkda.so not found at {p}; build it with gated_delta_rule_79_amd.build.build()")
+    lib = ctypes.CDLL(p)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(kda_desc)
+    lib.kda_workspace_bytes.argtypes = [D, ctypes.c_int]
+    lib.kda_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().kda_status_string(int(status)).decode()
+    except Exception:  # library missing: still give a readable message
+        return f"status {status}"
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def make_desc(B, T, H, dk, dv, dtype_code, num_seqs=0, scale=None, out_code=KDA_F32) -> kda_desc:
+    return kda_desc(int(B), int(T), int(H), int(dk), int(dv), int(num_seqs), int(dtype_code), int(out_code),
+                    float(scale) if scale else 0.0)
+
+
+def workspace_bytes(B, T, H, dk, dv, dtype, num_seqs=0, backward=False) -> int:
+    import torch
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    d = make_desc(B, T, H, dk, dv, code, num_seqs)
+    return int(load_library().kda_workspace_bytes(ctypes.byref(d), 1 if backward else 0))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale, out_dtype=None):
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on the GPU")
+    dt = q.dtype
+    _check("k", k, dt, (B, T, H, dk), dev)
+    _check("log_alpha", log_alpha, dt, (B, T, H, dk), dev)
+    _check("v", v, dt, (B, T, H, dv), dev)
+    _check("beta", beta, dt, (B, T, H), dev)
+    _check("q", q, dt, (B, T, H, dk), dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("cu_seqlens requires B == 1")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != dev:
+            raise ValueError("cu_seqlens must be int32 [N+1] on the GPU")
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    if init_state is not None:
+        _check("init_state", init_state, torch.float32, (N, H, dk, dv), dev)
+    odt = torch.float32 if out_dtype is None else out_dtype
+    desc = make_desc(B, T, H, dk, dv, _dtype_code(dt), N if cu_seqlens is not None else 0, scale, _dtype_code(odt))
+    return desc, (B, T, H, dk, dv, N), dev, odt
+
+
+def _stream(dev):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, output_final_state=True,
+        out=None, final_state=None, workspace=None, out_dtype=None):
+    """Forward pass; returns (o [B,T,H,dv] in out_dtype (default float32), final_state float32
+    [N,H,dk,dv] or None).  out_dtype=torch.bfloat16 is allowed for bf16 inputs."""
+    import torch
+    lib = load_library()
+    desc, (B, T, H, dk, dv, N), dev, dt = _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale,
+                                                   out_dtype)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _check("out", out, dt, (B, T, H, dv), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check("final_state", final_state, torch.float32, (N, H, dk, dv), dev)
+    need = lib.kda_workspace_bytes(ctypes.byref(desc), 0)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.kda_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state),
+                     _ptr(out), _ptr(final_state), _ptr(cu_seqlens), _ptr(workspace),
+                     workspace.numel() * workspace.element_size(), _stream(dev))
+    if rc:
+        raise KdaError("kda_fwd", rc)
+    return out, final_state
+
+
+def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu_seqlens=None, scale=None,
+        need_d_init=True, workspace=None, out_dtype=None):
+    """Backward pass; returns (dq, dk, dv, dlog_alpha, dbeta in out_dtype (default float32),
+    d_init_state float32 or None)."""
+    import torch
+    lib = load_library()
+    desc, (B, T, H, dk, dv, N), dev, odt = _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale,
+                                                    out_dtype)
+    _check("d_out", d_out, q.dtype, (B, T, H, dv), dev)
+    if d_final_state is not None:
+        _check("d_final_state", d_final_state, torch.float32, (N, H, dk, dv), dev)
+    dq = torch.empty(q.shape, dtype=odt, device=dev)
+    dkk = torch.empty(k.shape, dtype=odt, device=dev)
+    dvv = torch.empty(v.shape, dtype=odt, device=dev)
+    dla = torch.empty(log_alpha.shape, dtype=odt, device=dev)
+    db = torch.empty(beta.shape, dtype=odt, device=dev)
+    dinit = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if need_d_init else None
+    need = lib.kda_workspace_bytes(ctypes.byref(desc), 1)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.kda_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state),
+                     _ptr(cu_seqlens), _ptr(d_out), _ptr(d_final_state), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dla),
+                     _ptr(db), _ptr(dinit), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                     _stream(dev))
+    if rc:
+        raise KdaError("kda_bwd", rc)
+    return dq, dkk, dvv, dla, db, dinit

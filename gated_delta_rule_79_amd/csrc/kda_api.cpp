@@ -1,0 +1,263 @@
+// kda_api.cpp -- C ABI of libkda.so: validation, workspace planning, dispatch.
+//
+// Everything here runs on the host before any launch; errors return a status
+// and enqueue nothing.  See include/kda.h for the contract.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kda_internal.hpp"
+
+namespace {
+
+using kda::Args;
+using kda::bf16;
+using kda::CH;
+using kda::ChunkInfo;
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Plan {
+  int N = 0;
+  int max_chunks = 0;
+  size_t esz = 0;
+  size_t chunks = 0, sc0 = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
+  size_t T = 0, S = 0, dS = 0, dU = 0, dQS = 0, dKh = 0, dW = 0, dAqk = 0, dGam = 0;
+  size_t total = 0;
+};
+
+bool dims_ok(const kda_desc* d) {
+  return (d->dk == 64 || d->dk == 128) && (d->dv == 64 || d->dv == 128) &&
+         (d->dtype == KDA_F32 || d->dtype == KDA_BF16) &&
+         (d->out_dtype == KDA_F32 || (d->out_dtype == KDA_BF16 && d->dtype == KDA_BF16));
+}
+
+// Number of sequences and chunk slots; varlen when `varlen`.
+bool shape_of(const kda_desc* d, bool varlen, int* N, int* max_chunks) {
+  if (d->B < 1 || d->T < 0 || d->H < 1 || d->H > 65535) return false;
+  const long long tok = (long long)d->B * d->T;
+  if (tok >= (1LL << 31)) return false;
+  if (varlen) {
+    if (d->B != 1 || d->num_seqs < 1) return false;
+    *N = d->num_seqs;
+    *max_chunks = d->T / CH + d->num_seqs;
+  } else {
+    *N = d->B;
+    *max_chunks = d->B * ((d->T + CH - 1) / CH);
+  }
+  return true;
+}
+
+Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
+  Plan p;
+  p.N = N;
+  p.max_chunks = max_chunks;
+  p.esz = d->dtype == KDA_BF16 ? 2 : 4;
+  const size_t nb = (size_t)max_chunks * d->H;  // chunk-head blocks
+  const size_t dk = d->dk, dv = d->dv, e = p.esz;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+  p.chunks = take((size_t)max_chunks * sizeof(ChunkInfo));
+  p.sc0 = take((size_t)(N + 1) * sizeof(int32_t));
+  p.W = take(nb * CH * dk * e);
+  p.KhT = take(nb * dk * CH * 4);
+  p.Qt = take(nb * CH * dk * e);
+  p.Ut = take(nb * dv * CH * 4);
+  p.Aqk = take(nb * CH * CH * 4);
+  p.Gam = take(nb * dk * 4);
+  if (bwd) {
+    p.T = take(nb * CH * CH * 4);
+    p.S = take(nb * dk * dv * 4);
+    p.dS = take(nb * dk * dv * e);
+    p.dU = take(nb * CH * dv * e);
+    p.dQS = take(nb * CH * dk * 4);
+    p.dKh = take(nb * CH * dk * 4);
+    p.dW = take(nb * CH * dk * e);
+    p.dAqk = take(nb * CH * CH * e);
+    p.dGam = take(nb * dk * 4);
+  }
+  p.total = o;
+  return p;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  return s && *s ? std::atoi(s) : dflt;
+}
+
+// Optional synchronous check of cu_seqlens contents (KDA_DEBUG=1).
+bool cu_ok(const int32_t* cu, int N, int T, hipStream_t st) {
+  std::vector<int32_t> h((size_t)N + 1);
+  if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess) return false;
+  if (hipStreamSynchronize(st) != hipSuccess) return false;
+  if (h[0] != 0 || h[N] != T) return false;
+  for (int i = 0; i < N; ++i)
+    if (h[i + 1] < h[i]) return false;
+  return true;
+}
+
+void fill_ws(Args& a, const Plan& p, void* ws) {
+  char* b = static_cast<char*>(ws);
+  a.chunks = reinterpret_cast<ChunkInfo*>(b + p.chunks);
+  a.seq_chunk0 = reinterpret_cast<int32_t*>(b + p.sc0);
+  a.wsW = b + p.W;
+  a.wsKhT = b + p.KhT;
+  a.wsQt = b + p.Qt;
+  a.wsUt = b + p.Ut;
+  a.wsAqk = b + p.Aqk;
+  a.wsGam = reinterpret_cast<float*>(b + p.Gam);
+  a.wsT = p.T ? b + p.T : nullptr;
+  a.wsS = p.S ? b + p.S : nullptr;
+  a.wsdS = p.dS ? b + p.dS : nullptr;
+  a.wsdU = p.dU ? b + p.dU : nullptr;
+  a.wsdQS = p.dQS ? reinterpret_cast<float*>(b + p.dQS) : nullptr;
+  a.wsdKh = p.dKh ? reinterpret_cast<float*>(b + p.dKh) : nullptr;
+  a.wsdW = p.dW ? b + p.dW : nullptr;
+  a.wsdAqk = p.dAqk ? b + p.dAqk : nullptr;
+  a.wsdGam = p.dGam ? reinterpret_cast<float*>(b + p.dGam) : nullptr;
+}
+
+hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {
+  const bool bf = d->dtype == KDA_BF16, obf = d->out_dtype == KDA_BF16;
+#define KDA_CASE(DK, DV)                                                                        \
+  if (d->dk == DK && d->dv == DV)                                                               \
+    return bf ? (obf ? kda::launch_fwd<bf16, bf16, DK, DV>(a, st) : kda::launch_fwd<bf16, float, DK, DV>(a, st)) \
+              : kda::launch_fwd<float, float, DK, DV>(a, st);
+  KDA_CASE(64, 64)
+  KDA_CASE(64, 128)
+  KDA_CASE(128, 64)
+  KDA_CASE(128, 128)
+#undef KDA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t run_bwd(const kda_desc* d, const Args& a, hipStream_t st) {
+  const bool bf = d->dtype == KDA_BF16;
+#define KDA_CASE(DK, DV)                                                                        \
+  if (d->dk == DK && d->dv == DV)                                                               \
+    return bf ? kda::launch_bwd<bf16, DK, DV>(a, st) : kda::launch_bwd<float, DK, DV>(a, st);
+  KDA_CASE(64, 64)
+  KDA_CASE(64, 128)
+  KDA_CASE(128, 64)
+  KDA_CASE(128, 128)
+#undef KDA_CASE
+  return hipErrorInvalidValue;
+}
+
+void base_args(Args& a, const kda_desc* d, int N, int max_chunks) {
+  std::memset(&a, 0, sizeof a);
+  a.B = d->B;
+  a.T = d->T;
+  a.H = d->H;
+  a.dk = d->dk;
+  a.dv = d->dv;
+  a.N = N;
+  a.max_chunks = max_chunks;
+  a.scale = d->scale != 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
+  a.dvs = 16;
+  a.out_bf16 = d->out_dtype == KDA_BF16;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_SUCCESS: return "success";
+    case KDA_ERROR_INVALID_VALUE: return "invalid value";
+    case KDA_ERROR_NOT_SUPPORTED: return "not supported (dk, dv must be 64 or 128; dtype f32 or bf16; bf16 out_dtype needs bf16 inputs)";
+    case KDA_ERROR_MISALIGNED: return "pointer not 16-byte aligned";
+    case KDA_ERROR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KDA_ERROR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t kda_workspace_bytes(const kda_desc* d, int backward) {
+  if (!d || !dims_ok(d)) return 0;
+  int N, mc;
+  size_t best = 0;
+  if (shape_of(d, false, &N, &mc)) best = make_plan(d, backward != 0, N, mc).total;
+  if (d->num_seqs > 0 && shape_of(d, true, &N, &mc)) {
+    const size_t v = make_plan(d, backward != 0, N, mc).total;
+    if (v > best) best = v;
+  }
+  return best;
+}
+
+kda_status kda_fwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* beta, const float* init_state, void* out, float* final_state,
+                   const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!d) return KDA_ERROR_INVALID_VALUE;
+  if (!dims_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
+  int N, mc;
+  if (!shape_of(d, cu_seqlens != nullptr, &N, &mc)) return KDA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(d->scale)) return KDA_ERROR_INVALID_VALUE;
+  const bool any_tok = (long long)d->B * d->T > 0;
+  if (any_tok && (!q || !k || !v || !log_alpha || !beta || !out)) return KDA_ERROR_INVALID_VALUE;
+  const void* al16[] = {q, k, v, log_alpha, out, init_state, final_state, workspace};
+  for (const void* p : al16)
+    if (p && !aligned16(p)) return KDA_ERROR_MISALIGNED;
+  if (beta && ((uintptr_t)beta % (d->dtype == KDA_BF16 ? 2 : 4))) return KDA_ERROR_MISALIGNED;
+  if (out && ((uintptr_t)out % (d->out_dtype == KDA_BF16 ? 2 : 4))) return KDA_ERROR_MISALIGNED;
+  if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_MISALIGNED;
+  const Plan p = make_plan(d, false, N, mc);
+  if (!workspace || workspace_bytes < p.total) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cu_seqlens && env_int("KDA_DEBUG", 0) && !cu_ok(cu_seqlens, N, d->T, st)) return KDA_ERROR_INVALID_VALUE;
+
+  Args a;
+  base_args(a, d, N, mc);
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+  a.init = init_state; a.cu = cu_seqlens;
+  a.out = out; a.final_state = final_state;
+  fill_ws(a, p, workspace);
+  (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
+  return run_fwd(d, a, st) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
+kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* beta, const float* init_state, const int32_t* cu_seqlens, const void* d_out,
+                   const float* d_final_state, void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta,
+                   float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!d) return KDA_ERROR_INVALID_VALUE;
+  if (!dims_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
+  int N, mc;
+  if (!shape_of(d, cu_seqlens != nullptr, &N, &mc)) return KDA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(d->scale)) return KDA_ERROR_INVALID_VALUE;
+  const bool any_tok = (long long)d->B * d->T > 0;
+  if (any_tok && (!q || !k || !v || !log_alpha || !beta || !d_out || !dq || !dk || !dv || !dlog_alpha || !dbeta))
+    return KDA_ERROR_INVALID_VALUE;
+  const void* al16[] = {q, k, v, log_alpha, init_state, d_out, d_final_state, dq, dk, dv, dlog_alpha,
+                        d_init_state, workspace};
+  for (const void* p : al16)
+    if (p && !aligned16(p)) return KDA_ERROR_MISALIGNED;
+  const size_t es = d->dtype == KDA_BF16 ? 2 : 4, eo = d->out_dtype == KDA_BF16 ? 2 : 4;
+  if ((beta && (uintptr_t)beta % es) || (dbeta && (uintptr_t)dbeta % eo)) return KDA_ERROR_MISALIGNED;
+  if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_MISALIGNED;
+  const Plan p = make_plan(d, true, N, mc);
+  if (!workspace || workspace_bytes < p.total) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cu_seqlens && env_int("KDA_DEBUG", 0) && !cu_ok(cu_seqlens, N, d->T, st)) return KDA_ERROR_INVALID_VALUE;
+
+  Args a;
+  base_args(a, d, N, mc);
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+  a.init = init_state; a.cu = cu_seqlens;
+  a.dout = d_out; a.dfinal = d_final_state;
+  a.dq = dq; a.dk_ = dk; a.dv_ = dv; a.dla = dlog_alpha; a.dbeta = dbeta; a.dinit = d_init_state;
+  fill_ws(a, p, workspace);
+  (void)hipGetLastError();
+  return run_bwd(d, a, st) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+}
+
+}  // extern "C"

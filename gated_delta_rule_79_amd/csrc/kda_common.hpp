@@ -1,0 +1,264 @@
+// kda_common.hpp -- device building blocks shared by the gfx950 KDA kernels.
+//
+// Conventions
+//  * Chunk length CH = 64 tokens.  A "chunk-head" is one chunk of one head.
+//  * MFMA tiles are 16x16 with a 32-deep contraction (v_mfma_f32_16x16x32_bf16,
+//    or eight v_mfma_f32_16x16x4_f32 for the fp32 path).  In a wave, lane l
+//    supplies row/column (l & 15) of an operand and the 8 consecutive
+//    contraction indices 8*(l >> 4) .. +7; it receives the accumulator
+//    elements (row 4*(l >> 4) + i, column l & 15), i = 0..3.  A and B use the
+//    same lane->k assignment, so the product is exact whatever order the
+//    hardware sums the 32 terms in.
+//  * LDS operand arrays are stored "k-contiguous" where possible so one
+//    fragment is one 16-byte LDS read; rows are padded by 16 bytes to spread
+//    banks.  frag_col() reads a fragment from the other orientation with
+//    eight scalar reads (used where a second copy would cost more LDS).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace kda {
+
+constexpr int CH = 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct ChunkInfo {
+  int32_t seq;  // sequence index
+  int32_t t0;   // first packed token of the chunk
+  int32_t len;  // valid tokens (0 => unused slot)
+  int32_t idx;  // chunk index inside its sequence
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float f32(float x) { return x; }
+__device__ __forceinline__ float f32(bf16 x) { return (float)x; }
+template <typename E> __device__ __forceinline__ E cvt(float x);
+template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 cvt<bf16>(float x) { return (bf16)x; }  // RNE
+
+// Row padding of LDS arrays, in elements (16 bytes).
+template <typename E> constexpr int PADE = 16 / (int)sizeof(E);
+
+// ---------------------------------------------------------------------------
+// fragments and MFMA
+// ---------------------------------------------------------------------------
+template <typename E> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+// 8 consecutive elements p[row*ld + k0 .. +7]; (row*ld + k0) must be a multiple of 16/sizeof(E)/... 16B aligned.
+template <typename E> __device__ __forceinline__ Frag<E> frag_row(const E* p, int ld, int row, int k0);
+template <> __device__ __forceinline__ Frag<bf16> frag_row<bf16>(const bf16* p, int ld, int row, int k0) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p + row * ld + k0);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> frag_row<float>(const float* p, int ld, int row, int k0) {
+  Frag<float> f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + row * ld + k0);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + row * ld + k0 + 4);
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+  return f;
+}
+// 8 elements down a column: p[(k0+j)*ld + col], j = 0..7.
+template <typename E> __device__ __forceinline__ Frag<E> frag_col(const E* p, int ld, int col, int k0) {
+  Frag<E> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = p[(k0 + j) * ld + col];
+  return f;
+}
+// Fragment built from 8 float values (converted to the operand type).
+template <typename E> __device__ __forceinline__ Frag<E> frag_from(const float (&x)[8]) {
+  Frag<E> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = cvt<E>(x[j]);
+  return f;
+}
+
+__device__ __forceinline__ f32x4 mma(const Frag<bf16>& a, const Frag<bf16>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// split operands: an fp32 value carried as x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi); a product of two split operands drops only lo*lo, so its
+// error is ~2^-16 relative instead of 2^-8.  On the fp32 path the "split"
+// operand is just the fp32 value (lo unused) and every product is one MFMA.
+// ---------------------------------------------------------------------------
+template <typename E> struct SFrag { Frag<E> hi, lo; };
+
+template <typename E> __device__ __forceinline__ SFrag<E> sfrag_from(const float (&x)[8]) {
+  SFrag<E> s;
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16 h = (bf16)x[j];
+      s.hi.v[j] = h;
+      s.lo.v[j] = (bf16)(x[j] - (float)h);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s.hi.v[j] = x[j];
+  }
+  return s;
+}
+// 8 consecutive fp32 values of LDS row `row`, split.
+template <typename E> __device__ __forceinline__ SFrag<E> sfrag_row(const float* p, int ld, int row, int k0) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + row * ld + k0);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + row * ld + k0 + 4);
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return sfrag_from<E>(x);
+}
+// hi/lo halves already stored as two E arrays of the same layout.
+template <typename E> __device__ __forceinline__ SFrag<E> sfrag_pair(const E* hi, const E* lo, int ld, int row, int k0) {
+  SFrag<E> s;
+  s.hi = frag_row<E>(hi, ld, row, k0);
+  if constexpr (sizeof(E) == 2) s.lo = frag_row<E>(lo, ld, row, k0);
+  return s;
+}
+template <typename E> __device__ __forceinline__ f32x4 mma_ss(const SFrag<E>& a, const SFrag<E>& b, f32x4 c) {
+  if constexpr (sizeof(E) == 2) {
+    c = mma(a.lo, b.hi, c);
+    c = mma(a.hi, b.lo, c);
+  }
+  return mma(a.hi, b.hi, c);
+}
+template <typename E> __device__ __forceinline__ f32x4 mma_sp(const SFrag<E>& a, const Frag<E>& b, f32x4 c) {
+  if constexpr (sizeof(E) == 2) c = mma(a.lo, b, c);
+  return mma(a.hi, b, c);
+}
+template <typename E> __device__ __forceinline__ f32x4 mma_ps(const Frag<E>& a, const SFrag<E>& b, f32x4 c) {
+  if constexpr (sizeof(E) == 2) c = mma(a, b.lo, c);
+  return mma(a, b.hi, c);
+}
+// Write 4 fp32 values as a split pair into two E arrays (contiguous 4 elements each).
+template <typename E> __device__ __forceinline__ void store4_split(E* hi, E* lo, float a, float b, float c, float d) {
+  if constexpr (sizeof(E) == 2) {
+    const bf16 ha = (bf16)a, hb = (bf16)b, hc = (bf16)c, hd = (bf16)d;
+    *reinterpret_cast<bf16x4*>(hi) = bf16x4{ha, hb, hc, hd};
+    *reinterpret_cast<bf16x4*>(lo) = bf16x4{(bf16)(a - (float)ha), (bf16)(b - (float)hb), (bf16)(c - (float)hc),
+                                            (bf16)(d - (float)hd)};
+  } else {
+    *reinterpret_cast<f32x4*>(hi) = f32x4{a, b, c, d};
+  }
+}
+
+// C(16x16) += A(m0.., k) * B(k, n0..), contraction length K (multiple of 32).
+// Operands come from LDS through loaders: la(row_in_tile, k) / lb(col_in_tile, k).
+template <int K, typename LA, typename LB>
+__device__ __forceinline__ f32x4 tile_mm(LA la, LB lb, f32x4 acc) {
+  const int l = lane_id(), r16 = l & 15, kq = (l >> 4) * 8;
+#pragma unroll
+  for (int k = 0; k < K; k += 32) acc = mma(la(r16, k + kq), lb(r16, k + kq), acc);
+  return acc;
+}
+
+// C(16x16) += A(m0 + ., k) * S(k, n0 + .) where A is a plain operand stored
+// [m][k] and S a split operand stored as hi/lo arrays [n][k].
+template <typename E, int K>
+__device__ __forceinline__ f32x4 tile_mm_ps(const E* A, int lda, int m0, const E* Bh, const E* Bl, int ldb, int n0) {
+  const int l = lane_id(), r16 = l & 15, kq = (l >> 4) * 8;
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int k = 0; k < K; k += 32)
+    acc = mma_ps(frag_row<E>(A, lda, m0 + r16, k + kq), sfrag_pair<E>(Bh, Bl, ldb, n0 + r16, k + kq), acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// cooperative global <-> LDS copies (16-byte vectors)
+// ---------------------------------------------------------------------------
+// Copy a ROWS x COLS tile of E (row pitch src_ld elements in global, dst_ld in
+// LDS) with NT threads.  COLS*sizeof(E) must be a multiple of 16.
+// Compile-time loop: f(integral_constant<int, I>) for I in [I0, N).  Register
+// arrays indexed through it stay in registers (no dynamic indexing).
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, N>(f);
+  }
+}
+
+template <typename E, int ROWS, int COLS, int NT>
+struct TileCopy {
+  static constexpr int VPR = COLS * (int)sizeof(E) / 16;  // vectors per row
+  static constexpr int NV = ROWS * VPR;
+  static constexpr int PER = (NV + NT - 1) / NT;
+  uint4 r[PER];
+  __device__ __forceinline__ void load(const E* __restrict__ src, size_t src_ld) {
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      // threads past the tile re-read vector 0 (always in bounds) and skip the store,
+      // so every register is defined on every path
+      const int v0 = threadIdx.x + I * NT;
+      const int v = (NV % NT == 0 || v0 < NV) ? v0 : 0;
+      const int row = v / VPR, cv = v % VPR;
+      r[I] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src + row * src_ld) + cv * 16);
+    });
+  }
+  __device__ __forceinline__ void store(E* dst, int dst_ld) const {
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = threadIdx.x + I * NT;
+      if (NV % NT == 0 || v < NV) {
+        const int row = v / VPR, cv = v % VPR;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + row * dst_ld) + cv * 16) = r[I];
+      }
+    });
+  }
+};
+
+// Global -> LDS in one go (load then store).
+template <typename E, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void copy_in(E* dst, int dst_ld, const E* __restrict__ src, size_t src_ld) {
+  TileCopy<E, ROWS, COLS, NT> t;
+  t.load(src, src_ld);
+  t.store(dst, dst_ld);
+}
+
+// LDS -> global.
+template <typename E, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void copy_out(E* __restrict__ dst, size_t dst_ld, const E* src, int src_ld) {
+  constexpr int VPR = COLS * (int)sizeof(E) / 16;
+  constexpr int NV = ROWS * VPR;
+  for (int v = threadIdx.x; v < NV; v += NT) {
+    const int row = v / VPR, cv = v % VPR;
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + row * dst_ld) + cv * 16) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src + row * src_ld) + cv * 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout shared by the host planner and the kernels
+// ---------------------------------------------------------------------------
+// Per (chunk, head) blocks, chunk-major so one head's chunks are strided by H.
+// Element counts per block; the element type of each array is given beside it
+// (fp32 arrays feed split operands).
+template <typename E, int DK, int DV>
+struct WsBlock {
+  static constexpr size_t W = (size_t)CH * DK;     // W   [CH][DK]   E
+  static constexpr size_t KHT = (size_t)DK * CH;   // Kh^T[DK][CH]   float
+  static constexpr size_t QT = (size_t)CH * DK;    // Qt  [CH][DK]   E
+  static constexpr size_t UT = (size_t)DV * CH;    // U~^T[DV][CH]   float
+  static constexpr size_t AQK = (size_t)CH * CH;   // Aqk [CH][CH]   float
+  static constexpr size_t TT = (size_t)CH * CH;    // T   [CH][CH]   float (backward only)
+  static constexpr size_t GAM = DK;                // Gamma_C [DK]   float
+  static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk, [DV][DK] float (backward only)
+};
+
+}  // namespace kda

@@ -1,0 +1,112 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library (libkda.so).
+ *
+ * Operation (fireworks.ai, "Kimi K3 on Fireworks: Fast RL at frontier scale",
+ * section on Kimi Delta Attention: a linear attention that updates a compact
+ * per-head recurrent state with channel-wise gating, linear in sequence length,
+ * fixed-size decoding state).  Per sequence and head, with state S (dk x dv,
+ * row = key channel) and scale = dk^-1/2 unless given:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(log_alpha_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * S_0 = init_state (zero when NULL); final_state = S_T.  kda_bwd returns the
+ * gradients of L = <d_out, o> + <d_final_state, S_T> with respect to every
+ * input.  The same page says the training kernel must parallelise chunk-local
+ * work while limiting the stalls of the recurrent dependency and the movement
+ * of intermediates; the library does chunk-local work in parallel and runs
+ * the chunk-to-chunk state recurrence as a separate sequential pass.
+ *
+ * Layouts (all contiguous, token-major; sequences of a varlen batch packed):
+ *   q, k, log_alpha                      : [B, T, H, dk]   (desc.dtype)
+ *   v, d_out                             : [B, T, H, dv]   (desc.dtype)
+ *   beta                                 : [B, T, H]       (desc.dtype)
+ *   dq, dk, dlog_alpha                   : [B, T, H, dk]   (desc.out_dtype)
+ *   out, dv                              : [B, T, H, dv]   (desc.out_dtype)
+ *   dbeta                                : [B, T, H]       (desc.out_dtype)
+ *   init_state, final_state, d_final_state, d_init_state : float32 [N, H, dk, dv]
+ *     with N = B, or N = num_seqs when cu_seqlens is given.
+ *   cu_seqlens : int32 [num_seqs + 1] in device memory, cu[0] = 0,
+ *     non-decreasing, cu[num_seqs] = T; only valid with B == 1.
+ *
+ * Ownership: every pointer is device memory owned by the caller, including
+ * the workspace (size from kda_workspace_bytes).  The library allocates and
+ * frees nothing, does not synchronise, and keeps no pointer after a call
+ * returns.  All work is enqueued on `stream` in order.
+ *
+ * Aliasing: final_state may alias init_state (each state slice is read before
+ * it is written).  out and the gradient outputs must not overlap any input.
+ *
+ * Precision: all accumulation is fp32.  With bf16 inputs the products whose
+ * rounding would reach the outputs (decayed Gram blocks, the state, U, and the
+ * chunk matrices that multiply them) use a two-term bf16 split of the fp32
+ * operand (x = hi + lo), so their error is that of fp32 operands; the rest use
+ * plain bf16 operands.  A bf16 out_dtype rounds the results once at the end.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; on
+ * an error nothing is launched.  Launch failures return KDA_ERROR_LAUNCH.
+ * The contents of cu_seqlens are a precondition (checked with a synchronous
+ * copy only when the environment variable KDA_DEBUG=1).  log_alpha must be
+ * finite and <= 0; full accuracy is kept while the total log-decay of any
+ * channel over 8 consecutive tokens stays above -80.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_SUCCESS = 0,
+    KDA_ERROR_INVALID_VALUE = 1,     /* null required pointer, bad shape, bad num_seqs */
+    KDA_ERROR_NOT_SUPPORTED = 2,     /* dk or dv not in {64, 128}, unknown dtype */
+    KDA_ERROR_MISALIGNED = 3,        /* a pointer not 16-byte aligned */
+    KDA_ERROR_WORKSPACE_TOO_SMALL = 4,
+    KDA_ERROR_LAUNCH = 5             /* a kernel launch failed (hipGetLastError) */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef struct {
+    int32_t B;          /* rows; must be 1 when cu_seqlens is given                         */
+    int32_t T;          /* tokens per row (total packed tokens when cu_seqlens is given)    */
+    int32_t H;          /* heads                                                            */
+    int32_t dk;         /* key/query head dim: 64 or 128                                    */
+    int32_t dv;         /* value head dim: 64 or 128                                        */
+    int32_t num_seqs;   /* number of packed sequences when cu_seqlens is given, else ignored */
+    kda_dtype dtype;    /* storage dtype of q, k, v, log_alpha, beta, d_out                 */
+    kda_dtype out_dtype;/* storage dtype of out, dq, dk, dv, dlog_alpha, dbeta; KDA_BF16 is
+                           allowed only when dtype is KDA_BF16                               */
+    float scale;        /* output scale; 0 means dk^-1/2                                    */
+} kda_desc;
+
+/* Bytes of device workspace kda_fwd (backward = 0) or kda_bwd (backward != 0)
+ * needs for this problem; 0 if the descriptor is invalid. */
+size_t kda_workspace_bytes(const kda_desc *desc, int backward);
+
+/* Forward pass: out (and final_state unless NULL).  init_state may be NULL (zero). */
+kda_status kda_fwd(const kda_desc *desc, const void *q, const void *k, const void *v,
+                   const void *log_alpha, const void *beta, const float *init_state,
+                   void *out, float *final_state, const int32_t *cu_seqlens,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward pass: recomputes the forward internally (no saved activations).
+ * d_final_state may be NULL (zero); d_init_state may be NULL (not written). */
+kda_status kda_bwd(const kda_desc *desc, const void *q, const void *k, const void *v,
+                   const void *log_alpha, const void *beta, const float *init_state,
+                   const int32_t *cu_seqlens, const void *d_out, const float *d_final_state,
+                   void *dq, void *dk, void *dv, void *dlog_alpha, void *dbeta,
+                   float *d_init_state, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *kda_status_string(kda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,123 @@
+"""The C ABI: the library loads, exports what include/kda.h declares, and
+rejects bad arguments on the host before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_79_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+S_OK, S_INVALID, S_UNSUP, S_ALIGN, S_WS, S_LAUNCH = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.lib_path()):
+        import gated_delta_rule_79_amd.build as b
+        b.build()
+    return kda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["kda_bwd", "kda_fwd", "kda_status_string", "kda_workspace_bytes"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.kda_status_string(s)
+    assert b"unknown" in lib.kda_status_string(99)
+
+
+def _desc(**kw):
+    d = dict(B=1, T=256, H=2, dk=64, dv=64, num_seqs=0, dtype=1, out_dtype=0, scale=0.0)
+    d.update(kw)
+    return kda.kda_desc(**d)
+
+
+P = ctypes.c_void_p
+A = 0x100000  # an aligned fake address; never dereferenced on these paths
+
+
+def _fwd(lib, d, q=A, k=A, v=A, la=A, beta=A, init=None, out=A, fin=None, cu=None, ws=A, wsb=1 << 40):
+    return lib.kda_fwd(ctypes.byref(d) if d is not None else None, P(q), P(k), P(v), P(la), P(beta), P(init),
+                       P(out), P(fin), P(cu), P(ws), wsb, None)
+
+
+def _bwd(lib, d, ws=A, wsb=1 << 40, dq=A, cu=None):
+    return lib.kda_bwd(ctypes.byref(d), P(A), P(A), P(A), P(A), P(A), None, P(cu), P(A), None, P(dq), P(A), P(A),
+                       P(A), P(A), None, P(ws), wsb, None)
+
+
+def test_rejects_null_descriptor(lib):
+    assert _fwd(lib, None) == S_INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(dk=96), dict(dv=32), dict(dk=256), dict(dtype=7), dict(out_dtype=5),
+                                dict(dtype=0, out_dtype=1)])
+def test_rejects_unsupported(lib, kw):
+    assert _fwd(lib, _desc(**kw)) == S_UNSUP
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=-1), dict(H=0), dict(B=70000, T=40000)])
+def test_rejects_bad_shapes(lib, kw):
+    assert _fwd(lib, _desc(**kw)) == S_INVALID
+
+
+def test_rejects_varlen_misuse(lib):
+    assert _fwd(lib, _desc(B=2, num_seqs=2), cu=A) == S_INVALID
+    assert _fwd(lib, _desc(num_seqs=0), cu=A) == S_INVALID
+
+
+def test_rejects_null_required_pointer(lib):
+    for key in ("q", "k", "v", "la", "beta", "out"):
+        assert _fwd(lib, _desc(), **{key: None}) == S_INVALID, key
+    assert _bwd(lib, _desc(), dq=None) == S_INVALID
+
+
+def test_rejects_misaligned(lib):
+    assert _fwd(lib, _desc(), q=A + 8) == S_ALIGN
+    assert _fwd(lib, _desc(), init=A + 4) == S_ALIGN
+    assert _fwd(lib, _desc(), beta=A + 1) == S_ALIGN
+    assert _fwd(lib, _desc(), ws=A + 8) == S_ALIGN
+
+
+def test_rejects_small_workspace(lib):
+    d = _desc()
+    need = lib.kda_workspace_bytes(ctypes.byref(d), 0)
+    assert need > 0
+    assert _fwd(lib, d, wsb=need - 1) == S_WS
+    assert _fwd(lib, d, ws=None) == S_WS
+    needb = lib.kda_workspace_bytes(ctypes.byref(d), 1)
+    assert needb > need
+    assert _bwd(lib, d, wsb=needb - 1) == S_WS
+
+
+def test_workspace_sizes(lib):
+    sizes = [lib.kda_workspace_bytes(ctypes.byref(_desc(T=t)), 0) for t in (64, 128, 4096)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    assert lib.kda_workspace_bytes(ctypes.byref(_desc(dk=80)), 0) == 0
+    # a varlen descriptor reserves a slot per sequence for ragged tails
+    v = lib.kda_workspace_bytes(ctypes.byref(_desc(T=4096, num_seqs=8)), 0)
+    assert v > sizes[2]
+
+
+def test_empty_problem_needs_no_token_pointers(lib):
+    d = _desc(T=0)
+    need = lib.kda_workspace_bytes(ctypes.byref(d), 0)
+    assert need > 0
+    # validation passes (no null-pointer error); stop short of launching by giving a small workspace
+    assert _fwd(lib, d, q=None, k=None, v=None, la=None, beta=None, out=None, wsb=need - 1) == S_WS
