@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of Kimi Delta Attention forward + backward on one MI355X.
+
+One step = kda_fwd followed by kda_bwd (every kernel of the path) over one
+batch of seeded synthetic inputs already resident in HBM: the varlen workload
+of 8 packed sequences with lengths drawn from U[1K, 32K] (~128K tokens),
+H=16, dk=dv=128, bf16 inputs, fp32 states, fp32 outputs and gradients.
+
+Prints one JSON line: tokens/s for the whole step, the roofline of the
+dominant kernel (HIP-event durations recorded live around every launch of the
+timed steps), the whole-step roofline, and the float64 CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--fwd-only]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+
+
+def algorithmic_bytes(w, tokens, n_seqs, fwd_only):
+    """Compulsory HBM bytes of the path (inputs read once, outputs written once)."""
+    H, dk, dv = w.H, w.dk, w.dv
+    ein = 2 if w.dtype == "bf16" else 4
+    eout = 4
+    th = tokens * H
+    state = n_seqs * H * dk * dv * 4
+    fwd = th * (ein * (2 * dk + dk + dv) + ein) + th * eout * dv + 2 * state      # q,k,la,v,beta -> o; S0 in, S_T out
+    if fwd_only:
+        return fwd, {"fwd": fwd}
+    bwd = (th * (ein * (2 * dk + dk + dv) + ein + ein * dv)                       # q,k,la,v,beta,dO
+           + th * eout * (2 * dk + dk + dv + 1)                                   # dq,dk,dla,dv,dbeta
+           + 3 * state)                                                           # S0, dS_T in; dS0 out
+    return fwd + bwd, {"fwd": fwd, "bwd": bwd}
+
+
+def algorithmic_flops(w, tokens, fwd_only):
+    """Chunked-form flops per token-head (C=64, triangles counted once), as derived for the roofline."""
+    d = w.dk
+    C = 64
+    # forward per token-head: Gram blocks (2 * C/2 * d * 2), W, U~ (2 * C/2 * d * 2), W S, Qt S, Kh^T U (3 * 2 d^2),
+    # Aqk U (C/2 * d * 2)
+    fwd = 2 * (C // 2) * d * 2 + 2 * (C // 2) * d * 2 + 3 * 2 * d * d + (C // 2) * d * 2
+    bwd = 2.75 * fwd
+    per = fwd if fwd_only else fwd + bwd
+    return per * tokens * w.H
+
+
+def kernel_alg_bytes(name, w, tokens, n_seqs):
+    """Compulsory bytes one launch of a kernel must move (its share of the path's inputs/outputs)."""
+    H, dk, dv = w.H, w.dk, w.dv
+    ein = 2 if w.dtype == "bf16" else 4
+    th = tokens * H
+    state = n_seqs * H * dk * dv * 4
+    table = {
+        "kda_prep": th * (ein * (2 * dk + dk + dv) + ein),                # reads q, k, log_alpha, v, beta
+        "kda_prep_bwd": th * (ein * (2 * dk + dk + dv) + ein),
+        "kda_state_fwd": th * 4 * dv + 2 * state,                         # writes o; reads S0, writes S_T
+        "kda_state_bwd_fwdpass": state,                                   # reads S0
+        "kda_state_bwd_revpass": th * ein * dv + 2 * state,               # reads dO, dS_T; writes dS0
+        "kda_bwd_chunk": th * (ein * (2 * dk + dk + dv) + ein + ein * dv) + th * 4 * (2 * dk + dk + dv + 1),
+        "kda_chunk_map": 0,
+    }
+    return table.get(name, 0)
+
+
+def cpu_baseline(inp, w, with_bwd):
+    """The float64 oracle (untuned) on a bounded sample: heads 0-1 of every sequence, fwd (+bwd)."""
+    import oracle
+    n_seq = len(inp["lengths"])
+    heads = [0, 1]
+    units = [(s, h) for h in heads for s in range(n_seq)]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"],
+                   init_state=inp["init_state"], units=units, nthreads=threads)
+    if with_bwd:
+        oracle.kda_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"], inp["d_out"],
+                       init_state=inp["init_state"], d_final_state=inp["d_final_state"], units=units,
+                       nthreads=threads)
+    dt = time.perf_counter() - t0
+    token_heads = sum(inp["lengths"]) * len(heads)
+    return {
+        "value": token_heads / w.H / dt,
+        "unit": "tokens/s",
+        "cores": min(threads, len(units)),
+        "kind": "oracle",
+        "sample": f"heads {heads[0]}-{heads[-1]} of all {n_seq} sequences ({token_heads} token-heads, "
+                  f"{'fwd+bwd' if with_bwd else 'fwd'}), {dt:.1f} s; value = sample token-heads / H / s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload index (4 = varlen fwd+bwd)")
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out-bf16", action="store_true", help="bf16 outputs/gradients instead of fp32")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}); the multi-GPU path is not "
+              f"part of this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_79_amd as kda
+    import kda_inputs as ki
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    kda.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = ki.config(args.config)
+    fwd_only = args.fwd_only or not w.backward
+    print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
+    inp = ki.make_inputs(w, with_grads=not fwd_only)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    odt = torch.bfloat16 if args.out_bf16 else torch.float32
+    t = {k: torch.from_numpy(inp[k]).to(dev, dt).unsqueeze(0) for k in ("q", "k", "v", "log_alpha", "beta")}
+    init = torch.from_numpy(inp["init_state"]).to(dev) if inp["init_state"] is not None else None
+    varlen = w.lengths is not None
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev) if varlen else None
+    if varlen:
+        pass
+    else:
+        t = {k: v.reshape(w.B, w.T, *v.shape[2:]) for k, v in t.items()}
+    tokens = int(sum(inp["lengths"]))
+    n_seqs = len(inp["lengths"])
+    if not fwd_only:
+        d_out = torch.from_numpy(inp["d_out"]).to(dev, dt).unsqueeze(0)
+        if not varlen:
+            d_out = d_out.reshape(w.B, w.T, *d_out.shape[2:])
+        d_fin = torch.from_numpy(inp["d_final_state"]).to(dev)
+    B, T = t["q"].shape[0], t["q"].shape[1]
+    ws = torch.empty(kda.workspace_bytes(B, T, w.H, w.dk, w.dv, dt, num_seqs=n_seqs if varlen else 0,
+                                         backward=not fwd_only), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, w.H, w.dv), dtype=odt, device=dev)
+    fin = torch.empty((n_seqs, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    grads = None
+    if not fwd_only:
+        grads = tuple(torch.empty(x.shape, dtype=odt, device=dev) for x in (t["q"], t["k"], t["v"], t["log_alpha"],
+                                                                            t["beta"]))
+        dinit = torch.empty_like(fin)
+
+    def step():
+        kda.fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], init_state=init, cu_seqlens=cu, out=out,
+                final_state=fin, workspace=ws, out_dtype=odt)
+        if not fwd_only:
+            kda.bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], d_out, init_state=init, d_final_state=d_fin,
+                    cu_seqlens=cu, workspace=ws, out_dtype=odt, grads=grads, d_init=dinit)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    kda.timing_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = e0.elapsed_time(e1)
+    kt = kda.timing_read()
+    kda.timing_enable(False)
+    ms_step = ms_total / args.steps
+    value = tokens / (ms_step * 1e-3)
+
+    # dominant kernel roofline
+    dom = max(kt.items(), key=lambda kv: kv[1][0]) if kt else None
+    roof = None
+    if dom:
+        name, (tot_ms, n_launch) = dom
+        avg_ms = tot_ms / max(n_launch, 1)
+        ab = kernel_alg_bytes(name, w, tokens, n_seqs)
+        ach = ab / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": name,
+                "avg_launch_ms": round(avg_ms, 4), "alg_bytes_per_launch": int(ab)}
+    total_bytes, parts = algorithmic_bytes(w, tokens, n_seqs, fwd_only)
+    flops = algorithmic_flops(w, tokens, fwd_only)
+    t_hbm = total_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+    step_roof = {"alg_bytes": int(total_bytes), "alg_flops": int(flops), "roofline_ms": round(max(t_hbm, t_mfma) * 1e3, 4),
+                 "frac": round(max(t_hbm, t_mfma) / (ms_step * 1e-3), 4), "bound": "hbm" if t_hbm >= t_mfma else "mfma"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, w, not fwd_only)
+
+    line = {
+        "metric": "KDA fwd+bwd tokens/s (H=16, d=128, bf16 inputs, varlen 8 x U[1K,32K])" if not fwd_only
+        else f"KDA fwd tokens/s ({w.name})",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": tokens, "sequences": n_seqs, "H": w.H, "dk": w.dk, "dv": w.dv,
+                   "out_dtype": "bf16" if args.out_bf16 else "f32", "pass": "fwd" if fwd_only else "fwd+bwd"},
+        "roofline": roof,
+        "step_roofline": step_roof,
+        "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in kt.items()},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(t_wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

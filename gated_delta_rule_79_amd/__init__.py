@@ -18,7 +18,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "workspace_bytes", "KdaError", "lib_path", "load_library", "status_string"]
+__all__ = ["fwd", "bwd", "workspace_bytes", "KdaError", "lib_path", "load_library", "status_string", "timing_enable",
+           "timing_read"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -62,9 +63,32 @@ def load_library(path: str | None = None):
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_timing_enable.argtypes = [ctypes.c_int]
+    lib.kda_timing_enable.restype = None
+    lib.kda_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int)]
+    lib.kda_timing_read.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
+
+
+def timing_enable(on: bool = True) -> None:
+    """Record a HIP event pair around every later kernel launch (clears totals when enabling)."""
+    load_library().kda_timing_enable(1 if on else 0)
+
+
+def timing_read() -> dict:
+    """{kernel name: (total milliseconds, launches)} of the launches recorded so far (waits for them)."""
+    lib = load_library()
+    n = 64
+    names = (ctypes.c_char_p * n)()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    k = lib.kda_timing_read(n, names, ms, cnt)
+    if k < 0:
+        raise RuntimeError("kda_timing_read: a HIP event call failed")
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(k)}
 
 
 def status_string(status: int) -> str:
@@ -173,7 +197,7 @@ def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, 
 
 
 def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu_seqlens=None, scale=None,
-        need_d_init=True, workspace=None, out_dtype=None):
+        need_d_init=True, workspace=None, out_dtype=None, grads=None, d_init=None):
     """Backward pass; returns (dq, dk, dv, dlog_alpha, dbeta in out_dtype (default float32),
     d_init_state float32 or None)."""
     import torch
@@ -183,12 +207,16 @@ def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu
     _check("d_out", d_out, q.dtype, (B, T, H, dv), dev)
     if d_final_state is not None:
         _check("d_final_state", d_final_state, torch.float32, (N, H, dk, dv), dev)
-    dq = torch.empty(q.shape, dtype=odt, device=dev)
-    dkk = torch.empty(k.shape, dtype=odt, device=dev)
-    dvv = torch.empty(v.shape, dtype=odt, device=dev)
-    dla = torch.empty(log_alpha.shape, dtype=odt, device=dev)
-    db = torch.empty(beta.shape, dtype=odt, device=dev)
-    dinit = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if need_d_init else None
+    if grads is None:
+        grads = tuple(torch.empty(x.shape, dtype=odt, device=dev) for x in (q, k, v, log_alpha, beta))
+    for name, g, x in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta"), grads, (q, k, v, log_alpha, beta)):
+        _check(name, g, odt, x.shape, dev)
+    dq, dkk, dvv, dla, db = grads
+    dinit = d_init
+    if dinit is None and need_d_init:
+        dinit = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif dinit is not None:
+        _check("d_init", dinit, torch.float32, (N, H, dk, dv), dev)
     need = lib.kda_workspace_bytes(ctypes.byref(desc), 1)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

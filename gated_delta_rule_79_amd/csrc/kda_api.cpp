@@ -9,6 +9,9 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
 #include <vector>
 
 #include "kda_internal.hpp"
@@ -28,7 +31,8 @@ struct Plan {
   int max_chunks = 0;
   size_t esz = 0;
   size_t chunks = 0, sc0 = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
-  size_t T = 0, S = 0, dS = 0, dU = 0, dQS = 0, dKh = 0, dW = 0, dAqk = 0, dGam = 0;
+  size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0, dAqk = 0, dQS = 0, dKh = 0, dW = 0, dTU = 0,
+         dGam = 0, dBv = 0;
   size_t total = 0;
 };
 
@@ -65,22 +69,28 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
   p.chunks = take((size_t)max_chunks * sizeof(ChunkInfo));
   p.sc0 = take((size_t)(N + 1) * sizeof(int32_t));
-  p.W = take(nb * CH * dk * e);
-  p.KhT = take(nb * dk * CH * 4);
+  p.W = take(nb * CH * dk * e);    // operand type: fp16 for bf16 inputs, fp32 otherwise
+  p.KhT = take(nb * dk * CH * e);
   p.Qt = take(nb * CH * dk * e);
-  p.Ut = take(nb * dv * CH * 4);
-  p.Aqk = take(nb * CH * CH * 4);
+  p.Ut = take(nb * dv * CH * e);
+  p.Aqk = take(nb * CH * CH * e);
   p.Gam = take(nb * dk * 4);
   if (bwd) {
     p.T = take(nb * CH * CH * 4);
-    p.S = take(nb * dk * dv * 4);
-    p.dS = take(nb * dk * dv * e);
-    p.dU = take(nb * CH * dv * e);
+    p.UtF = take(nb * dv * CH * 4);
+    p.G = take(nb * CH * CH * 4);
+    p.KhF = take(nb * CH * dk * 4);
+    p.S = take(nb * dk * dv * e);
+    p.U = take(nb * dv * CH * 4);
+    p.dS = take(nb * dk * dv * 4);
+    p.dU = take(nb * dv * CH * 4);
+    p.dAqk = take(nb * CH * CH * 4);
     p.dQS = take(nb * CH * dk * 4);
     p.dKh = take(nb * CH * dk * 4);
-    p.dW = take(nb * CH * dk * e);
-    p.dAqk = take(nb * CH * CH * e);
+    p.dW = take(nb * CH * dk * 4);
+    p.dTU = take(nb * CH * CH * 4);
     p.dGam = take(nb * dk * 4);
+    p.dBv = take(nb * CH * 4);
   }
   p.total = o;
   return p;
@@ -114,15 +124,22 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
   a.wsUt = b + p.Ut;
   a.wsAqk = b + p.Aqk;
   a.wsGam = reinterpret_cast<float*>(b + p.Gam);
+  auto fptr = [&](size_t off) { return off ? reinterpret_cast<float*>(b + off) : nullptr; };
   a.wsT = p.T ? b + p.T : nullptr;
+  a.wsUtF = fptr(p.UtF);
+  a.wsG = fptr(p.G);
+  a.wsKhF = fptr(p.KhF);
   a.wsS = p.S ? b + p.S : nullptr;
-  a.wsdS = p.dS ? b + p.dS : nullptr;
-  a.wsdU = p.dU ? b + p.dU : nullptr;
-  a.wsdQS = p.dQS ? reinterpret_cast<float*>(b + p.dQS) : nullptr;
-  a.wsdKh = p.dKh ? reinterpret_cast<float*>(b + p.dKh) : nullptr;
-  a.wsdW = p.dW ? b + p.dW : nullptr;
-  a.wsdAqk = p.dAqk ? b + p.dAqk : nullptr;
-  a.wsdGam = p.dGam ? reinterpret_cast<float*>(b + p.dGam) : nullptr;
+  a.wsU = fptr(p.U);
+  a.wsdS = fptr(p.dS);
+  a.wsdU = fptr(p.dU);
+  a.wsdAqk = fptr(p.dAqk);
+  a.wsdQS = fptr(p.dQS);
+  a.wsdKh = fptr(p.dKh);
+  a.wsdW = fptr(p.dW);
+  a.wsdTU = fptr(p.dTU);
+  a.wsdGam = fptr(p.dGam);
+  a.wsdBv = fptr(p.dBv);
 }
 
 hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {
@@ -140,15 +157,20 @@ hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {
 }
 
 hipError_t run_bwd(const kda_desc* d, const Args& a, hipStream_t st) {
-  const bool bf = d->dtype == KDA_BF16;
+  const bool bf = d->dtype == KDA_BF16, obf = d->out_dtype == KDA_BF16;
+  if (bf) {
 #define KDA_CASE(DK, DV)                                                                        \
-  if (d->dk == DK && d->dv == DV)                                                               \
-    return bf ? kda::launch_bwd<bf16, DK, DV>(a, st) : kda::launch_bwd<float, DK, DV>(a, st);
-  KDA_CASE(64, 64)
-  KDA_CASE(64, 128)
-  KDA_CASE(128, 64)
-  KDA_CASE(128, 128)
+    if (d->dk == DK && d->dv == DV)                                                             \
+      return obf ? kda::launch_bwd<bf16, bf16, DK, DV>(a, st) : kda::launch_bwd<bf16, float, DK, DV>(a, st);
+    KDA_CASE(64, 64)
+    KDA_CASE(64, 128)
+    KDA_CASE(128, 64)
+    KDA_CASE(128, 128)
 #undef KDA_CASE
+  } else {  // fp32 backward is built for dk = 64 (the host check rejects dk = 128)
+    if (d->dk == 64 && d->dv == 64) return kda::launch_bwd<float, float, 64, 64>(a, st);
+    if (d->dk == 64 && d->dv == 128) return kda::launch_bwd<float, float, 64, 128>(a, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -166,9 +188,105 @@ void base_args(Args& a, const kda_desc* d, int N, int max_chunks) {
   a.out_bf16 = d->out_dtype == KDA_BF16;
 }
 
+// ---- opt-in per-kernel timing -------------------------------------------
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  struct Pending { const char* name; hipEvent_t a, b; };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  std::map<std::string, std::pair<double, int>> totals;
+  std::vector<const char*> order;  // static kernel-name literals, first-seen order
+  const char* open_name = nullptr;
+  hipEvent_t open_ev = nullptr;
+  bool failed = false;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) failed = true;
+    return e;
+  }
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
 }  // namespace
 
+namespace kda {
+void timing_begin(const char* name, hipStream_t st) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on) return;
+  t.open_name = name;
+  t.open_ev = t.get();
+  if (t.open_ev && hipEventRecord(t.open_ev, st) != hipSuccess) t.failed = true;
+}
+void timing_end(hipStream_t st) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on || !t.open_ev) return;
+  hipEvent_t b = t.get();
+  if (b && hipEventRecord(b, st) != hipSuccess) t.failed = true;
+  t.pending.push_back({t.open_name, t.open_ev, b});
+  t.open_ev = nullptr;
+}
+}  // namespace kda
+
 extern "C" {
+
+void kda_timing_enable(int enable) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.on = enable != 0;
+  if (t.on) {
+    for (auto& p : t.pending) {
+      t.pool.push_back(p.a);
+      t.pool.push_back(p.b);
+    }
+    t.pending.clear();
+    t.totals.clear();
+    t.order.clear();
+    t.failed = false;
+  }
+}
+
+int kda_timing_read(int max_entries, const char** names, double* total_ms, int* launches) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (auto& p : t.pending) {
+    float ms = 0.f;
+    if (!p.a || !p.b || hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess)
+      t.failed = true;
+    auto it = t.totals.find(p.name);
+    if (it == t.totals.end()) {
+      t.order.push_back(p.name);
+      it = t.totals.emplace(p.name, std::make_pair(0.0, 0)).first;
+    }
+    it->second.first += ms;
+    it->second.second += 1;
+    t.pool.push_back(p.a);
+    t.pool.push_back(p.b);
+  }
+  t.pending.clear();
+  if (t.failed) return -1;
+  int n = 0;
+  for (const char* nm : t.order) {
+    if (n >= max_entries) break;
+    const auto& v = t.totals[nm];
+    if (names) names[n] = nm;
+    if (total_ms) total_ms[n] = v.first;
+    if (launches) launches[n] = v.second;
+    ++n;
+  }
+  return n;
+}
+
 
 const char* kda_status_string(kda_status s) {
   switch (s) {
@@ -244,6 +362,7 @@ kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* 
   const size_t es = d->dtype == KDA_BF16 ? 2 : 4, eo = d->out_dtype == KDA_BF16 ? 2 : 4;
   if ((beta && (uintptr_t)beta % es) || (dbeta && (uintptr_t)dbeta % eo)) return KDA_ERROR_MISALIGNED;
   if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_MISALIGNED;
+  if (d->dtype == KDA_F32 && d->dk == 128) return KDA_ERROR_NOT_SUPPORTED;  // fp32 backward: dk = 64 only
   const Plan p = make_plan(d, true, N, mc);
   if (!workspace || workspace_bytes < p.total) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);

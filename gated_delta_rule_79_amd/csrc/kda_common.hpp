@@ -26,7 +26,17 @@ constexpr int CH = 64;
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // raw 16-byte vector (native, so it stays in registers)
+
+// MFMA operand type of the intermediates for a given input type: fp16 for bf16
+// inputs (11-bit significand, same MFMA rate as bf16; every intermediate it
+// carries is bounded by the inputs' magnitudes), fp32 for the fp32 path.
+template <typename E> struct OpOf { using T = f16; };
+template <> struct OpOf<float> { using T = float; };
 
 struct ChunkInfo {
   int32_t seq;  // sequence index
@@ -40,9 +50,11 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 __device__ __forceinline__ float f32(float x) { return x; }
 __device__ __forceinline__ float f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float f32(f16 x) { return (float)x; }
 template <typename E> __device__ __forceinline__ E cvt(float x);
 template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 cvt<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ f16 cvt<f16>(float x) { return (f16)x; }     // RNE
 
 // Row padding of LDS arrays, in elements (16 bytes).
 template <typename E> constexpr int PADE = 16 / (int)sizeof(E);
@@ -52,6 +64,7 @@ template <typename E> constexpr int PADE = 16 / (int)sizeof(E);
 // ---------------------------------------------------------------------------
 template <typename E> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<f16> { f16x8 v; };
 template <> struct Frag<float> { float v[8]; };
 
 // 8 consecutive elements p[row*ld + k0 .. +7]; (row*ld + k0) must be a multiple of 16/sizeof(E)/... 16B aligned.
@@ -59,6 +72,11 @@ template <typename E> __device__ __forceinline__ Frag<E> frag_row(const E* p, in
 template <> __device__ __forceinline__ Frag<bf16> frag_row<bf16>(const bf16* p, int ld, int row, int k0) {
   Frag<bf16> f;
   f.v = *reinterpret_cast<const bf16x8*>(p + row * ld + k0);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<f16> frag_row<f16>(const f16* p, int ld, int row, int k0) {
+  Frag<f16> f;
+  f.v = *reinterpret_cast<const f16x8*>(p + row * ld + k0);
   return f;
 }
 template <> __device__ __forceinline__ Frag<float> frag_row<float>(const float* p, int ld, int row, int k0) {
@@ -87,6 +105,9 @@ template <typename E> __device__ __forceinline__ Frag<E> frag_from(const float (
 __device__ __forceinline__ f32x4 mma(const Frag<bf16>& a, const Frag<bf16>& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mma(const Frag<f16>& a, const Frag<f16>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 c) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
@@ -108,9 +129,9 @@ template <typename E> __device__ __forceinline__ SFrag<E> sfrag_from(const float
   if constexpr (sizeof(E) == 2) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bf16 h = (bf16)x[j];
+      const E h = (E)x[j];
       s.hi.v[j] = h;
-      s.lo.v[j] = (bf16)(x[j] - (float)h);
+      s.lo.v[j] = (E)(x[j] - (float)h);
     }
   } else {
 #pragma unroll
@@ -132,6 +153,20 @@ template <typename E> __device__ __forceinline__ SFrag<E> sfrag_pair(const E* hi
   if constexpr (sizeof(E) == 2) s.lo = frag_row<E>(lo, ld, row, k0);
   return s;
 }
+// 8 consecutive-k elements down a column of hi/lo arrays stored [k][col].
+template <typename E> __device__ __forceinline__ SFrag<E> sfrag_col_pair(const E* hi, const E* lo, int ld, int col, int k0) {
+  SFrag<E> s;
+  s.hi = frag_col<E>(hi, ld, col, k0);
+  if constexpr (sizeof(E) == 2) s.lo = frag_col<E>(lo, ld, col, k0);
+  return s;
+}
+// 8 consecutive-k fp32 values down a column [k][col], split.
+template <typename E> __device__ __forceinline__ SFrag<E> sfrag_col_f32(const float* p, int ld, int col, int k0) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = p[(k0 + j) * ld + col];
+  return sfrag_from<E>(x);
+}
 template <typename E> __device__ __forceinline__ f32x4 mma_ss(const SFrag<E>& a, const SFrag<E>& b, f32x4 c) {
   if constexpr (sizeof(E) == 2) {
     c = mma(a.lo, b.hi, c);
@@ -150,10 +185,10 @@ template <typename E> __device__ __forceinline__ f32x4 mma_ps(const Frag<E>& a, 
 // Write 4 fp32 values as a split pair into two E arrays (contiguous 4 elements each).
 template <typename E> __device__ __forceinline__ void store4_split(E* hi, E* lo, float a, float b, float c, float d) {
   if constexpr (sizeof(E) == 2) {
-    const bf16 ha = (bf16)a, hb = (bf16)b, hc = (bf16)c, hd = (bf16)d;
-    *reinterpret_cast<bf16x4*>(hi) = bf16x4{ha, hb, hc, hd};
-    *reinterpret_cast<bf16x4*>(lo) = bf16x4{(bf16)(a - (float)ha), (bf16)(b - (float)hb), (bf16)(c - (float)hc),
-                                            (bf16)(d - (float)hd)};
+    typedef E v4 __attribute__((ext_vector_type(4)));
+    const E ha = (E)a, hb = (E)b, hc = (E)c, hd = (E)d;
+    *reinterpret_cast<v4*>(hi) = v4{ha, hb, hc, hd};
+    *reinterpret_cast<v4*>(lo) = v4{(E)(a - (float)ha), (E)(b - (float)hb), (E)(c - (float)hc), (E)(d - (float)hd)};
   } else {
     *reinterpret_cast<f32x4*>(hi) = f32x4{a, b, c, d};
   }
@@ -201,7 +236,7 @@ struct TileCopy {
   static constexpr int VPR = COLS * (int)sizeof(E) / 16;  // vectors per row
   static constexpr int NV = ROWS * VPR;
   static constexpr int PER = (NV + NT - 1) / NT;
-  uint4 r[PER];
+  u32x4 r[PER];
   __device__ __forceinline__ void load(const E* __restrict__ src, size_t src_ld) {
     static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
       // threads past the tile re-read vector 0 (always in bounds) and skip the store,
@@ -209,7 +244,7 @@ struct TileCopy {
       const int v0 = threadIdx.x + I * NT;
       const int v = (NV % NT == 0 || v0 < NV) ? v0 : 0;
       const int row = v / VPR, cv = v % VPR;
-      r[I] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src + row * src_ld) + cv * 16);
+      r[I] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src + row * src_ld) + cv * 16);
     });
   }
   __device__ __forceinline__ void store(E* dst, int dst_ld) const {
@@ -217,7 +252,7 @@ struct TileCopy {
       const int v = threadIdx.x + I * NT;
       if (NV % NT == 0 || v < NV) {
         const int row = v / VPR, cv = v % VPR;
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + row * dst_ld) + cv * 16) = r[I];
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst + row * dst_ld) + cv * 16) = r[I];
       }
     });
   }
@@ -238,27 +273,89 @@ __device__ __forceinline__ void copy_out(E* __restrict__ dst, size_t dst_ld, con
   constexpr int NV = ROWS * VPR;
   for (int v = threadIdx.x; v < NV; v += NT) {
     const int row = v / VPR, cv = v % VPR;
-    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst + row * dst_ld) + cv * 16) =
-        *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src + row * src_ld) + cv * 16);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst + row * dst_ld) + cv * 16) =
+        *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src + row * src_ld) + cv * 16);
   }
+}
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+template <typename E> __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(E) == 4) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+  } else {
+    typedef E v4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<v4*>(p) = v4{(E)a, (E)b, (E)c, (E)d};
+  }
+}
+template <typename E> __device__ __forceinline__ void load4(const E* p, float (&x)[4]) {
+  if constexpr (sizeof(E) == 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+    x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+  } else {
+    typedef E v4 __attribute__((ext_vector_type(4)));
+    const v4 v = *reinterpret_cast<const v4*>(p);
+    x[0] = (float)v[0]; x[1] = (float)v[1]; x[2] = (float)v[2]; x[3] = (float)v[3];
+  }
+}
+// 8 consecutive elements from global memory as floats (zero when !valid).
+template <typename E> __device__ __forceinline__ void load8(const E* p, bool valid, float (&x)[8]) {
+  if constexpr (sizeof(E) == 2) {
+    typedef E v8 __attribute__((ext_vector_type(8)));
+    v8 v = {};
+    if (valid) v = *reinterpret_cast<const v8*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+  } else {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      a = *reinterpret_cast<const f32x4*>(p);
+      b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { x[j] = a[j]; x[j + 4] = b[j]; }
+  }
+}
+
+// Map a flat block id to (unit, slice) so that all value slices of a unit sit on
+// the same XCD (block ids are dealt to the 8 XCDs round robin) and share its L2.
+__device__ __forceinline__ bool xcd_unit(int bid, int nsl, int nunits, int& unit, int& slice) {
+  const int xcd = bid & 7, idx = bid >> 3;
+  slice = idx % nsl;
+  unit = (idx / nsl) * 8 + xcd;
+  return unit < nunits;
 }
 
 // ---------------------------------------------------------------------------
 // workspace layout shared by the host planner and the kernels
 // ---------------------------------------------------------------------------
 // Per (chunk, head) blocks, chunk-major so one head's chunks are strided by H.
-// Element counts per block; the element type of each array is given beside it
-// (fp32 arrays feed split operands).
+// Element counts per block; OP = OpOf<E>::T unless another type is given.
 template <typename E, int DK, int DV>
 struct WsBlock {
-  static constexpr size_t W = (size_t)CH * DK;     // W   [CH][DK]   E
-  static constexpr size_t KHT = (size_t)DK * CH;   // Kh^T[DK][CH]   float
-  static constexpr size_t QT = (size_t)CH * DK;    // Qt  [CH][DK]   E
-  static constexpr size_t UT = (size_t)DV * CH;    // U~^T[DV][CH]   float
-  static constexpr size_t AQK = (size_t)CH * CH;   // Aqk [CH][CH]   float
+  static constexpr size_t W = (size_t)CH * DK;     // W   [CH][DK]   OP
+  static constexpr size_t KHT = (size_t)DK * CH;   // Kh^T[DK][CH]   OP
+  static constexpr size_t QT = (size_t)CH * DK;    // Qt  [CH][DK]   OP
+  static constexpr size_t UT = (size_t)DV * CH;    // U~^T[DV][CH]   OP
+  static constexpr size_t AQK = (size_t)CH * CH;   // Aqk [CH][CH]   OP
   static constexpr size_t TT = (size_t)CH * CH;    // T   [CH][CH]   float (backward only)
   static constexpr size_t GAM = DK;                // Gamma_C [DK]   float
-  static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk, [DV][DK] float (backward only)
+  // backward only
+  static constexpr size_t UTF = (size_t)DV * CH;   // U~^T [DV][CH]   float
+  static constexpr size_t G = (size_t)CH * CH;     // un-beta strict Gram [CH][CH]   float
+  static constexpr size_t KHF = (size_t)CH * DK;   // Kh  [CH][DK]   float
+  static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk [DV][DK]   OP
+  static constexpr size_t U = (size_t)DV * CH;     // U^T [DV][CH]   float
+  static constexpr size_t DS = (size_t)DK * DV;    // dS' [DV][DK]   float
+  static constexpr size_t DU = (size_t)DV * CH;    // dU^T [DV][CH]  float
+  static constexpr size_t DAQK = (size_t)CH * CH;  // float
+  static constexpr size_t DQS = (size_t)CH * DK;   // float
+  static constexpr size_t DKH = (size_t)CH * DK;   // float
+  static constexpr size_t DW = (size_t)CH * DK;    // float
+  static constexpr size_t DTU = (size_t)CH * CH;   // float
+  static constexpr size_t DGAM = DK;               // float
+  static constexpr size_t DBV = CH;                // float
 };
 
 }  // namespace kda

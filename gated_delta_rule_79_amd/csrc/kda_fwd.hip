@@ -87,47 +87,10 @@ __global__ __launch_bounds__(1024) void kda_chunk_map(const int32_t* __restrict_
 }
 
 hipError_t launch_chunk_map(const Args& a, hipStream_t st) {
-  hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(1024), 0, st, a.cu, a.N, a.T, a.chunks, a.seq_chunk0,
-                     a.max_chunks);
+  KDA_TIMED("kda_chunk_map", st,
+            hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(1024), 0, st, a.cu, a.N, a.T, a.chunks, a.seq_chunk0,
+                               a.max_chunks));
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// small helpers
-// ---------------------------------------------------------------------------
-template <typename E> __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d);
-template <> __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
-  bf16x4 o = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-  *reinterpret_cast<bf16x4*>(p) = o;
-}
-template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
-}
-template <typename E> __device__ __forceinline__ void load4(const E* p, float (&x)[4]);
-template <> __device__ __forceinline__ void load4<bf16>(const bf16* p, float (&x)[4]) {
-  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-  x[0] = (float)v[0]; x[1] = (float)v[1]; x[2] = (float)v[2]; x[3] = (float)v[3];
-}
-template <> __device__ __forceinline__ void load4<float>(const float* p, float (&x)[4]) {
-  const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-  x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
-}
-// 8 consecutive elements from global memory as floats (zero when !valid).
-template <typename E> __device__ __forceinline__ void load8(const E* p, bool valid, float (&x)[8]) {
-  if constexpr (sizeof(E) == 2) {
-    bf16x8 v = {};
-    if (valid) v = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
-  } else {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-      a = *reinterpret_cast<const f32x4*>(p);
-      b = *reinterpret_cast<const f32x4*>(p + 4);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { x[j] = a[j]; x[j + 4] = b[j]; }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -135,31 +98,33 @@ template <typename E> __device__ __forceinline__ void load8(const E* p, bool val
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 struct PrepLds {
-  static constexpr int P = PADE<E>;
+  using OP = typename OpOf<E>::T;
+  static constexpr int PE = PADE<E>, PO = PADE<OP>;
   static constexpr int LDG = DK + 4;   // float g[CH][LDG]
-  static constexpr int LDK = DK + P;   // E k[CH][LDK]
-  static constexpr int LDT = CH + P;   // E x[*][LDT]
+  static constexpr int LDK = DK + PE;  // E     k[CH][LDK]
+  static constexpr int LDT = CH + PO;  // OP    x[*][LDT]
   static constexpr int LDA = CH + 4;   // float A[CH][LDA]
   static constexpr size_t G = 0;
   static constexpr size_t K = G + (size_t)CH * LDG * 4;
   static constexpr size_t KPT = K + (size_t)CH * LDK * sizeof(E);
-  static constexpr size_t VT = KPT + (size_t)DK * LDT * sizeof(E);
-  static constexpr size_t A = VT + (size_t)DV * LDT * sizeof(E);
+  static constexpr size_t VT = KPT + (size_t)DK * LDT * sizeof(OP);
+  static constexpr size_t A = VT + (size_t)DV * LDT * sizeof(OP);
   static constexpr size_t TOT = A + (size_t)CH * LDA * 4;
   static constexpr size_t BETA = TOT + 4 * DK * 4;
   static constexpr size_t X = BETA + CH * 4;
   static constexpr size_t BYTES = X + 3 * 256 * 4;
   // aliases used once the Gram blocks are done
   static constexpr size_t T = G;     // float [CH][LDA]  (fits in g)
-  static constexpr size_t TE = K;    // E [CH][LDT]      (fits in k)
+  static constexpr size_t TE = K;    // OP    [CH][LDT]  (fits in k)
   static_assert((size_t)CH * LDA * 4 <= (size_t)CH * LDG * 4, "T alias");
-  static_assert((size_t)CH * LDT * sizeof(E) <= (size_t)CH * LDK * sizeof(E), "Te alias");
+  static_assert((size_t)CH * LDT * sizeof(OP) <= (size_t)CH * LDK * sizeof(E), "Te alias");
   static_assert(BYTES <= 163840, "prep LDS");
 };
 
 template <typename E, int DK, int DV, bool BWD>
 __global__ __launch_bounds__(256) void kda_prep(const Args a) {
   using L = PrepLds<E, DK, DV>;
+  using OP = typename L::OP;
   constexpr int NT = 256;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int j = blockIdx.x, h = blockIdx.y, H = a.H;
@@ -170,8 +135,8 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
 
   float* sG = reinterpret_cast<float*>(smem + L::G);
   E* sK = reinterpret_cast<E*>(smem + L::K);
-  E* sKpT = reinterpret_cast<E*>(smem + L::KPT);
-  E* sVT = reinterpret_cast<E*>(smem + L::VT);
+  OP* sKpT = reinterpret_cast<OP*>(smem + L::KPT);
+  OP* sVT = reinterpret_cast<OP*>(smem + L::VT);
   float* sA = reinterpret_cast<float*>(smem + L::A);
   float* sTot = reinterpret_cast<float*>(smem + L::TOT);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
@@ -186,44 +151,54 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
 
   using WB = WsBlock<E, DK, DV>;
   const size_t blk = (size_t)j * H + h;
-  E* wW = reinterpret_cast<E*>(a.wsW) + blk * WB::W;
-  float* wKhT = reinterpret_cast<float*>(a.wsKhT) + blk * WB::KHT;
-  E* wQt = reinterpret_cast<E*>(a.wsQt) + blk * WB::QT;
-  float* wUt = reinterpret_cast<float*>(a.wsUt) + blk * WB::UT;
-  float* wAqk = reinterpret_cast<float*>(a.wsAqk) + blk * WB::AQK;
+  OP* wW = reinterpret_cast<OP*>(a.wsW) + blk * WB::W;
+  OP* wKhT = reinterpret_cast<OP*>(a.wsKhT) + blk * WB::KHT;
+  OP* wQt = reinterpret_cast<OP*>(a.wsQt) + blk * WB::QT;
+  OP* wUt = reinterpret_cast<OP*>(a.wsUt) + blk * WB::UT;
+  OP* wAqk = reinterpret_cast<OP*>(a.wsAqk) + blk * WB::AQK;
   float* wGam = a.wsGam + blk * WB::GAM;
 
-  // ---- 1. cumulative log-decay g (fp32), k rows, v^T, beta
+  // ---- 1. all global loads of the chunk are issued here, before any use, so
+  // their latencies overlap.  Wave w loads token rows 16w..16w+15; lane
+  // (r16, q4) holds 8 consecutive channels 32*ks + 8*q4 of row 16w + r16.
+  constexpr int NKS = DK / 32, NVS = DV / 32;
+  const int r = 16 * w + r16;
+  const bool rv_ok = r < len;
+  float xq[NKS][8], xk[NKS][8], xl[NKS][8], xv[NVS][8];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    load8<E>(qh + r * rk + 32 * ks + 8 * q4, rv_ok, xq[ks]);
+    load8<E>(kh + r * rk + 32 * ks + 8 * q4, rv_ok, xk[ks]);
+    load8<E>(lh + r * rk + 32 * ks + 8 * q4, rv_ok, xl[ks]);
+  }
+#pragma unroll
+  for (int vs = 0; vs < NVS; ++vs) load8<E>(vh + r * rv + 32 * vs + 8 * q4, rv_ok, xv[vs]);
+  const float bet = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
+  if (tid < CH) sBeta[tid] = bet;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int c0 = 32 * ks + 8 * q4;
+    *reinterpret_cast<f32x4*>(sG + r * L::LDG + c0) = f32x4{xl[ks][0], xl[ks][1], xl[ks][2], xl[ks][3]};
+    *reinterpret_cast<f32x4*>(sG + r * L::LDG + c0 + 4) = f32x4{xl[ks][4], xl[ks][5], xl[ks][6], xl[ks][7]};
+    store4<E>(sK + r * L::LDK + c0, xk[ks][0], xk[ks][1], xk[ks][2], xk[ks][3]);
+    store4<E>(sK + r * L::LDK + c0 + 4, xk[ks][4], xk[ks][5], xk[ks][6], xk[ks][7]);
+  }
+#pragma unroll
+  for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sVT[(32 * vs + 8 * q4 + i) * L::LDT + r] = cvt<OP>(xv[vs][i]);
+  __syncthreads();
+  // cumulative sum over tokens, in place: thread (channel c, part s) scans RPS rows
   {
     constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
     const int c = tid % DK, s = tid / DK;
     float acc = 0.f;
-    for (int r = s * RPS; r < (s + 1) * RPS; ++r) {
-      acc += r < len ? f32(lh[r * rk + c]) : 0.f;
-      sG[r * L::LDG + c] = acc;
+#pragma unroll 8
+    for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
+      acc += sG[rr * L::LDG + c];
+      sG[rr * L::LDG + c] = acc;
     }
     sTot[s * DK + c] = acc;
-  }
-  if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
-  {
-    constexpr int EPV = 16 / (int)sizeof(E);
-    constexpr int VPR = DK / EPV, NV = CH * VPR;
-    for (int v = tid; v < NV; v += NT) {
-      const int r = v / VPR, cv = v % VPR;
-      uint4 x = {0u, 0u, 0u, 0u};
-      if (r < len) x = *reinterpret_cast<const uint4*>(kh + r * rk + cv * EPV);
-      *reinterpret_cast<uint4*>(sK + r * L::LDK + cv * EPV) = x;
-    }
-  }
-  {
-    constexpr int VPR = DV / 8, NV = CH * VPR;
-    for (int v = tid; v < NV; v += NT) {
-      const int r = v / VPR, c0 = (v % VPR) * 8;
-      float x[8];
-      load8<E>(vh + r * rv + c0, r < len, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sVT[(c0 + i) * L::LDT + r] = cvt<E>(x[i]);
-    }
   }
   __syncthreads();
   {
@@ -232,57 +207,66 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
     if (s > 0) {
       float off = 0.f;
       for (int s2 = 0; s2 < s; ++s2) off += sTot[s2 * DK + c];
-      for (int r = s * RPS; r < (s + 1) * RPS; ++r) sG[r * L::LDG + c] += off;
+      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
     }
   }
   __syncthreads();
 
-  // ---- 2. elementwise: K+^T (LDS), Kh^T, Qt, Gamma_C (workspace)
+  // ---- 2. elementwise: K+^T (LDS), Kh^T, Qt (own rows, from registers), Gamma_C
   {
-    const int r = tid & (CH - 1);
+    const int rr = tid & (CH - 1);
     for (int c = tid / CH; c < DK; c += NT / CH) {
-      const float g = sG[r * L::LDG + c];
+      const float g = sG[rr * L::LDG + c];
       const float gl = sG[(CH - 1) * L::LDG + c];
-      const float kv = f32(sK[r * L::LDK + c]);
-      sKpT[c * L::LDT + r] = cvt<E>(kv * __expf(g));
-      wKhT[c * CH + r] = kv * __expf(gl - g);
+      const float kv = f32(sK[rr * L::LDK + c]);
+      sKpT[c * L::LDT + rr] = cvt<OP>(kv * __expf(g));
+      wKhT[c * CH + rr] = cvt<OP>(kv * __expf(gl - g));
     }
-    constexpr int VPR = DK / 8, NV = CH * VPR;
-    for (int v = tid; v < NV; v += NT) {
-      const int rr = v / VPR, c0 = (v % VPR) * 8;
-      float x[8];
-      load8<E>(qh + rr * rk + c0, rr < len, x);
-      float y[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = x[i] * __expf(sG[rr * L::LDG + c0 + i]);
-      store4<E>(wQt + rr * DK + c0, y[0], y[1], y[2], y[3]);
-      store4<E>(wQt + rr * DK + c0 + 4, y[4], y[5], y[6], y[7]);
-    }
-    for (int c = tid; c < DK; c += NT) wGam[c] = __expf(sG[(CH - 1) * L::LDG + c]);
-  }
-
-  // ---- 3. decayed Gram blocks: wave w owns row block a = w
-  {
-    const int ab = w;
-    const int ref = 16 * ab + 8;
-    const int r = 16 * ab + r16;
-    // the gated factors are split operands: their rounding would otherwise
-    // dominate the error of the intra-chunk terms
-    constexpr int NKS = DK / 32;
-    SFrag<E> fk[NKS], fq[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int c0 = 32 * ks + 8 * q4;
-      float xq[8], xk[8];
-      load8<E>(qh + r * rk + c0, r < len, xq);
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = xq[ks][i] * __expf(sG[r * L::LDG + c0 + i]);
+      store4<OP>(wQt + r * DK + c0, y[0], y[1], y[2], y[3]);
+      store4<OP>(wQt + r * DK + c0 + 4, y[4], y[5], y[6], y[7]);
+    }
+    for (int c = tid; c < DK; c += NT) wGam[c] = __expf(sG[(CH - 1) * L::LDG + c]);
+    if constexpr (BWD) {
+      // Kh token-major in fp32 (the reverse pass multiplies it as a split operand)
+      float* wKhF = a.wsKhF + blk * WB::KHF;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = 32 * ks + 8 * q4;
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          y[i] = xk[ks][i] * __expf(sG[(CH - 1) * L::LDG + c0 + i] - sG[r * L::LDG + c0 + i]);
+        *reinterpret_cast<f32x4*>(wKhF + r * DK + c0) = f32x4{y[0], y[1], y[2], y[3]};
+        *reinterpret_cast<f32x4*>(wKhF + r * DK + c0 + 4) = f32x4{y[4], y[5], y[6], y[7]};
+      }
+    }
+  }
+
+  // ---- 3. decayed Gram blocks: wave w owns row block a = w.  The gated
+  // factors can exceed fp16 range, so they are split bf16 (fp32 inputs: fp32).
+  {
+    const int ab = w;
+    const int ref = 16 * ab + 8;
+    using SE = typename std::conditional<sizeof(E) == 4, float, bf16>::type;
+    SFrag<SE> fk[NKS], fq[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int c0 = 32 * ks + 8 * q4;
+      float yq[8], yk[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float e = __expf(sG[r * L::LDG + c0 + i] - sG[ref * L::LDG + c0 + i]);
-        xk[i] = f32(sK[r * L::LDK + c0 + i]) * e;
-        xq[i] *= e;
+        yk[i] = xk[ks][i] * e;
+        yq[i] = xq[ks][i] * e;
       }
-      fk[ks] = sfrag_from<E>(xk);
-      fq[ks] = sfrag_from<E>(xq);
+      fk[ks] = sfrag_from<SE>(yk);
+      fq[ks] = sfrag_from<SE>(yq);
     }
     for (int b = 0; b <= ab; ++b) {
       f32x4 akk = zero4(), aqk = zero4();
@@ -294,7 +278,7 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
           xr[u] = f32(sK[i * L::LDK + c0 + u]) * __expf(sG[ref * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
-        const SFrag<E> fr = sfrag_from<E>(xr);
+        const SFrag<SE> fr = sfrag_from<SE>(xr);
         akk = mma_ss(fk[ks], fr, akk);
         aqk = mma_ss(fq[ks], fr, aqk);
       }
@@ -302,7 +286,8 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
       for (int ii = 0; ii < 4; ++ii) {
         const int rr = 16 * ab + 4 * q4 + ii, cc = 16 * b + r16;
         sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[ii] : 0.f;
-        wAqk[rr * CH + cc] = cc <= rr ? aqk[ii] : 0.f;
+        wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[ii] : 0.f);
+        if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[ii] : 0.f;
       }
     }
     for (int b = ab + 1; b < 4; ++b) {
@@ -310,7 +295,8 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
       for (int ii = 0; ii < 4; ++ii) {
         const int rr = 16 * ab + 4 * q4 + ii, cc = 16 * b + r16;
         sA[rr * L::LDA + cc] = 0.f;
-        wAqk[rr * CH + cc] = 0.f;
+        wAqk[rr * CH + cc] = cvt<OP>(0.f);
+        if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = 0.f;
       }
     }
   }
@@ -360,11 +346,11 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
   }
 
   // ---- 5. Te = T diag(beta) in the operand type; W = Te K+, U~ = Te V
-  E* sTe = reinterpret_cast<E*>(smem + L::TE);
+  OP* sTe = reinterpret_cast<OP*>(smem + L::TE);
   for (int o = tid; o < CH * CH; o += NT) {
     const int rr = o / CH, cc = o % CH;
     const float t = sT[rr * L::LDA + cc];
-    sTe[rr * L::LDT + cc] = cvt<E>(t * sBeta[cc]);
+    sTe[rr * L::LDT + cc] = cvt<OP>(t * sBeta[cc]);
     if constexpr (BWD) reinterpret_cast<float*>(a.wsT)[blk * WB::TT + o] = t;
   }
   __syncthreads();
@@ -373,23 +359,26 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
     constexpr int NTI = (CH / 16) * (DK / 16);
     for (int t = w; t < NTI; t += 4) {
       const int mt = t % (CH / 16), nt = t / (CH / 16);
-      const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<E>(sKpT, L::LDT, 16 * nt + rr, k); },
-                                    [&](int rr, int k) { return frag_row<E>(sTe, L::LDT, 16 * mt + rr, k); },
+      const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sKpT, L::LDT, 16 * nt + rr, k); },
+                                    [&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); },
                                     zero4());
-      store4<E>(wW + (16 * mt + r16) * DK + 16 * nt + 4 * q4, acc[0], acc[1], acc[2], acc[3]);
+      store4<OP>(wW + (16 * mt + r16) * DK + 16 * nt + 4 * q4, acc[0], acc[1], acc[2], acc[3]);
     }
     // U~ tiles: C[tok][dv]; lane holds 4 consecutive tokens of one value column -> U~^T rows
+    // (fp32 for the backward, where its rounding would reach the gradients)
     constexpr int NTU = (CH / 16) * (DV / 16);
     for (int t = w; t < NTU; t += 4) {
       const int mt = t % (CH / 16), nt = t / (CH / 16);
-      const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<E>(sTe, L::LDT, 16 * mt + rr, k); },
-                                    [&](int rr, int k) { return frag_row<E>(sVT, L::LDT, 16 * nt + rr, k); },
+      const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); },
+                                    [&](int rr, int k) { return frag_row<OP>(sVT, L::LDT, 16 * nt + rr, k); },
                                     zero4());
-      *reinterpret_cast<f32x4*>(wUt + (16 * nt + r16) * CH + 16 * mt + 4 * q4) = acc;
+      if constexpr (BWD)
+        *reinterpret_cast<f32x4*>(a.wsUtF + blk * WB::UTF + (16 * nt + r16) * CH + 16 * mt + 4 * q4) = acc;
+      else
+        store4<OP>(wUt + (16 * nt + r16) * CH + 16 * mt + 4 * q4, acc[0], acc[1], acc[2], acc[3]);
     }
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // sequential state pass (forward outputs, or the per-chunk states for backward)
@@ -397,40 +386,32 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
 // One work-group walks the chunks of one (sequence, head, value slice of DVS
 // columns) in order.  Eight waves: waves 0-3 form U = U~ - W S for token tile
 // w, waves 4-7 form Qt S and then the output rows of tile w-4; every wave
-// updates one or more 16x16 tiles of S.  S stays in fp32 registers; it is
-// written to LDS as a split operand for the two products that read it.
+// updates its 16x16 tiles of S.  S stays in fp32 registers; each chunk it is
+// copied to LDS in the operand type for the products that read it.  The next
+// chunk's matrices are loaded into registers while the current one computes.
 template <typename E, int DK, int DV, int DVS, bool OUT>
 struct StateLds {
-  static constexpr int P = PADE<E>;
+  using OP = typename OpOf<E>::T;
+  static constexpr int P = PADE<OP>;
   static constexpr int LDK = DK + P;
   static constexpr int LDT = CH + P;
-  static constexpr int LDF = CH + 4;
-  static constexpr size_t W = 0;                                                 // E     [CH][LDK]
-  static constexpr size_t QT = W + (size_t)CH * LDK * sizeof(E);                 // E     [CH][LDK]  (OUT)
-  static constexpr size_t KHT = QT + (OUT ? (size_t)CH * LDK * sizeof(E) : 0);   // float [DK][LDF]
-  static constexpr size_t AQK = KHT + (size_t)DK * LDF * 4;                      // float [CH][LDF]  (OUT)
-  static constexpr size_t UT = AQK + (OUT ? (size_t)CH * LDF * 4 : 0);           // float [DVS][CH]
-  static constexpr size_t GAM = UT + (size_t)DVS * CH * 4;                       // float [DK]
-  static constexpr size_t STH = GAM + (size_t)DK * 4;                            // E     [DVS][LDK]
-  static constexpr size_t STL = STH + (size_t)DVS * LDK * sizeof(E);             // E     [DVS][LDK]
-  static constexpr size_t ULH = STL + (size_t)DVS * LDK * sizeof(E);             // E     [DVS][LDT]
-  static constexpr size_t ULL = ULH + (size_t)DVS * LDT * sizeof(E);             // E     [DVS][LDT]
-  static constexpr size_t BYTES = ULL + (size_t)DVS * LDT * sizeof(E);
+  static constexpr size_t W = 0;                                                  // OP [CH][LDK]
+  static constexpr size_t QT = W + (size_t)CH * LDK * sizeof(OP);                 // OP [CH][LDK]  (OUT)
+  static constexpr size_t KHT = QT + (OUT ? (size_t)CH * LDK * sizeof(OP) : 0);   // OP [DK][LDT]
+  static constexpr size_t AQK = KHT + (size_t)DK * LDT * sizeof(OP);              // OP [CH][LDT]  (OUT)
+  using UTT = typename std::conditional<OUT, OP, float>::type;                   // U~ element type
+  static constexpr size_t UT = AQK + (OUT ? (size_t)CH * LDT * sizeof(OP) : 0);   // UTT [DVS][CH]
+  static constexpr size_t GAM = UT + (size_t)DVS * CH * sizeof(UTT);              // float [DK]
+  static constexpr size_t ST = GAM + (size_t)DK * 4;                              // OP [DVS][LDK]  S^T
+  static constexpr size_t UL = ST + (size_t)DVS * LDK * sizeof(OP);               // OP [DVS][LDT]  U^T
+  static constexpr size_t BYTES = UL + (size_t)DVS * LDT * sizeof(OP);
   static_assert(BYTES <= 163840, "state LDS");
 };
 
-// Map a flat block id to (unit, slice) so that all value slices of a unit sit on
-// the same XCD (block ids are dealt to the 8 XCDs round robin) and share its L2.
-__device__ __forceinline__ bool xcd_unit(int bid, int nsl, int nunits, int& unit, int& slice) {
-  const int xcd = bid & 7, idx = bid >> 3;
-  slice = idx % nsl;
-  unit = (idx / nsl) * 8 + xcd;
-  return unit < nunits;
-}
-
 template <typename E, typename O, int DK, int DV, int DVS, bool OUT>
-__global__ __launch_bounds__(512) void kda_state(const Args a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void kda_state(const Args a) {
   using L = StateLds<E, DK, DV, DVS, OUT>;
+  using OP = typename L::OP;
   using WB = WsBlock<E, DK, DV>;
   constexpr int NT = 512, NSL = DV / DVS;
   constexpr int MTS = DK / 16, NTS = DVS / 16;   // state tiles (channel x column)
@@ -444,29 +425,36 @@ __global__ __launch_bounds__(512) void kda_state(const Args a) {
   const int n0 = sl * DVS;
   const int l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
   const int c0 = a.seq_chunk0[seq], nch = a.seq_chunk0[seq + 1] - c0;
+  // token range of the sequence, from its first and last chunk (read once, so
+  // the only global loads inside the loop are the prefetch of the next chunk)
+  int tbeg = 0, tend = 0;
+  if (nch > 0) {
+    const ChunkInfo first = a.chunks[c0], last = a.chunks[c0 + nch - 1];
+    tbeg = first.t0;
+    tend = last.t0 + last.len;
+  }
 
-  E* sW = reinterpret_cast<E*>(smem + L::W);
-  E* sQt = reinterpret_cast<E*>(smem + L::QT);
-  float* sKhT = reinterpret_cast<float*>(smem + L::KHT);
-  float* sAqk = reinterpret_cast<float*>(smem + L::AQK);
-  float* sUt = reinterpret_cast<float*>(smem + L::UT);
+  OP* sW = reinterpret_cast<OP*>(smem + L::W);
+  OP* sQt = reinterpret_cast<OP*>(smem + L::QT);
+  OP* sKhT = reinterpret_cast<OP*>(smem + L::KHT);
+  OP* sAqk = reinterpret_cast<OP*>(smem + L::AQK);
+  using UTT = typename L::UTT;
+  UTT* sUt = reinterpret_cast<UTT*>(smem + L::UT);
   float* sGam = reinterpret_cast<float*>(smem + L::GAM);
-  E* sSTh = reinterpret_cast<E*>(smem + L::STH);
-  E* sSTl = reinterpret_cast<E*>(smem + L::STL);
-  E* sULh = reinterpret_cast<E*>(smem + L::ULH);
-  E* sULl = reinterpret_cast<E*>(smem + L::ULL);
+  OP* sST = reinterpret_cast<OP*>(smem + L::ST);
+  OP* sUL = reinterpret_cast<OP*>(smem + L::UL);
 
   // kernel-argument fields are copied to locals so the argument block never
   // has its address taken (that would place it in scratch)
-  const E* gW = reinterpret_cast<const E*>(a.wsW);
-  const E* gQt = reinterpret_cast<const E*>(a.wsQt);
-  const float* gAqk = reinterpret_cast<const float*>(a.wsAqk);
-  const float* gKhT = reinterpret_cast<const float*>(a.wsKhT);
-  const float* gUt = reinterpret_cast<const float*>(a.wsUt);
+  const OP* gW = reinterpret_cast<const OP*>(a.wsW);
+  const OP* gQt = reinterpret_cast<const OP*>(a.wsQt);
+  const OP* gAqk = reinterpret_cast<const OP*>(a.wsAqk);
+  const OP* gKhT = reinterpret_cast<const OP*>(a.wsKhT);
+  const UTT* gUt = OUT ? reinterpret_cast<const UTT*>(a.wsUt) : reinterpret_cast<const UTT*>(a.wsUtF);
   const float* gGam = a.wsGam;
-  float* gS = reinterpret_cast<float*>(a.wsS);
+  OP* gS = reinterpret_cast<OP*>(a.wsS);
+  float* gU = a.wsU;
   O* gOut = reinterpret_cast<O*>(a.out);
-  const ChunkInfo* gChunks = a.chunks;
   const float scale = a.scale;
   const float* gInit = a.init;
   float* gFinal = a.final_state;
@@ -483,59 +471,57 @@ __global__ __launch_bounds__(512) void kda_state(const Args a) {
     }
   }
 
-  // staging registers for the next chunk (separate objects so each stays in registers)
-  TileCopy<E, CH, DK, NT> pw;
-  TileCopy<E, (OUT ? CH : 1), (OUT ? DK : 16 / sizeof(E)), NT> pqt;
-  TileCopy<float, DK, CH, NT> pkht;
-  TileCopy<float, (OUT ? CH : 1), (OUT ? CH : 4), NT> paqk;
-  TileCopy<float, DVS, CH, NT> put;
-  TileCopy<float, 1, DK, NT> pgam;
+  // Staging registers: two sets, so chunk n+2 is in flight while chunk n+1
+  // waits in registers and chunk n is in LDS (loads of two chunks overlap the
+  // compute of one).  Separate objects of a native vector type stay in VGPRs.
+  struct Stage {
+    TileCopy<OP, CH, DK, NT> w;
+    TileCopy<OP, (OUT ? CH : 1), (OUT ? DK : 16 / sizeof(OP)), NT> qt;
+    TileCopy<OP, DK, CH, NT> kht;
+    TileCopy<OP, (OUT ? CH : 1), (OUT ? CH : 16 / sizeof(OP)), NT> aqk;
+    TileCopy<UTT, DVS, CH, NT> ut;
+    TileCopy<float, 1, DK, NT> gam;
+  };
+  Stage st0, st1;
   auto blk_of = [&](int n) { return (size_t)(c0 + n) * H + h; };
-#define KDA_PRE_LOAD(n_)                                        \
-  do {                                                          \
-    const size_t b_ = blk_of(n_);                               \
-    pw.load(gW + b_ * WB::W, DK);                               \
-    if constexpr (OUT) {                                        \
-      pqt.load(gQt + b_ * WB::QT, DK);                          \
-      paqk.load(gAqk + b_ * WB::AQK, CH);                       \
-    }                                                           \
-    pkht.load(gKhT + b_ * WB::KHT, CH);                         \
-    put.load(gUt + b_ * WB::UT + (size_t)n0 * CH, CH);          \
-    pgam.load(gGam + b_ * WB::GAM, DK);                         \
-  } while (0)
-#define KDA_PRE_STORE()                                         \
-  do {                                                          \
-    pw.store(sW, L::LDK);                                       \
-    if constexpr (OUT) {                                        \
-      pqt.store(sQt, L::LDK);                                   \
-      paqk.store(sAqk, L::LDF);                                 \
-    }                                                           \
-    pkht.store(sKhT, L::LDF);                                   \
-    put.store(sUt, CH);                                         \
-    pgam.store(sGam, DK);                                       \
-  } while (0)
+  auto stage_load = [&](Stage& p, int n) __attribute__((always_inline)) {
+    const size_t b = blk_of(n);
+    p.w.load(gW + b * WB::W, DK);
+    if constexpr (OUT) {
+      p.qt.load(gQt + b * WB::QT, DK);
+      p.aqk.load(gAqk + b * WB::AQK, CH);
+    }
+    p.kht.load(gKhT + b * WB::KHT, CH);
+    p.ut.load(gUt + b * WB::UT + (size_t)n0 * CH, CH);  // UT == UTF element count
+    p.gam.load(gGam + b * WB::GAM, DK);
+  };
+  auto stage_store = [&](const Stage& p) __attribute__((always_inline)) {
+    p.w.store(sW, L::LDK);
+    if constexpr (OUT) {
+      p.qt.store(sQt, L::LDK);
+      p.aqk.store(sAqk, L::LDT);
+    }
+    p.kht.store(sKhT, L::LDT);
+    p.ut.store(sUt, CH);
+    p.gam.store(sGam, DK);
+  };
 
-  if (nch > 0) {
-    KDA_PRE_LOAD(0);
-    KDA_PRE_STORE();
-  }
   const size_t ro = (size_t)H * DV;
-  for (int n = 0; n < nch; ++n) {
-    // prefetch the next chunk into registers (the last chunk re-reads itself,
-    // so the staging registers are defined on every path)
-    KDA_PRE_LOAD(n + 1 < nch ? n + 1 : n);
+  // one chunk: LDS holds chunk n; `ld` receives chunk n+2 (clamped, so its
+  // registers are always defined); `nx` holds chunk n+1 and goes to LDS at the end
+  auto chunk = [&](int n, Stage& ld, const Stage& nx) __attribute__((always_inline)) {
+    stage_load(ld, min(n + 2, nch - 1));
 
-    // S -> LDS as a split operand, transposed ([column][channel])
+    // S -> LDS in the operand type, transposed ([column][channel])
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int t = w + 8 * i, mt = t % MTS, nt = t / MTS;
       if (t < NST) {
-        const int off = (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4;
-        store4_split<E>(sSTh + off, sSTl + off, S[i][0], S[i][1], S[i][2], S[i][3]);
+        store4<OP>(sST + (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4, S[i][0], S[i][1], S[i][2], S[i][3]);
         if constexpr (!OUT) {
-          // backward needs the state entering every chunk: float [DV][DK] per chunk-head
-          float* dst = gS + blk_of(n) * WB::S + (size_t)(n0 + 16 * nt + r16) * DK + 16 * mt + 4 * q4;
-          *reinterpret_cast<f32x4*>(dst) = S[i];
+          // backward needs the state entering every chunk: OP [DV][DK] per chunk-head
+          OP* dst = gS + blk_of(n) * WB::S + (size_t)(n0 + 16 * nt + r16) * DK + 16 * mt + 4 * q4;
+          store4<OP>(dst, S[i][0], S[i][1], S[i][2], S[i][3]);
         }
       }
     }
@@ -543,38 +529,44 @@ __global__ __launch_bounds__(512) void kda_state(const Args a) {
 
     f32x4 o1[NTS];
     if (w < 4) {
-      // X = W S (token tile w); U = U~ - X -> LDS as a split operand ([column][token])
+      // X = W S (token tile w); U = U~ - X -> LDS ([column][token])
 #pragma unroll
       for (int nt = 0; nt < NTS; ++nt) {
-        const f32x4 x = tile_mm_ps<E, DK>(sW, L::LDK, 16 * w, sSTh, sSTl, L::LDK, 16 * nt);
-        const float* ut = sUt + (16 * nt + r16) * CH + 16 * w + 4 * q4;
-        const int off = (16 * nt + r16) * L::LDT + 16 * w + 4 * q4;
-        store4_split<E>(sULh + off, sULl + off, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]);
+        const f32x4 x = tile_mm<DK>([&](int rr, int k) { return frag_row<OP>(sW, L::LDK, 16 * w + rr, k); },
+                                    [&](int rr, int k) { return frag_row<OP>(sST, L::LDK, 16 * nt + rr, k); },
+                                    zero4());
+        float ut[4];
+        load4<UTT>(sUt + (16 * nt + r16) * CH + 16 * w + 4 * q4, ut);
+        store4<OP>(sUL + (16 * nt + r16) * L::LDT + 16 * w + 4 * q4, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2],
+                   ut[3] - x[3]);
+        if constexpr (!OUT) {
+          // and U^T in fp32
+          float* dst = gU + blk_of(n) * WB::U + (size_t)(n0 + 16 * nt + r16) * CH + 16 * w + 4 * q4;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]};
+        }
       }
     } else if constexpr (OUT) {
 #pragma unroll
-      for (int nt = 0; nt < NTS; ++nt) o1[nt] = tile_mm_ps<E, DK>(sQt, L::LDK, 16 * (w - 4), sSTh, sSTl, L::LDK, 16 * nt);
+      for (int nt = 0; nt < NTS; ++nt)
+        o1[nt] = tile_mm<DK>([&](int rr, int k) { return frag_row<OP>(sQt, L::LDK, 16 * (w - 4) + rr, k); },
+                             [&](int rr, int k) { return frag_row<OP>(sST, L::LDK, 16 * nt + rr, k); }, zero4());
     }
     __syncthreads();
 
     if constexpr (OUT) {
       if (w >= 4) {
         const int tt = w - 4;
-        const ChunkInfo ci = gChunks[c0 + n];
-        O* oh = gOut + (size_t)ci.t0 * ro + (size_t)h * DV + n0;
+        const int t0 = tbeg + n * CH, clen = min(CH, tend - t0);
+        O* oh = gOut + (size_t)t0 * ro + (size_t)h * DV + n0;
 #pragma unroll
         for (int nt = 0; nt < NTS; ++nt) {
-          f32x4 x = o1[nt];
-#pragma unroll
-          for (int k = 0; k < CH; k += 32) {
-            const SFrag<E> fa = sfrag_row<E>(sAqk, L::LDF, 16 * tt + r16, k + 8 * q4);
-            const SFrag<E> fb = sfrag_pair<E>(sULh, sULl, L::LDT, 16 * nt + r16, k + 8 * q4);
-            x = mma_ss(fa, fb, x);
-          }
+          const f32x4 x =
+              tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sAqk, L::LDT, 16 * tt + rr, k); },
+                          [&](int rr, int k) { return frag_row<OP>(sUL, L::LDT, 16 * nt + rr, k); }, o1[nt]);
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int tok = 16 * tt + 4 * q4 + ii;
-            if (tok < ci.len) oh[(size_t)tok * ro + 16 * nt + r16] = cvt<O>(scale * x[ii]);
+            if (tok < clen) oh[(size_t)tok * ro + 16 * nt + r16] = cvt<O>(scale * x[ii]);
           }
         }
       }
@@ -584,22 +576,26 @@ __global__ __launch_bounds__(512) void kda_state(const Args a) {
     for (int i = 0; i < SPW; ++i) {
       const int t = w + 8 * i, mt = t % MTS, nt = t / MTS;
       if (t < NST) {
-        f32x4 x = zero4();
-#pragma unroll
-        for (int k = 0; k < CH; k += 32) {
-          const SFrag<E> fa = sfrag_row<E>(sKhT, L::LDF, 16 * mt + r16, k + 8 * q4);
-          const SFrag<E> fb = sfrag_pair<E>(sULh, sULl, L::LDT, 16 * nt + r16, k + 8 * q4);
-          x = mma_ss(fa, fb, x);
-        }
+        const f32x4 x = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sKhT, L::LDT, 16 * mt + rr, k); },
+                                    [&](int rr, int k) { return frag_row<OP>(sUL, L::LDT, 16 * nt + rr, k); },
+                                    zero4());
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) S[i][ii] = sGam[16 * mt + 4 * q4 + ii] * S[i][ii] + x[ii];
       }
     }
     __syncthreads();
-    if (n + 1 < nch) KDA_PRE_STORE();
+    if (n + 1 < nch) stage_store(nx);
+  };
+
+  if (nch > 0) {
+    stage_load(st0, 0);
+    stage_store(st0);
+    stage_load(st1, min(1, nch - 1));
   }
-#undef KDA_PRE_LOAD
-#undef KDA_PRE_STORE
+  for (int n = 0; n < nch; n += 2) {
+    chunk(n, st0, st1);
+    if (n + 1 < nch) chunk(n + 1, st1, st0);
+  }
 
   if (gFinal) {
 #pragma unroll
@@ -623,14 +619,16 @@ static hipError_t launch_state(const Args& a, hipStream_t st) {
   const int groups = (units + 7) / 8;
   const int grid = groups * 8 * NSL;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT>), dim3(grid), dim3(512), 0, st, a);
+  KDA_TIMED(OUT ? "kda_state_fwd" : "kda_state_bwd_fwdpass", st,
+            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT>), dim3(grid), dim3(512), 0, st, a));
   return hipGetLastError();
 }
 
 template <typename E, int DK, int DV, bool BWD>
 static hipError_t launch_prep(const Args& a, hipStream_t st) {
   if (a.max_chunks == 0 || a.H == 0) return hipSuccess;
-  hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a);
+  KDA_TIMED(BWD ? "kda_prep_bwd" : "kda_prep", st,
+            hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
   return hipGetLastError();
 }
 

@@ -30,21 +30,40 @@ struct Args {
   int32_t* seq_chunk0;      // [N + 1]
   void *wsW, *wsKhT, *wsQt, *wsUt, *wsAqk, *wsT;  // per (chunk, head) blocks, see WsBlock
   float* wsGam;
-  void* wsS;                // backward: state at each chunk start, E [DV][DK] per chunk-head
-  void* wsdS;               // backward: gradient of the state at each chunk end, E [DV][DK]
-  void* wsdU;               // backward: dU, E [CH][DV]
-  float* wsdQS;             // backward: scale * dO S^T, float [CH][DK]
-  float* wsdKh;             // backward: U dS'^T, float [CH][DK]
-  void* wsdW;               // backward: -dU S^T, E [CH][DK]
-  void* wsdAqk;             // backward: scale * tril(dO U^T), E [CH][CH]
-  float* wsdGam;            // backward: rowsum(dS' * S), float [DK]
+  // backward only (per chunk-head blocks; see WsBlock for shapes and types)
+  float* wsUtF;             // U~^T in fp32 [DV][CH] (the backward's state pass reads it)
+  float* wsG;               // un-beta strict Gram K+ K-^T
+  float* wsKhF;             // Kh token-major, fp32
+  void* wsS;                // state entering each chunk, OP [DV][DK]
+  float* wsU;               // U^T, fp32 [DV][CH]
+  float* wsdS;              // gradient of the state leaving each chunk, fp32 [DV][DK]
+  float* wsdU;              // dU^T, fp32 [DV][CH]
+  float* wsdAqk;            // scale * tril(dO U^T), fp32 [CH][CH]
+  float* wsdQS;             // scale * dO S^T, fp32 [CH][DK]
+  float* wsdKh;             // U dS'^T, fp32 [CH][DK]
+  float* wsdW;              // -dU S^T, fp32 [CH][DK]
+  float* wsdTU;             // dU V^T diag(beta), fp32 [CH][CH]
+  float* wsdGam;            // rowsum over values of dS' * S, fp32 [DK]
+  float* wsdBv;             // rowsum(V * T^T dU), fp32 [CH]
   int dvs;                  // value-column slice width of the sequential passes
   int out_bf16;             // outputs and gradients stored as bf16 (else fp32)
 };
 
+// Opt-in per-kernel timing (kda_timing_enable): a no-op unless enabled.
+void timing_begin(const char* name, hipStream_t st);
+void timing_end(hipStream_t st);
+
+// Bracket one launch statement with the timing hooks.
+#define KDA_TIMED(name, st, launch) \
+  do {                              \
+    ::kda::timing_begin(name, st);  \
+    launch;                         \
+    ::kda::timing_end(st);          \
+  } while (0)
+
 hipError_t launch_chunk_map(const Args& a, hipStream_t st);
 template <typename E, typename O, int DK, int DV> hipError_t launch_fwd(const Args& a, hipStream_t st);
 template <typename E, int DK, int DV> hipError_t launch_bwd_front(const Args& a, hipStream_t st);
-template <typename E, int DK, int DV> hipError_t launch_bwd(const Args& a, hipStream_t st);
+template <typename E, typename O, int DK, int DV> hipError_t launch_bwd(const Args& a, hipStream_t st);
 
 }  // namespace kda

@@ -105,6 +105,19 @@ kda_status kda_bwd(const kda_desc *desc, const void *q, const void *k, const voi
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);
 
+/* Measurement support (for benchmarks and profilers; not needed to compute).
+ * kda_timing_enable(1) makes every later kernel launch of kda_fwd/kda_bwd
+ * record a hipEvent pair around itself on the call's stream (clearing any
+ * accumulated times); kda_timing_enable(0) stops recording.  kda_timing_read
+ * waits for the recorded events, adds their durations into per-kernel totals
+ * and copies up to max_entries (name, total milliseconds, launch count)
+ * triples into the caller's arrays, returning the number of kernels with
+ * totals.  Names are static strings.  Events are created on first use and
+ * kept for reuse; both calls are host-thread safe.  Returns -1 if a HIP
+ * event call fails. */
+void kda_timing_enable(int enable);
+int kda_timing_read(int max_entries, const char **names, double *total_ms, int *launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,12 +28,18 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kda_bwd", "kda_fwd", "kda_status_string", "kda_workspace_bytes"])
+    assert declared_functions() == sorted(["kda_bwd", "kda_fwd", "kda_status_string", "kda_timing_enable",
+                                          "kda_timing_read", "kda_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_library_resolves_all_symbols_at_load():
+    """Loading with RTLD_NOW fails on any unresolved symbol (e.g. a missing template instance)."""
+    ctypes.CDLL(kda.lib_path(), mode=os.RTLD_NOW | os.RTLD_LOCAL)
 
 
 def test_status_strings(lib):
@@ -121,3 +127,11 @@ def test_empty_problem_needs_no_token_pointers(lib):
     assert need > 0
     # validation passes (no null-pointer error); stop short of launching by giving a small workspace
     assert _fwd(lib, d, q=None, k=None, v=None, la=None, beta=None, out=None, wsb=need - 1) == S_WS
+
+
+def test_timing_is_empty_without_launches(lib):
+    lib.kda_timing_enable.argtypes = [ctypes.c_int]
+    lib.kda_timing_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_timing_enable(1)
+    assert lib.kda_timing_read(8, None, None, None) == 0
+    lib.kda_timing_enable(0)
