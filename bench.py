@@ -28,13 +28,93 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
+METRIC = "KDA fwd(+bwd) tokens/s and % MFMA/HBM roofline, H=16 d=128 bf16, T=4K\u2013128K"
+
+CSRC = os.path.join(ROOT, "gated_delta_rule_79_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def algorithmic_bytes(w, tokens, n_seqs, fwd_only):
+def sources_digest():
+    """sha256 over the HIP sources: counters taken from other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(path):
+    import csv
+    out = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _short_name(name):
+    """rocprofv3 kernel name -> the timing name the library uses."""
+    for key, short in (("kda_prep", None), ("kda_state_rev", "kda_state_bwd_revpass"), ("kda_bwd_dv", "kda_bwd_dv"),
+                       ("kda_bwd_dk", "kda_bwd_dk"), ("kda_chunk_map", "kda_chunk_map"), ("kda_state", None)):
+        if key in name:
+            if short:
+                return short
+            if key == "kda_prep":
+                return "kda_prep_bwd" if ("Lb1E" in name or ", true>" in name) else "kda_prep"
+            return "kda_state_fwd" if ("Lb1E" in name or ", true>" in name) else "kda_state_bwd_fwdpass"
+    return None
+
+
+def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, workload):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (one bench step, and a plain copy of
+    copy_bytes bytes) into per-kernel HBM bytes per launch, scaled by the copy's calibration."""
+    cf = _counter_rows(copy_fetch_csv)
+    cw = _counter_rows(copy_write_csv)
+    copy_name = next(n for n in cf if "copyBuffer" in n)
+    f_kib = sum(cf[copy_name]) / len(cf[copy_name])
+    w_kib = sum(cw[copy_name]) / len(cw[copy_name])
+    scale_f = copy_bytes / (f_kib * 1024.0)   # bytes per counted KiB-unit, reads
+    scale_w = copy_bytes / (w_kib * 1024.0)
+    kf, kw = _counter_rows(fetch_csv), _counter_rows(write_csv)
+    kernels = {}
+    for name in kf:
+        short = _short_name(name)
+        if not short or name not in kw:
+            continue
+        fk = sum(kf[name]) / len(kf[name])
+        wk = sum(kw[name]) / len(kw[name])
+        kernels[short] = {"fetch_kib": fk, "write_kib": wk,
+                          "read_bytes": fk * 1024.0 * scale_f, "write_bytes": wk * 1024.0 * scale_w,
+                          "bytes": fk * 1024.0 * scale_f + wk * 1024.0 * scale_w}
+    doc = {"workload": workload, "sources_sha256": sources_digest(),
+           "calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": f_kib, "copy_write_kib": w_kib,
+                           "fetch_scale": scale_f, "write_scale": scale_w},
+           "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return doc
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counters, or None when absent or stale."""
+    try:
+        doc = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if doc.get("workload") != workload or doc.get("sources_sha256") != sources_digest():
+        return None
+    k = doc.get("kernels", {}).get(kernel)
+    return int(k["bytes"]) if k else None
+
+
+def algorithmic_bytes(w, tokens, n_seqs, fwd_only, eout=4):
     """Compulsory HBM bytes of the path (inputs read once, outputs written once)."""
     H, dk, dv = w.H, w.dk, w.dv
     ein = 2 if w.dtype == "bf16" else 4
-    eout = 4
     th = tokens * H
     state = n_seqs * H * dk * dv * 4
     fwd = th * (ein * (2 * dk + dk + dv) + ein) + th * eout * dv + 2 * state      # q,k,la,v,beta -> o; S0 in, S_T out
@@ -58,22 +138,39 @@ def algorithmic_flops(w, tokens, fwd_only):
     return per * tokens * w.H
 
 
-def kernel_alg_bytes(name, w, tokens, n_seqs):
-    """Compulsory bytes one launch of a kernel must move (its share of the path's inputs/outputs)."""
+def kernel_alg_bytes(name, w, tokens, n_seqs, eout=4):
+    """Compulsory bytes one launch of a kernel must move: its share of the path's
+    own inputs and outputs (intermediates in the workspace are not counted)."""
     H, dk, dv = w.H, w.dk, w.dv
     ein = 2 if w.dtype == "bf16" else 4
     th = tokens * H
     state = n_seqs * H * dk * dv * 4
     table = {
-        "kda_prep": th * (ein * (2 * dk + dk + dv) + ein),                # reads q, k, log_alpha, v, beta
-        "kda_prep_bwd": th * (ein * (2 * dk + dk + dv) + ein),
-        "kda_state_fwd": th * 4 * dv + 2 * state,                         # writes o; reads S0, writes S_T
+        "kda_prep": th * (ein * (3 * dk + dv) + ein),                     # reads q, k, log_alpha, v, beta
+        "kda_prep_bwd": th * (ein * (3 * dk + dv) + ein),                 # same reads, backward recompute
+        "kda_state_fwd": th * eout * dv + 2 * state,                      # writes o; reads S0, writes S_T
         "kda_state_bwd_fwdpass": state,                                   # reads S0
         "kda_state_bwd_revpass": th * ein * dv + 2 * state,               # reads dO, dS_T; writes dS0
-        "kda_bwd_chunk": th * (ein * (2 * dk + dk + dv) + ein + ein * dv) + th * 4 * (2 * dk + dk + dv + 1),
+        "kda_bwd_dv": th * (2 * ein * dv + ein + eout * dv),              # reads v, dO, beta; writes dv
+        "kda_bwd_dk": th * (3 * ein * dk + ein + eout * (3 * dk + 1)),    # reads q, k, log_alpha, beta; writes dq, dk, dla, dbeta
         "kda_chunk_map": 0,
     }
     return table.get(name, 0)
+
+
+def kernel_alg_flops(name, w, tokens):
+    """Algorithmic flops of one launch (chunk C=64, triangular products counted once)."""
+    dk, dv, C = w.dk, w.dv, 64
+    per = {
+        "kda_prep": 2 * C * dk + C * dk + C * dv,                          # Gram Akk, Aqk; W, U~
+        "kda_prep_bwd": 2 * C * dk + C * dk + C * dv,
+        "kda_state_fwd": 3 * 2 * dk * dv + C * dv,                         # W S, Qt S, Kh^T U; Aqk U
+        "kda_state_bwd_fwdpass": 2 * 2 * dk * dv,                          # W S, Kh^T U
+        "kda_state_bwd_revpass": 3 * 2 * dk * dv + C * dv,                 # Kh dS', Qt^T dO, W^T dU; Aqk^T dO
+        "kda_bwd_dv": 3 * 2 * dk * dv + C * dv + 2 * C * dv + C * dv,      # dO S^T, U dS'^T, dU S^T; dO U^T, dU V^T, T^T dU
+        "kda_bwd_dk": C * dk + 2 * C * dk + 2 * C * C + 4 * C * dk,        # T^T dW, dW K+^T, T-products, gated products
+    }.get(name, 0)
+    return per * tokens * w.H
 
 
 def cpu_baseline(inp, w, with_bwd):
@@ -111,7 +208,19 @@ def main() -> int:
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="bf16 outputs/gradients instead of fp32")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc counter_collection CSVs "
+                         "(one bench step; a --copy-probe 1024 run); needs no GPU")
     args = ap.parse_args()
+    if args.ingest_counters:
+        import kda_inputs as ki
+        doc = ingest_counters(*args.ingest_counters, copy_bytes=1024 << 20, workload=ki.config(args.config).name)
+        print(json.dumps(doc["calibration"]))
+        for k, v in sorted(doc["kernels"].items()):
+            print(f"{k:24s} read {v['read_bytes'] / 1e9:8.3f} GB  write {v['write_bytes'] / 1e9:8.3f} GB")
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}); the multi-GPU path is not "
@@ -127,9 +236,18 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    kda.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return 0
+    kda.load_library()
 
     w = ki.config(args.config)
     fwd_only = args.fwd_only or not w.backward
@@ -199,12 +317,19 @@ def main() -> int:
     if dom:
         name, (tot_ms, n_launch) = dom
         avg_ms = tot_ms / max(n_launch, 1)
-        ab = kernel_alg_bytes(name, w, tokens, n_seqs)
-        ach = ab / (avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": name,
-                "avg_launch_ms": round(avg_ms, 4), "alg_bytes_per_launch": int(ab)}
-    total_bytes, parts = algorithmic_bytes(w, tokens, n_seqs, fwd_only)
+        ab = kernel_alg_bytes(name, w, tokens, n_seqs, 2 if args.out_bf16 else 4)
+        af = kernel_alg_flops(name, w, tokens)
+        if ab / (HBM_PEAK_GBS * 1e9) >= af / (BF16_PEAK_TFLOPS * 1e12):
+            ach = ab / (avg_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4)}
+        else:
+            ach = af / (avg_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+        roof.update({"traffic": measured_traffic(name, w.name), "kernel": name, "avg_launch_ms": round(avg_ms, 4),
+                     "launches": n_launch, "alg_bytes_per_launch": int(ab), "alg_flops_per_launch": int(af)})
+    total_bytes, parts = algorithmic_bytes(w, tokens, n_seqs, fwd_only, 2 if args.out_bf16 else 4)
     flops = algorithmic_flops(w, tokens, fwd_only)
     t_hbm = total_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
@@ -217,8 +342,7 @@ def main() -> int:
         cpu = cpu_baseline(inp, w, not fwd_only)
 
     line = {
-        "metric": "KDA fwd+bwd tokens/s (H=16, d=128, bf16 inputs, varlen 8 x U[1K,32K])" if not fwd_only
-        else f"KDA fwd tokens/s ({w.name})",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
