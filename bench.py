@@ -56,8 +56,8 @@ def _counter_rows(path):
 
 def _short_name(name):
     """rocprofv3 kernel name -> the timing name the library uses."""
-    for key, short in (("kda_prep", None), ("kda_state_rev", "kda_state_bwd_revpass"), ("kda_bwd_dv", "kda_bwd_dv"),
-                       ("kda_bwd_dk", "kda_bwd_dk"), ("kda_chunk_map", "kda_chunk_map"), ("kda_state", None)):
+    for key, short in (("kda_prep", None), ("kda_state_rev", "kda_state_bwd_revpass"), ("kda_bwd_chunk", "kda_bwd_chunk"),
+                       ("kda_chunk_map", "kda_chunk_map"), ("kda_state", None)):
         if key in name:
             if short:
                 return short
@@ -151,8 +151,8 @@ def kernel_alg_bytes(name, w, tokens, n_seqs, eout=4):
         "kda_state_fwd": th * eout * dv + 2 * state,                      # writes o; reads S0, writes S_T
         "kda_state_bwd_fwdpass": state,                                   # reads S0
         "kda_state_bwd_revpass": th * ein * dv + 2 * state,               # reads dO, dS_T; writes dS0
-        "kda_bwd_dv": th * (2 * ein * dv + ein + eout * dv),              # reads v, dO, beta; writes dv
-        "kda_bwd_dk": th * (3 * ein * dk + ein + eout * (3 * dk + 1)),    # reads q, k, log_alpha, beta; writes dq, dk, dla, dbeta
+        # reads q, k, log_alpha, v, dO, beta; writes dq, dk, dlog_alpha, dv, dbeta
+        "kda_bwd_chunk": th * (ein * (3 * dk + 2 * dv) + ein + eout * (3 * dk + dv + 1)),
         "kda_chunk_map": 0,
     }
     return table.get(name, 0)
@@ -167,8 +167,8 @@ def kernel_alg_flops(name, w, tokens):
         "kda_state_fwd": 3 * 2 * dk * dv + C * dv,                         # W S, Qt S, Kh^T U; Aqk U
         "kda_state_bwd_fwdpass": 2 * 2 * dk * dv,                          # W S, Kh^T U
         "kda_state_bwd_revpass": 3 * 2 * dk * dv + C * dv,                 # Kh dS', Qt^T dO, W^T dU; Aqk^T dO
-        "kda_bwd_dv": 3 * 2 * dk * dv + C * dv + 2 * C * dv + C * dv,      # dO S^T, U dS'^T, dU S^T; dO U^T, dU V^T, T^T dU
-        "kda_bwd_dk": C * dk + 2 * C * dk + 2 * C * C + 4 * C * dk,        # T^T dW, dW K+^T, T-products, gated products
+        # dO S^T, U dS'^T, dU S^T; dO U^T, dU V^T, T^T dU; T^T dW, dW K+^T, T-products, gated products
+        "kda_bwd_chunk": 3 * 2 * dk * dv + 4 * C * dv + 3 * C * dk + 2 * C * C + 4 * C * dk,
     }.get(name, 0)
     return per * tokens * w.H
 

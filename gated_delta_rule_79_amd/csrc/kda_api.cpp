@@ -31,8 +31,7 @@ struct Plan {
   int max_chunks = 0;
   size_t esz = 0;
   size_t chunks = 0, sc0 = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
-  size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0, dAqk = 0, dQS = 0, dKh = 0, dW = 0, dTU = 0,
-         dGam = 0, dBv = 0;
+  size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0;
   size_t total = 0;
 };
 
@@ -84,13 +83,6 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
     p.U = take(nb * dv * CH * 4);
     p.dS = take(nb * dk * dv * 4);
     p.dU = take(nb * dv * CH * 4);
-    p.dAqk = take(nb * CH * CH * 4);
-    p.dQS = take(nb * CH * dk * 4);
-    p.dKh = take(nb * CH * dk * 4);
-    p.dW = take(nb * CH * dk * 4);
-    p.dTU = take(nb * CH * CH * 4);
-    p.dGam = take(nb * dk * 4);
-    p.dBv = take(nb * CH * 4);
   }
   p.total = o;
   return p;
@@ -133,13 +125,6 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
   a.wsU = fptr(p.U);
   a.wsdS = fptr(p.dS);
   a.wsdU = fptr(p.dU);
-  a.wsdAqk = fptr(p.dAqk);
-  a.wsdQS = fptr(p.dQS);
-  a.wsdKh = fptr(p.dKh);
-  a.wsdW = fptr(p.dW);
-  a.wsdTU = fptr(p.dTU);
-  a.wsdGam = fptr(p.dGam);
-  a.wsdBv = fptr(p.dBv);
 }
 
 hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {

@@ -17,9 +17,9 @@
 //   chunk map, prep (also T, G, fp32 Kh), state pass (S entering each chunk, U),
 //   kda_state_rev   : reverse sequential pass over the chunks of one (sequence,
 //                     head, value slice): dS', dU and d_init_state.
-//   kda_bwd_dv      : chunk-parallel contractions over the value dimension.
-//   kda_bwd_dk      : chunk-parallel contractions over tokens, gated products,
-//                     and the assembly of dq, dk, dlog_alpha, dbeta.
+//   kda_bwd_chunk   : chunk-parallel; contractions over the value dimension,
+//                     then over tokens, the gated products, and the assembly
+//                     of dq, dk, dv, dlog_alpha, dbeta.
 // The gated products never form K- = K/Gamma: they use the same per-block
 // reference rows as the forward's decayed Gram blocks.
 #include "kda_internal.hpp"
@@ -253,166 +253,217 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// chunk-parallel contractions over the value dimension
+// chunk-parallel gradients: one workgroup per chunk-head, 8 waves
 // ---------------------------------------------------------------------------
-// Wave w owns token rows 16w..16w+15 of every output; the value dimension is
-// walked in quarters of 32 columns so the working set fits in LDS.
+// Wave w owns token tile tw = w & 3 (rows 16tw..16tw+15) and half hf = w >> 2
+// of the column tiles of every product it computes.
+//
+// Phase A walks the value dimension in quarters of 32 columns and accumulates
+// the contractions over it (dAqk = scale tril(dO U^T), dT_U = dU V^T,
+// dQS = dO S^T, dKh = U dS'^T, dW = -dU S^T), writes dV = beta T^T dU, and
+// the value sums of V * T^T dU (for dbeta) and dS' * S (dGamma_C).  The
+// quarter after the current one is loaded into registers while the current
+// one is multiplied.
+//
+// Phase B works over tokens and channels: T^T dW, dT, dA = -strict(T^T dT T^T),
+// the gated products with per-block reference rows, and the assembly of dq,
+// dk, dg, dbeta; dlog_alpha is the reverse cumulative sum of dg over the chunk.
+// dQS, dKh and dT_U stay in the accumulator registers of phase A, in the same
+// tile layout phase B consumes them in.
 template <typename E, int DK, int DV>
-struct DvLds {
+struct BwdLds {
   using OP = typename OpOf<E>::T;
-  static constexpr int P = PADE<OP>;
-  static constexpr int QC = 32;             // value columns per pass
-  static constexpr int LDK = DK + P;
-  static constexpr int LDT = CH + P;
-  static constexpr int LDQ = QC + P;
-  static constexpr size_t T = 0;                                           // OP [CH][LDT]
-  static constexpr size_t S = T + (size_t)CH * LDT * sizeof(OP);           // OP [QC][LDK]   S^T quarter
-  static constexpr size_t DSH = S + (size_t)QC * LDK * sizeof(OP);         // OP [QC][LDK]   dS'^T split
-  static constexpr size_t DSL = DSH + (size_t)QC * LDK * sizeof(OP);
-  static constexpr size_t UH = DSL + (size_t)QC * LDK * sizeof(OP);        // OP [QC][LDT]   U^T split
-  static constexpr size_t UL = UH + (size_t)QC * LDT * sizeof(OP);
-  static constexpr size_t DUH = UL + (size_t)QC * LDT * sizeof(OP);        // OP [QC][LDT]   dU^T split
-  static constexpr size_t DUL = DUH + (size_t)QC * LDT * sizeof(OP);
-  static constexpr size_t DO = DUL + (size_t)QC * LDT * sizeof(OP);        // OP [CH][LDQ]   dO quarter
-  static constexpr size_t V = DO + (size_t)CH * LDQ * sizeof(OP);          // OP [CH][LDQ]   V quarter
-  static constexpr size_t BETA = V + (size_t)CH * LDQ * sizeof(OP);        // float [CH]
-  static constexpr size_t GAMP = BETA + CH * 4;                            // float [256] partial rowsums
-  static constexpr size_t BYTES = GAMP + 256 * 4;
-  static_assert(BYTES <= 163840, "dv kernel LDS");
+  static constexpr int PE = PADE<E>, PO = PADE<OP>;
+  static constexpr int QC = 32;                      // value columns per quarter
+  static constexpr bool SPLIT = sizeof(OP) == 2;     // lo halves exist only for 2-byte operands
+  static constexpr size_t OPB = sizeof(OP);
+  // phase A (leading dimensions in elements)
+  static constexpr int LSK = DK + PO;   // OP [QC][DK]  S^T, dS'^T quarters
+  static constexpr int LST = CH + PO;   // OP [QC][CH]  U^T, dU^T quarters
+  static constexpr int LSQ = QC + PO;   // OP [CH][QC]  dO, V quarters
+  static constexpr size_t A_S = 0;
+  static constexpr size_t A_DSH = A_S + (size_t)QC * LSK * OPB;
+  static constexpr size_t A_DSL = A_DSH + (size_t)QC * LSK * OPB;
+  static constexpr size_t A_UH = A_DSL + (SPLIT ? (size_t)QC * LSK * OPB : 0);
+  static constexpr size_t A_UL = A_UH + (size_t)QC * LST * OPB;
+  static constexpr size_t A_DUH = A_UL + (SPLIT ? (size_t)QC * LST * OPB : 0);
+  static constexpr size_t A_DUL = A_DUH + (size_t)QC * LST * OPB;
+  static constexpr size_t A_DO = A_DUL + (SPLIT ? (size_t)QC * LST * OPB : 0);
+  static constexpr size_t A_V = A_DO + (size_t)CH * LSQ * OPB;
+  static constexpr size_t A_END = A_V + (size_t)CH * LSQ * OPB;
+  // phase B (shares the first region with phase A)
+  static constexpr int LDG = DK + 4;    // float [CH][LDG]  g, later dg
+  static constexpr int LDK = DK + PE;   // E     [CH][LDK]  k, q
+  static constexpr int LDO = DK + PO;   // OP    [CH][LDO]  dW, K+
+  static constexpr int LDT = CH + PO;   // OP    [CH][LDT]  T, Y
+  static constexpr int LDA = CH + 4;    // float [CH][LDA]  dAqk, dT / dG
+  static constexpr size_t G = 0;
+  static constexpr size_t K = G + (size_t)CH * LDG * 4;
+  static constexpr size_t Q = K + (size_t)CH * LDK * sizeof(E);
+  static constexpr size_t B_END = Q + (size_t)CH * LDK * sizeof(E);
+  static constexpr size_t UNION = A_END > B_END ? A_END : B_END;
+  // both phases
+  static constexpr size_t T = UNION;                                  // OP    [CH][LDT]
+  static constexpr size_t A1 = T + (size_t)CH * LDT * OPB;            // float [CH][LDA]  scale tril(dO U^T)
+  static constexpr size_t A2 = A1 + (size_t)CH * LDA * 4;             // float [CH][LDA]  dT, then dG
+  static constexpr size_t DW = A2 + (size_t)CH * LDA * 4;             // OP    [CH][LDO]  dW (Y after it is dead)
+  static constexpr size_t KP = DW + (size_t)CH * LDO * OPB;           // OP    [CH][LDO]  K+
+  static constexpr size_t BETA = KP + (size_t)CH * LDO * OPB;         // float [CH]
+  static constexpr size_t RED = BETA + CH * 4;                        // float [512]  scan / column-sum partials
+  static constexpr size_t GAMP = RED + 512 * 4;                       // float [512]  dGamma_C partials
+  static constexpr size_t DGAM = GAMP + 512 * 4;                      // float [DK]
+  static constexpr size_t BV = DGAM + DK * 4;                         // float [2][CH] rowsum(V * T^T dU) halves
+  static constexpr size_t DBP = BV + 2 * CH * 4;                      // float [2][CH] dbeta halves
+  static constexpr size_t BYTES = DBP + 2 * CH * 4;
+  static constexpr size_t Y = DW;                                     // OP [CH][LDT]
+  static_assert(BYTES <= 163840, "backward chunk kernel LDS");
+  static_assert(A_END % 16 == 0 && B_END % 16 == 0, "LDS regions stay 16-byte aligned");
 };
 
 template <typename E, typename O, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_bwd_dv(const Args a) {
-  using L = DvLds<E, DK, DV>;
+__global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
+  using L = BwdLds<E, DK, DV>;
   using OP = typename L::OP;
   using WB = WsBlock<E, DK, DV>;
-  constexpr int NT = 256, QC = L::QC, NQ = DV / QC;
-  constexpr int NKT = DK / 16;   // channel tiles
+  using SE = typename std::conditional<sizeof(E) == 4, float, bf16>::type;   // gated products: split bf16
+  constexpr int NT = 512, NKT = DK / 16, NKH = NKT / 2, QC = L::QC, NQ = DV / QC;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int j = blockIdx.x, h = blockIdx.y, H = a.H;
   const ChunkInfo ci = a.chunks[j];
   if (ci.len <= 0) return;
   const int len = ci.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
+  const int tw = w & 3, hf = w >> 2, kq = 8 * q4;
   const size_t blk = (size_t)j * H + h;
-  const size_t rv = (size_t)H * DV;
+  const size_t rk = (size_t)H * DK, rv = (size_t)H * DV;
+  const float scale = a.scale;
 
+  OP* sS = reinterpret_cast<OP*>(smem + L::A_S);
+  OP* sDSh = reinterpret_cast<OP*>(smem + L::A_DSH);
+  OP* sDSl = reinterpret_cast<OP*>(smem + L::A_DSL);
+  OP* sUh = reinterpret_cast<OP*>(smem + L::A_UH);
+  OP* sUl = reinterpret_cast<OP*>(smem + L::A_UL);
+  OP* sDUh = reinterpret_cast<OP*>(smem + L::A_DUH);
+  OP* sDUl = reinterpret_cast<OP*>(smem + L::A_DUL);
+  OP* sDO = reinterpret_cast<OP*>(smem + L::A_DO);
+  OP* sV = reinterpret_cast<OP*>(smem + L::A_V);
+  float* sG = reinterpret_cast<float*>(smem + L::G);
+  E* sK = reinterpret_cast<E*>(smem + L::K);
+  E* sQ = reinterpret_cast<E*>(smem + L::Q);
   OP* sT = reinterpret_cast<OP*>(smem + L::T);
-  OP* sS = reinterpret_cast<OP*>(smem + L::S);
-  OP* sDSh = reinterpret_cast<OP*>(smem + L::DSH);
-  OP* sDSl = reinterpret_cast<OP*>(smem + L::DSL);
-  OP* sUh = reinterpret_cast<OP*>(smem + L::UH);
-  OP* sUl = reinterpret_cast<OP*>(smem + L::UL);
-  OP* sDUh = reinterpret_cast<OP*>(smem + L::DUH);
-  OP* sDUl = reinterpret_cast<OP*>(smem + L::DUL);
-  OP* sDO = reinterpret_cast<OP*>(smem + L::DO);
-  OP* sV = reinterpret_cast<OP*>(smem + L::V);
+  float* sA1 = reinterpret_cast<float*>(smem + L::A1);
+  float* sA2 = reinterpret_cast<float*>(smem + L::A2);
+  OP* sDW = reinterpret_cast<OP*>(smem + L::DW);
+  OP* sY = reinterpret_cast<OP*>(smem + L::Y);
+  OP* sKp = reinterpret_cast<OP*>(smem + L::KP);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
+  float* sRed = reinterpret_cast<float*>(smem + L::RED);
   float* sGamP = reinterpret_cast<float*>(smem + L::GAMP);
+  float* sDGam = reinterpret_cast<float*>(smem + L::DGAM);
+  float* sBv = reinterpret_cast<float*>(smem + L::BV);
+  float* sDbp = reinterpret_cast<float*>(smem + L::DBP);
 
-  const E* gV = reinterpret_cast<const E*>(a.v) + (size_t)ci.t0 * rv + (size_t)h * DV;
-  const E* gDO = reinterpret_cast<const E*>(a.dout) + (size_t)ci.t0 * rv + (size_t)h * DV;
-  const E* gB = reinterpret_cast<const E*>(a.beta) + (size_t)ci.t0 * H + h;
+  const E* qh = reinterpret_cast<const E*>(a.q) + (size_t)ci.t0 * rk + (size_t)h * DK;
+  const E* kh = reinterpret_cast<const E*>(a.k) + (size_t)ci.t0 * rk + (size_t)h * DK;
+  const E* lh = reinterpret_cast<const E*>(a.la) + (size_t)ci.t0 * rk + (size_t)h * DK;
+  const E* vh = reinterpret_cast<const E*>(a.v) + (size_t)ci.t0 * rv + (size_t)h * DV;
+  const E* doh = reinterpret_cast<const E*>(a.dout) + (size_t)ci.t0 * rv + (size_t)h * DV;
+  const E* bh = reinterpret_cast<const E*>(a.beta) + (size_t)ci.t0 * H + h;
   const OP* gS = reinterpret_cast<const OP*>(a.wsS) + blk * WB::S;
   const float* gdS = a.wsdS + blk * WB::DS;
   const float* gU = a.wsU + blk * WB::U;
   const float* gdU = a.wsdU + blk * WB::DU;
   const float* gT = reinterpret_cast<const float*>(a.wsT) + blk * WB::TT;
+  const float* gGm = a.wsG + blk * WB::G;
   O* gdV = reinterpret_cast<O*>(a.dv_) + (size_t)ci.t0 * rv + (size_t)h * DV;
 
-  for (int o = tid; o < CH * CH; o += NT) sT[(o / CH) * L::LDT + o % CH] = cvt<OP>(gT[o]);
-  if (tid < CH) sBeta[tid] = tid < len ? f32(gB[(size_t)tid * H]) : 0.f;
+  // phase B's inputs (q, k, log_alpha rows) are loaded during the last quarter of phase A
+  TileCopy<E, CH, DK, NT> pk, pq, pl;
 
-  f32x4 accA[4], accQ[NKT], accK[NKT], accW[NKT], accT[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) accA[i] = accT[i] = zero4();
-#pragma unroll
-  for (int i = 0; i < NKT; ++i) accQ[i] = accK[i] = accW[i] = zero4();
-  float bv[4] = {0.f, 0.f, 0.f, 0.f};   // rowsum(V * T^T dU) partials for rows 16w + 4q4 + ii (lane r16 == 0)
-  float gp = 0.f;                       // rowsum(dS' * S) partial for channel tid % DK
+  // ---- T -> LDS (operand type), beta
+  {
+    TileCopy<float, CH, CH, NT> tt;
+    tt.load(gT, CH);
+    tt.template store_cvt<OP>(sT, L::LDT, CH);
+  }
+  if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
 
+  // ---- phase A: contractions over the value dimension
+  struct QStage {
+    TileCopy<OP, QC, DK, NT> s;
+    TileCopy<float, QC, DK, NT> ds;
+    TileCopy<float, QC, CH, NT> u, du;
+    TileCopy<E, CH, QC, NT> dov, vv;
+  };
+  QStage qs;
+  auto qload = [&](int qq) __attribute__((always_inline)) {
+    const int cq = qq * QC;
+    qs.s.load(gS + (size_t)cq * DK, DK);
+    qs.ds.load(gdS + (size_t)cq * DK, DK);
+    qs.u.load(gU + (size_t)cq * CH, CH);
+    qs.du.load(gdU + (size_t)cq * CH, CH);
+    qs.dov.load(doh + cq, rv, len);   // rows past the chunk are not read; they are zeroed on store
+    qs.vv.load(vh + cq, rv, len);
+  };
+  f32x4 accA[2], accT[2], accQ[NKH], accK[NKH], accW[NKH];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) accA[i] = accT[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NKH; ++i) accQ[i] = accK[i] = accW[i] = zero4();
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  float gp = 0.f;
+
+  qload(0);
   for (int qq = 0; qq < NQ; ++qq) {
     const int cq = qq * QC;
-    __syncthreads();  // previous quarter's LDS reads are done
-    // S^T and dS'^T quarter: rows cq..cq+QC of [DV][DK]
-    {
-      constexpr int VPR = DK / 8;
-      for (int v = tid; v < QC * VPR; v += NT) {
-        const int row = v / VPR, c0 = (v % VPR) * 8;
-        float s8[8];
-        load8<OP>(gS + (size_t)(cq + row) * DK + c0, true, s8);
-        store4<OP>(sS + row * L::LDK + c0, s8[0], s8[1], s8[2], s8[3]);
-        store4<OP>(sS + row * L::LDK + c0 + 4, s8[4], s8[5], s8[6], s8[7]);
-        const float* src = gdS + (size_t)(cq + row) * DK + c0;
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(src + 4);
-        store4_split<OP>(sDSh + row * L::LDK + c0, sDSl + row * L::LDK + c0, d0[0], d0[1], d0[2], d0[3]);
-        store4_split<OP>(sDSh + row * L::LDK + c0 + 4, sDSl + row * L::LDK + c0 + 4, d1[0], d1[1], d1[2], d1[3]);
-      }
-      // U^T, dU^T quarter: rows cq..cq+QC of [DV][CH]
-      constexpr int VPT = CH / 4;
-      for (int v = tid; v < QC * VPT; v += NT) {
-        const int row = v / VPT, c0 = (v % VPT) * 4;
-        const f32x4 u = *reinterpret_cast<const f32x4*>(gU + (size_t)(cq + row) * CH + c0);
-        const f32x4 du = *reinterpret_cast<const f32x4*>(gdU + (size_t)(cq + row) * CH + c0);
-        store4_split<OP>(sUh + row * L::LDT + c0, sUl + row * L::LDT + c0, u[0], u[1], u[2], u[3]);
-        store4_split<OP>(sDUh + row * L::LDT + c0, sDUl + row * L::LDT + c0, du[0], du[1], du[2], du[3]);
-      }
-      // dO and V quarters, token-major, rows past the chunk zeroed
-      constexpr int VPQ = QC / 8;
-      for (int v = tid; v < CH * VPQ; v += NT) {
-        const int row = v / VPQ, c0 = (v % VPQ) * 8;
-        float x[8], y[8];
-        load8<E>(gDO + (size_t)row * rv + cq + c0, row < len, x);
-        load8<E>(gV + (size_t)row * rv + cq + c0, row < len, y);
-        store4<OP>(sDO + row * L::LDQ + c0, x[0], x[1], x[2], x[3]);
-        store4<OP>(sDO + row * L::LDQ + c0 + 4, x[4], x[5], x[6], x[7]);
-        store4<OP>(sV + row * L::LDQ + c0, y[0], y[1], y[2], y[3]);
-        store4<OP>(sV + row * L::LDQ + c0 + 4, y[4], y[5], y[6], y[7]);
-      }
-    }
+    __syncthreads();  // the previous quarter's LDS reads are done
+    qs.s.store(sS, L::LSK);
+    qs.ds.template store_split<OP>(sDSh, sDSl, L::LSK);
+    qs.u.template store_split<OP>(sUh, sUl, L::LST);
+    qs.du.template store_split<OP>(sDUh, sDUl, L::LST);
+    qs.dov.template store_cvt<OP>(sDO, L::LSQ, len);
+    qs.vv.template store_cvt<OP>(sV, L::LSQ, len);
+    if (qq + 1 < NQ) qload(qq + 1);
     __syncthreads();
-    // rowsum over values of dS' * S (channel c, half of the quarter's columns)
+    // value sums of dS' * S for channel c (NT / DK parts of the quarter's columns)
     {
-      const int c = tid % DK, part = tid / DK;  // NT / DK parts
       constexpr int NPART = NT / DK, CPP = QC / NPART;
-      for (int col = part * CPP; col < (part + 1) * CPP; ++col) {
-        const int o = col * L::LDK + c;
-        // the low half exists only for 2-byte operands (store4_split leaves it unwritten for fp32)
-        const float ds = sizeof(OP) == 2 ? f32(sDSh[o]) + f32(sDSl[o]) : f32(sDSh[o]);
+      const int c = tid % DK, p = tid / DK;
+#pragma unroll
+      for (int col = p * CPP; col < (p + 1) * CPP; ++col) {
+        const int o = col * L::LSK + c;
+        const float ds = L::SPLIT ? f32(sDSh[o]) + f32(sDSl[o]) : f32(sDSh[o]);
         gp += ds * f32(sS[o]);
       }
     }
-    const int kq = 8 * q4;
-    const Frag<OP> fdo = frag_row<OP>(sDO, L::LDQ, 16 * w + r16, kq);        // dO rows of tile w
-    const SFrag<OP> fdu = sfrag_col_pair<OP>(sDUh, sDUl, L::LDT, 16 * w + r16, kq);   // dU rows of tile w
-    const SFrag<OP> fu = sfrag_col_pair<OP>(sUh, sUl, L::LDT, 16 * w + r16, kq);      // U rows of tile w
-    // dAqk += dO U^T ; dT_U += dU V^T
+    const Frag<OP> fdo = frag_row<OP>(sDO, L::LSQ, 16 * tw + r16, kq);
+    const SFrag<OP> fdu = sfrag_col_pair<OP>(sDUh, sDUl, L::LST, 16 * tw + r16, kq);
+    const SFrag<OP> fu = sfrag_col_pair<OP>(sUh, sUl, L::LST, 16 * tw + r16, kq);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      accA[nt] = mma_ps(fdo, sfrag_col_pair<OP>(sUh, sUl, L::LDT, 16 * nt + r16, kq), accA[nt]);
-      accT[nt] = mma_sp(fdu, frag_row<OP>(sV, L::LDQ, 16 * nt + r16, kq), accT[nt]);
+    for (int jj = 0; jj < 2; ++jj) {
+      const int nt = 2 * hf + jj;
+      accA[jj] = mma_ps(fdo, sfrag_col_pair<OP>(sUh, sUl, L::LST, 16 * nt + r16, kq), accA[jj]);
+      accT[jj] = mma_sp(fdu, frag_row<OP>(sV, L::LSQ, 16 * nt + r16, kq), accT[jj]);
     }
-    // dQS += dO S^T ; dKh += U dS'^T ; dW += dU S^T
 #pragma unroll
-    for (int nt = 0; nt < NKT; ++nt) {
-      const Frag<OP> fs = frag_col<OP>(sS, L::LDK, 16 * nt + r16, kq);
-      accQ[nt] = mma(fdo, fs, accQ[nt]);
-      accW[nt] = mma_sp(fdu, fs, accW[nt]);
-      accK[nt] = mma_ss(fu, sfrag_col_pair<OP>(sDSh, sDSl, L::LDK, 16 * nt + r16, kq), accK[nt]);
+    for (int jj = 0; jj < NKH; ++jj) {
+      const int nt = hf * NKH + jj;
+      const Frag<OP> fs = frag_col<OP>(sS, L::LSK, 16 * nt + r16, kq);
+      accQ[jj] = mma(fdo, fs, accQ[jj]);
+      accW[jj] = mma_sp(fdu, fs, accW[jj]);
+      accK[jj] = mma_ss(fu, sfrag_col_pair<OP>(sDSh, sDSl, L::LSK, 16 * nt + r16, kq), accK[jj]);
     }
-    // T^T dU for token tile w and the quarter's columns -> dV, and rowsum(V * T^T dU)
-#pragma unroll
-    for (int nt = 0; nt < QC / 16; ++nt) {
+    __builtin_amdgcn_sched_barrier(0);
+    // dV = beta T^T dU for token tile tw and the quarter's column tile hf
+    {
       f32x4 x = zero4();
 #pragma unroll
       for (int k = 0; k < CH; k += 32)
-        x = mma_ps(frag_col<OP>(sT, L::LDT, 16 * w + r16, k + kq),
-                   sfrag_pair<OP>(sDUh, sDUl, L::LDT, 16 * nt + r16, k + kq), x);
+        x = mma_ps(frag_col<OP>(sT, L::LDT, 16 * tw + r16, k + kq), sfrag_pair<OP>(sDUh, sDUl, L::LST, 16 * hf + r16, k + kq), x);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int r = 16 * w + 4 * q4 + ii, col = 16 * nt + r16;
-        float p = f32(sV[r * L::LDQ + col]) * x[ii];
+        const int r = 16 * tw + 4 * q4 + ii, col = 16 * hf + r16;
+        float p = f32(sV[r * L::LSQ + col]) * x[ii];
         p += __shfl_xor(p, 1);
         p += __shfl_xor(p, 2);
         p += __shfl_xor(p, 4);
@@ -422,140 +473,46 @@ __global__ __launch_bounds__(256) void kda_bwd_dv(const Args a) {
       }
     }
   }
+  pk.load(kh, rk, len);
+  pq.load(qh, rk, len);
+  pl.load(lh, rk, len);
+  __syncthreads();  // phase A's LDS reads are done; its region is reused below
 
-  // outputs of this kernel (fp32 workspace), rows 16w + 4q4 + ii
-  const float scale = a.scale;
-  float* wA = a.wsdAqk + blk * WB::DAQK;
-  float* wTU = a.wsdTU + blk * WB::DTU;
-  float* wQ = a.wsdQS + blk * WB::DQS;
-  float* wK = a.wsdKh + blk * WB::DKH;
-  float* wW = a.wsdW + blk * WB::DW;
+  // ---- hand-over: dAqk, dW to LDS; partial sums; phase B inputs to LDS
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
-    const int r = 16 * w + 4 * q4 + ii;
+    const int rr = 16 * tw + 4 * q4 + ii;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int c = 16 * nt + r16;
-      wA[r * CH + c] = c <= r ? scale * accA[nt][ii] : 0.f;
-      wTU[r * CH + c] = accT[nt][ii] * sBeta[c];
+    for (int jj = 0; jj < 2; ++jj) {
+      const int cc = 16 * (2 * hf + jj) + r16;
+      sA1[rr * L::LDA + cc] = cc <= rr ? scale * accA[jj][ii] : 0.f;
     }
 #pragma unroll
-    for (int nt = 0; nt < NKT; ++nt) {
-      const int c = 16 * nt + r16;
-      wQ[r * DK + c] = scale * accQ[nt][ii];
-      wK[r * DK + c] = accK[nt][ii];
-      wW[r * DK + c] = -accW[nt][ii];
-    }
-    if (r16 == 0) a.wsdBv[blk * WB::DBV + r] = bv[ii];
+    for (int jj = 0; jj < NKH; ++jj) sDW[rr * L::LDO + 16 * (hf * NKH + jj) + r16] = cvt<OP>(-accW[jj][ii]);
+    if (r16 == 0) sBv[hf * CH + rr] = bv[ii];
   }
-  sGamP[tid] = gp;  // part tid / DK of channel tid % DK
+  sGamP[tid] = gp;
+  float gGram[2][4];   // this wave's tiles of the un-beta strict Gram (for dbeta)
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) gGram[jj][ii] = gGm[(16 * tw + 4 * q4 + ii) * CH + 16 * (2 * hf + jj) + r16];
+  pk.template store_cvt<E>(sK, L::LDK, len);
+  pq.template store_cvt<E>(sQ, L::LDK, len);
+  pl.template store_cvt<float>(sG, L::LDG, len);
   __syncthreads();
   if (tid < DK) {
     float s = 0.f;
+#pragma unroll
     for (int p = 0; p < NT / DK; ++p) s += sGamP[p * DK + tid];
-    a.wsdGam[blk * WB::DGAM + tid] = s;
+    sDGam[tid] = s;
   }
-}
-
-// ---------------------------------------------------------------------------
-// chunk-parallel contractions over tokens, gated products and assembly
-// ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
-struct DkLds {
-  using OP = typename OpOf<E>::T;
-  static constexpr int PE = PADE<E>, PO = PADE<OP>;
-  static constexpr int LDG = DK + 4;
-  static constexpr int LDK = DK + PE;   // E rows
-  static constexpr int LDO = DK + PO;   // OP rows
-  static constexpr int LDT = CH + PO;
-  static constexpr int LDA = CH + 4;
-  static constexpr size_t G = 0;                                             // float [CH][LDG]  g, later dg
-  static constexpr size_t K = G + (size_t)CH * LDG * 4;                      // E     [CH][LDK]
-  static constexpr size_t Q = K + (size_t)CH * LDK * sizeof(E);              // E     [CH][LDK]
-  static constexpr size_t T = Q + (size_t)CH * LDK * sizeof(E);              // OP    [CH][LDT]
-  static constexpr size_t A1 = T + (size_t)CH * LDT * sizeof(OP);            // float [CH][LDA]  dAqk
-  static constexpr size_t A2 = A1 + (size_t)CH * LDA * 4;                    // float [CH][LDA]  dT, then dG
-  static constexpr size_t DW = A2 + (size_t)CH * LDA * 4;                    // OP    [CH][LDO]  dW, then Y
-  static constexpr size_t KP = DW + (size_t)CH * LDO * sizeof(OP);           // OP    [CH][LDO]  K+
-  static constexpr size_t BETA = KP + (size_t)CH * LDO * sizeof(OP);         // float [CH]
-  static constexpr size_t RED = BETA + CH * 4;                               // float [4][DK] reductions
-  static constexpr size_t BYTES = RED + 4 * DK * 4;
-  static constexpr size_t Y = DW;                                            // OP [CH][LDT] (after dW is dead)
-  static_assert(BYTES <= 163840, "dk kernel LDS");
-};
-
-template <typename E, typename O, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_bwd_dk(const Args a) {
-  using L = DkLds<E, DK, DV>;
-  using OP = typename L::OP;
-  using WB = WsBlock<E, DK, DV>;
-  using SE = typename std::conditional<sizeof(E) == 4, float, bf16>::type;   // gated products: split bf16
-  constexpr int NT = 256, NKT = DK / 16;
-  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-  const int j = blockIdx.x, h = blockIdx.y, H = a.H;
-  const ChunkInfo ci = a.chunks[j];
-  if (ci.len <= 0) return;
-  const int len = ci.len;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
-  const size_t blk = (size_t)j * H + h;
-  const size_t rk = (size_t)H * DK;
-
-  float* sG = reinterpret_cast<float*>(smem + L::G);
-  E* sK = reinterpret_cast<E*>(smem + L::K);
-  E* sQ = reinterpret_cast<E*>(smem + L::Q);
-  OP* sT = reinterpret_cast<OP*>(smem + L::T);
-  float* sA1 = reinterpret_cast<float*>(smem + L::A1);
-  float* sA2 = reinterpret_cast<float*>(smem + L::A2);
-  OP* sDW = reinterpret_cast<OP*>(smem + L::DW);
-  OP* sKp = reinterpret_cast<OP*>(smem + L::KP);
-  OP* sY = reinterpret_cast<OP*>(smem + L::Y);
-  float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
-  float* sRed = reinterpret_cast<float*>(smem + L::RED);
-
-  const E* qh = reinterpret_cast<const E*>(a.q) + (size_t)ci.t0 * rk + (size_t)h * DK;
-  const E* kh = reinterpret_cast<const E*>(a.k) + (size_t)ci.t0 * rk + (size_t)h * DK;
-  const E* lh = reinterpret_cast<const E*>(a.la) + (size_t)ci.t0 * rk + (size_t)h * DK;
-  const E* bh = reinterpret_cast<const E*>(a.beta) + (size_t)ci.t0 * H + h;
-  const float* gT = reinterpret_cast<const float*>(a.wsT) + blk * WB::TT;
-  const float* gGm = a.wsG + blk * WB::G;
-  const float* gA = a.wsdAqk + blk * WB::DAQK;
-  const float* gTU = a.wsdTU + blk * WB::DTU;
-  const float* gQS = a.wsdQS + blk * WB::DQS;
-  const float* gKH = a.wsdKh + blk * WB::DKH;
-  const float* gW = a.wsdW + blk * WB::DW;
-
-  // ---- 1. loads: log_alpha -> g (cumsum), k, q rows; T, dAqk, dW; beta
-  constexpr int NKS = DK / 32;
-  const int r = 16 * w + r16;   // row held by this lane in the row-block layout
-  float xk[NKS][8], xq[NKS][8], xl[NKS][8];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    load8<E>(kh + r * rk + 32 * ks + 8 * q4, r < len, xk[ks]);
-    load8<E>(qh + r * rk + 32 * ks + 8 * q4, r < len, xq[ks]);
-    load8<E>(lh + r * rk + 32 * ks + 8 * q4, r < len, xl[ks]);
-  }
-  if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const int c0 = 32 * ks + 8 * q4;
-    *reinterpret_cast<f32x4*>(sG + r * L::LDG + c0) = f32x4{xl[ks][0], xl[ks][1], xl[ks][2], xl[ks][3]};
-    *reinterpret_cast<f32x4*>(sG + r * L::LDG + c0 + 4) = f32x4{xl[ks][4], xl[ks][5], xl[ks][6], xl[ks][7]};
-    store4<E>(sK + r * L::LDK + c0, xk[ks][0], xk[ks][1], xk[ks][2], xk[ks][3]);
-    store4<E>(sK + r * L::LDK + c0 + 4, xk[ks][4], xk[ks][5], xk[ks][6], xk[ks][7]);
-    store4<E>(sQ + r * L::LDK + c0, xq[ks][0], xq[ks][1], xq[ks][2], xq[ks][3]);
-    store4<E>(sQ + r * L::LDK + c0 + 4, xq[ks][4], xq[ks][5], xq[ks][6], xq[ks][7]);
-  }
-  for (int o = tid; o < CH * CH; o += NT) {
-    const int rr = o / CH, cc = o % CH;
-    sT[rr * L::LDT + cc] = cvt<OP>(gT[o]);
-    sA1[rr * L::LDA + cc] = gA[o];
-  }
-  for (int o = tid; o < CH * DK; o += NT) sDW[(o / DK) * L::LDO + o % DK] = cvt<OP>(gW[o]);
-  __syncthreads();
+  // cumulative sum of log_alpha over the chunk (per channel, NT / DK row parts)
+  constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
   {
-    constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
     const int c = tid % DK, s = tid / DK;
     float acc = 0.f;
+#pragma unroll
     for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
       acc += sG[rr * L::LDG + c];
       sG[rr * L::LDG + c] = acc;
@@ -564,192 +521,169 @@ __global__ __launch_bounds__(256) void kda_bwd_dk(const Args a) {
   }
   __syncthreads();
   {
-    constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
     const int c = tid % DK, s = tid / DK;
-    if (s > 0) {
-      float off = 0.f;
-      for (int s2 = 0; s2 < s; ++s2) off += sRed[s2 * DK + c];
-      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
-    }
+    float off = 0.f;
+    for (int s2 = 0; s2 < s; ++s2) off += sRed[s2 * DK + c];
+#pragma unroll
+    for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
   }
   __syncthreads();
-  // K+ = k * exp(g) (operand copy)
   for (int o = tid; o < CH * DK; o += NT) {
     const int rr = o / DK, cc = o % DK;
     sKp[rr * L::LDO + cc] = cvt<OP>(f32(sK[rr * L::LDK + cc]) * __expf(sG[rr * L::LDG + cc]));
   }
   __syncthreads();
 
-  // per-lane C-tile layout: rows 16w + 4q4 + ii, columns 16nt + r16
-  // ---- 2. T^T dW (token tile w, all channel tiles), and rowsum(K+ * T^T dW)
-  f32x4 tdw[NKT];
+  // per-lane C-tile layout below: rows 16tw + 4q4 + ii, columns 16nt + r16
+  // ---- T^T dW (channel tiles of half hf) and rowsum(K+ * T^T dW)
+  f32x4 tdw[NKH];
   float dbeta[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nt = 0; nt < NKT; ++nt) {
+  for (int jj = 0; jj < NKH; ++jj) {
+    const int nt = hf * NKH + jj;
     f32x4 x = zero4();
 #pragma unroll
     for (int k = 0; k < CH; k += 32)
-      x = mma(frag_col<OP>(sT, L::LDT, 16 * w + r16, k + 8 * q4), frag_col<OP>(sDW, L::LDO, 16 * nt + r16, k + 8 * q4), x);
-    tdw[nt] = x;
+      x = mma(frag_col<OP>(sT, L::LDT, 16 * tw + r16, k + kq), frag_col<OP>(sDW, L::LDO, 16 * nt + r16, k + kq), x);
+    tdw[jj] = x;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const int rr = 16 * w + 4 * q4 + ii, cc = 16 * nt + r16;
+      const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;
       dbeta[ii] += f32(sK[rr * L::LDK + cc]) * __expf(sG[rr * L::LDG + cc]) * x[ii];
     }
   }
-  // ---- 3. dT = dW (b K+)^T + dT_U  (token tile w, 4 column tiles) -> sA2
-  {
-    f32x4 x[4];
+  // ---- dT = (dW K+^T + dU V^T) diag(beta), column tiles 2hf, 2hf+1 -> sA2
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      x[nt] = zero4();
+  for (int jj = 0; jj < 2; ++jj) {
+    const int nt = 2 * hf + jj;
+    f32x4 x = zero4();
 #pragma unroll
-      for (int k = 0; k < DK; k += 32)
-        x[nt] = mma(frag_row<OP>(sDW, L::LDO, 16 * w + r16, k + 8 * q4), frag_row<OP>(sKp, L::LDO, 16 * nt + r16, k + 8 * q4),
-                    x[nt]);
+    for (int k = 0; k < DK; k += 32)
+      x = mma(frag_row<OP>(sDW, L::LDO, 16 * tw + r16, k + kq), frag_row<OP>(sKp, L::LDO, 16 * nt + r16, k + kq), x);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;
+      sA2[rr * L::LDA + cc] = (x[ii] + accT[jj][ii]) * sBeta[cc];
     }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int rr = 16 * w + 4 * q4 + ii, cc = 16 * nt + r16;
-        sA2[rr * L::LDA + cc] = x[nt][ii] * sBeta[cc] + gTU[rr * CH + cc];
-      }
   }
   __syncthreads();  // dT complete; dW and K+ are dead
-  // ---- 4. Y = dT T^T -> sY ; dA = -strict(T^T Y) ; dG = b dA -> sA2 ; rowsum(dA * G)
-  {
+  // ---- Y = dT T^T -> sY
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 x = zero4();
+  for (int jj = 0; jj < 2; ++jj) {
+    const int nt = 2 * hf + jj;
+    f32x4 x = zero4();
 #pragma unroll
-      for (int k = 0; k < CH; k += 32) {
-        float y8[8];
+    for (int k = 0; k < CH; k += 32) {
+      float y8[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) y8[u] = sA2[(16 * w + r16) * L::LDA + k + 8 * q4 + u];
-        x = mma(frag_from<OP>(y8), frag_row<OP>(sT, L::LDT, 16 * nt + r16, k + 8 * q4), x);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sY[(16 * w + 4 * q4 + ii) * L::LDT + 16 * nt + r16] = cvt<OP>(x[ii]);
+      for (int u = 0; u < 8; ++u) y8[u] = sA2[(16 * tw + r16) * L::LDA + k + kq + u];
+      x = mma(frag_from<OP>(y8), frag_row<OP>(sT, L::LDT, 16 * nt + r16, k + kq), x);
     }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) sY[(16 * tw + 4 * q4 + ii) * L::LDT + 16 * nt + r16] = cvt<OP>(x[ii]);
   }
   __syncthreads();
-  {
-    f32x4 x[4];
+  // ---- dA = -strict(T^T Y); dG = beta dA -> sA2; dbeta += rowsum(dA * G)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      x[nt] = zero4();
+  for (int jj = 0; jj < 2; ++jj) {
+    const int nt = 2 * hf + jj;
+    f32x4 x = zero4();
 #pragma unroll
-      for (int k = 0; k < CH; k += 32)
-        x[nt] = mma(frag_col<OP>(sT, L::LDT, 16 * w + r16, k + 8 * q4), frag_col<OP>(sY, L::LDT, 16 * nt + r16, k + 8 * q4),
-                    x[nt]);
+    for (int k = 0; k < CH; k += 32)
+      x = mma(frag_col<OP>(sT, L::LDT, 16 * tw + r16, k + kq), frag_col<OP>(sY, L::LDT, 16 * nt + r16, k + kq), x);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;
+      const float da = cc < rr ? -x[ii] : 0.f;
+      dbeta[ii] += da * gGram[jj][ii];
+      sA2[rr * L::LDA + cc] = sBeta[rr] * da;
     }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int rr = 16 * w + 4 * q4 + ii, cc = 16 * nt + r16;
-        const float da = cc < rr ? -x[nt][ii] : 0.f;
-        dbeta[ii] += da * gGm[rr * CH + cc];
-        sA2[rr * L::LDA + cc] = sBeta[rr] * da;   // dG (each element written by its only reader-to-be later)
-      }
   }
   __syncthreads();
 
-  // ---- 5. gated products with per-block reference rows (split bf16 operands)
-  // row side, block a = w: dq_g = e^{g_r - g_m} (dAqk . R_a), dkp_g = e^{g_r - g_m} (dG . R_a),
-  // R_a[i] = k_i e^{g_m - g_i}; column side, block b = w:
+  // ---- per channel tile of half hf: gated products, then the assembly of dq, dk, dg.
+  // Gated products use per-block reference rows (split bf16 operands):
+  // row side, block a = tw: dq_g = e^{g_r - g_m} (dAqk . R_a), dkp_g = e^{g_r - g_m} (dG . R_a),
+  // R_a[i] = k_i e^{g_m - g_i}; column side, block b = tw:
   // dkm = sum_{a >= b} e^{g_m(a) - g_i} ((dAqk_a^T q_a + dG_a^T k_a) e^{g_a - g_m(a)})
-  f32x4 dqg[NKT], dkpg[NKT], dkm[NKT];
+  O* dqo = reinterpret_cast<O*>(a.dq) + (size_t)ci.t0 * rk + (size_t)h * DK;
+  O* dko = reinterpret_cast<O*>(a.dk_) + (size_t)ci.t0 * rk + (size_t)h * DK;
+  O* dlo = reinterpret_cast<O*>(a.dla) + (size_t)ci.t0 * rk + (size_t)h * DK;
+  float dgv[NKH][4];
+  float khs[NKH];   // column sums over this lane's rows of dKh * Kh (for dg_C)
 #pragma unroll
-  for (int nt = 0; nt < NKT; ++nt) dqg[nt] = dkpg[nt] = dkm[nt] = zero4();
-  {
-    const int ab = w, ref = 16 * ab + 8;
-    const int kmax = 16 * (ab + 1);  // columns i < kmax can be nonzero
-#pragma unroll
-    for (int nt = 0; nt < NKT; ++nt) {
-      const int cc = 16 * nt + r16;
+  for (int jj = 0; jj < NKH; ++jj) {
+    const int cc = 16 * (hf * NKH + jj) + r16;
+    f32x4 dqg = zero4(), dkpg = zero4(), dkm = zero4();
+    {
+      const int ab = tw, ref = 16 * ab + 8;
+      const int kmax = 16 * (ab + 1);  // columns i < kmax can be nonzero
+      const float gref = sG[ref * L::LDG + cc];
       for (int k = 0; k < kmax; k += 32) {
-        const SFrag<SE> fa1 = sfrag_row<SE>(sA1, L::LDA, 16 * ab + r16, k + 8 * q4);
-        const SFrag<SE> fa2 = sfrag_row<SE>(sA2, L::LDA, 16 * ab + r16, k + 8 * q4);
+        const SFrag<SE> fa1 = sfrag_row<SE>(sA1, L::LDA, 16 * ab + r16, k + kq);
+        const SFrag<SE> fa2 = sfrag_row<SE>(sA2, L::LDA, 16 * ab + r16, k + kq);
         float xr[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int i = k + 8 * q4 + u;
-          xr[u] = i < kmax ? f32(sK[i * L::LDK + cc]) * __expf(sG[ref * L::LDG + cc] - sG[i * L::LDG + cc]) : 0.f;
+          const int i = k + kq + u;
+          xr[u] = i < kmax ? f32(sK[i * L::LDK + cc]) * __expf(gref - sG[i * L::LDG + cc]) : 0.f;
         }
         const SFrag<SE> fr = sfrag_from<SE>(xr);
-        dqg[nt] = mma_ss(fa1, fr, dqg[nt]);
-        dkpg[nt] = mma_ss(fa2, fr, dkpg[nt]);
+        dqg = mma_ss(fa1, fr, dqg);
+        dkpg = mma_ss(fa2, fr, dkpg);
       }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int rr = 16 * ab + 4 * q4 + ii;
-        const float e = __expf(sG[rr * L::LDG + cc] - sG[ref * L::LDG + cc]);
-        dqg[nt][ii] *= e;
-        dkpg[nt][ii] *= e;
+        const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gref);
+        dqg[ii] *= e;
+        dkpg[ii] *= e;
       }
     }
-  }
-  {
-    const int b = w;
-    for (int ab = b; ab < 4; ++ab) {
-      const int ref = 16 * ab + 8;
-#pragma unroll
-      for (int nt = 0; nt < NKT; ++nt) {
-        const int cc = 16 * nt + r16;
+    {
+      const int b = tw;
+      for (int ab = b; ab < 4; ++ab) {
+        const int ref = 16 * ab + 8;
         // A[m = i][k = r'] : r' < 16 -> dAqk[16a + r'][i], r' >= 16 -> dG[16a + r' - 16][i]
         const float* srcA = q4 < 2 ? sA1 : sA2;
         const int rbase = 16 * ab + 8 * (q4 & 1);
         const SFrag<SE> fa = sfrag_col_f32<SE>(srcA, L::LDA, 16 * b + r16, rbase);
+        const float gref = sG[ref * L::LDG + cc];
         float xl8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int rr = rbase + u;
           const float src = q4 < 2 ? f32(sQ[rr * L::LDK + cc]) : f32(sK[rr * L::LDK + cc]);
-          xl8[u] = src * __expf(sG[rr * L::LDG + cc] - sG[ref * L::LDG + cc]);
+          xl8[u] = src * __expf(sG[rr * L::LDG + cc] - gref);
         }
         const f32x4 y = mma_ss(fa, sfrag_from<SE>(xl8), zero4());
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int i = 16 * b + 4 * q4 + ii;
-          dkm[nt][ii] += __expf(sG[ref * L::LDG + cc] - sG[i * L::LDG + cc]) * y[ii];
+          dkm[ii] += __expf(gref - sG[i * L::LDG + cc]) * y[ii];
         }
       }
     }
-  }
-
-  // ---- 6. assembly: dq, dk, dg (rows 16w + 4q4 + ii, channel tiles nt)
-  O* dqh = reinterpret_cast<O*>(a.dq) + (size_t)ci.t0 * rk + (size_t)h * DK;
-  O* dkh_ = reinterpret_cast<O*>(a.dk_) + (size_t)ci.t0 * rk + (size_t)h * DK;
-  O* dlh = reinterpret_cast<O*>(a.dla) + (size_t)ci.t0 * rk + (size_t)h * DK;
-  float dgv[NKT][4];
-  float khs[NKT];   // column sums over this lane's rows of dKh * Kh  (for dg_C)
-#pragma unroll
-  for (int nt = 0; nt < NKT; ++nt) {
-    khs[nt] = 0.f;
-    const int cc = 16 * nt + r16;
+    // assembly (rows 16tw + 4q4 + ii)
+    khs[jj] = 0.f;
     const float gl = sG[(CH - 1) * L::LDG + cc];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const int rr = 16 * w + 4 * q4 + ii;
+      const int rr = 16 * tw + 4 * q4 + ii;
       const float g = sG[rr * L::LDG + cc];
       const float eg = __expf(g);
       const float kv = f32(sK[rr * L::LDK + cc]), qv = f32(sQ[rr * L::LDK + cc]);
-      const float dq = eg * gQS[rr * DK + cc] + dqg[nt][ii];
-      const float dkp = eg * sBeta[rr] * tdw[nt][ii] + dkpg[nt][ii];
-      const float dkmv = dkm[nt][ii];
-      const float dkh = __expf(gl - g) * gKH[rr * DK + cc];
-      const float dk = dkp + dkmv + dkh;
-      dgv[nt][ii] = dq * qv + (dkp - dkmv - dkh) * kv;
-      khs[nt] += dkh * kv;
+      const float dq = eg * scale * accQ[jj][ii] + dqg[ii];
+      const float dkp = eg * sBeta[rr] * tdw[jj][ii] + dkpg[ii];
+      const float dkh = __expf(gl - g) * accK[jj][ii];
+      dgv[jj][ii] = dq * qv + (dkp - dkm[ii] - dkh) * kv;
+      khs[jj] += dkh * kv;
       if (rr < len) {
-        dqh[(size_t)rr * rk + cc] = cvt<O>(dq);
-        dkh_[(size_t)rr * rk + cc] = cvt<O>(dk);
+        dqo[(size_t)rr * rk + cc] = cvt<O>(dq);
+        dko[(size_t)rr * rk + cc] = cvt<O>(dkp + dkm[ii] + dkh);
       }
     }
   }
-  // rowsums for dbeta: reduce over the 16 column lanes, then over nothing else
+  // dbeta partials: reduce over the 16 column lanes; halves meet in LDS
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     float p = dbeta[ii];
@@ -757,58 +691,48 @@ __global__ __launch_bounds__(256) void kda_bwd_dk(const Args a) {
     p += __shfl_xor(p, 2);
     p += __shfl_xor(p, 4);
     p += __shfl_xor(p, 8);
-    dbeta[ii] = p;
+    if (r16 == 0) sDbp[hf * CH + 16 * tw + 4 * q4 + ii] = p;
   }
-  __syncthreads();  // all reads of g done before dg overwrites it
-  // dg -> LDS (sG region), column sums of dKh*Kh -> sRed
+  __syncthreads();  // all reads of g are done before dg overwrites it
 #pragma unroll
-  for (int nt = 0; nt < NKT; ++nt)
+  for (int jj = 0; jj < NKH; ++jj) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) sG[(16 * w + 4 * q4 + ii) * L::LDG + 16 * nt + r16] = dgv[nt][ii];
-  {
-    // reduce khs over q4 (lanes differing in bits 4,5) then over waves via sRed
-#pragma unroll
-    for (int nt = 0; nt < NKT; ++nt) {
-      float p = khs[nt];
-      p += __shfl_xor(p, 16);
-      p += __shfl_xor(p, 32);
-      if (q4 == 0) sRed[w * DK + 16 * nt + r16] = p;
-    }
-  }
-  if (r16 == 0) {
-    const float* gbv = a.wsdBv + blk * WB::DBV;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int rr = 16 * w + 4 * q4 + ii;
-      if (rr < len) reinterpret_cast<O*>(a.dbeta)[((size_t)ci.t0 + rr) * H + h] = cvt<O>(dbeta[ii] + gbv[rr]);
-    }
+    for (int ii = 0; ii < 4; ++ii) sG[(16 * tw + 4 * q4 + ii) * L::LDG + 16 * (hf * NKH + jj) + r16] = dgv[jj][ii];
+    float p = khs[jj];
+    p += __shfl_xor(p, 16);
+    p += __shfl_xor(p, 32);
+    if (q4 == 0) sRed[tw * DK + 16 * (hf * NKH + jj) + r16] = p;
   }
   __syncthreads();
-  // dg_C terms on the last row, then the reverse cumulative sum over rows -> dlog_alpha
-  if (tid < DK) {
-    const int c = tid;
-    float s = 0.f;
-    for (int ww = 0; ww < 4; ++ww) s += sRed[ww * DK + c];
-    const float gl_exp = a.wsGam[blk * WB::GAM + c];
-    sG[(CH - 1) * L::LDG + c] += s + a.wsdGam[blk * WB::DGAM + c] * gl_exp;
+  if (tid < CH) {
+    const int rr = tid;
+    if (rr < len)
+      reinterpret_cast<O*>(a.dbeta)[((size_t)ci.t0 + rr) * H + h] =
+          cvt<O>((sDbp[rr] + sDbp[CH + rr]) + (sBv[rr] + sBv[CH + rr]));
+  } else if (tid >= 64 && tid < 64 + DK) {
+    // dg_C: the last row collects sum_r dKh * Kh and dGamma_C * Gamma_C
+    const int c = tid - 64;
+    const float s = (sRed[c] + sRed[DK + c]) + (sRed[2 * DK + c] + sRed[3 * DK + c]);
+    sG[(CH - 1) * L::LDG + c] += s + sDGam[c] * a.wsGam[blk * WB::GAM + c];
   }
   __syncthreads();
+  // reverse cumulative sum over rows -> dlog_alpha
   {
-    constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
     const int c = tid % DK, s = tid / DK;
     float acc = 0.f;
+#pragma unroll
     for (int rr = (s + 1) * RPS - 1; rr >= s * RPS; --rr) acc += sG[rr * L::LDG + c];
-    sRed[s * DK + c] = acc;   // total of this part
+    sRed[s * DK + c] = acc;
   }
   __syncthreads();
   {
-    constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
     const int c = tid % DK, s = tid / DK;
     float acc = 0.f;
     for (int s2 = s + 1; s2 < NSPLIT; ++s2) acc += sRed[s2 * DK + c];
+#pragma unroll
     for (int rr = (s + 1) * RPS - 1; rr >= s * RPS; --rr) {
       acc += sG[rr * L::LDG + c];
-      if (rr < len) dlh[(size_t)rr * rk + c] = cvt<O>(acc);
+      if (rr < len) dlo[(size_t)rr * rk + c] = cvt<O>(acc);
     }
   }
 }
@@ -829,9 +753,8 @@ hipError_t launch_bwd(const Args& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.max_chunks > 0) {
-    KDA_TIMED("kda_bwd_dv", st, hipLaunchKernelGGL((kda_bwd_dv<E, O, DK, DV>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    KDA_TIMED("kda_bwd_dk", st, hipLaunchKernelGGL((kda_bwd_dk<E, O, DK, DV>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
+    KDA_TIMED("kda_bwd_chunk", st,
+              hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV>), dim3(a.max_chunks, a.H), dim3(512), 0, st, a));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -231,20 +231,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+template <typename E> __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d);
+
 template <typename E, int ROWS, int COLS, int NT>
 struct TileCopy {
   static constexpr int VPR = COLS * (int)sizeof(E) / 16;  // vectors per row
   static constexpr int NV = ROWS * VPR;
   static constexpr int PER = (NV + NT - 1) / NT;
   u32x4 r[PER];
-  __device__ __forceinline__ void load(const E* __restrict__ src, size_t src_ld) {
+  // Rows >= nrows (nrows >= 1) are not read: they re-read row 0, and a store
+  // with the same nrows writes zeros there.
+  __device__ __forceinline__ void load(const E* __restrict__ src, size_t src_ld, int nrows = ROWS) {
     static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
       // threads past the tile re-read vector 0 (always in bounds) and skip the store,
       // so every register is defined on every path
       const int v0 = threadIdx.x + I * NT;
       const int v = (NV % NT == 0 || v0 < NV) ? v0 : 0;
       const int row = v / VPR, cv = v % VPR;
-      r[I] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src + row * src_ld) + cv * 16);
+      const int rr = row < nrows ? row : 0;
+      r[I] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src + rr * src_ld) + cv * 16);
     });
   }
   __device__ __forceinline__ void store(E* dst, int dst_ld) const {
@@ -253,6 +258,36 @@ struct TileCopy {
       if (NV % NT == 0 || v < NV) {
         const int row = v / VPR, cv = v % VPR;
         *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst + row * dst_ld) + cv * 16) = r[I];
+      }
+    });
+  }
+  // Store converted to D; rows >= nrows are stored as zeros.
+  template <typename D>
+  __device__ __forceinline__ void store_cvt(D* dst, int dst_ld, int nrows) const {
+    constexpr int EPV = 16 / (int)sizeof(E);
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = threadIdx.x + I * NT;
+      if (NV % NT == 0 || v < NV) {
+        const int row = v / VPR, c0 = (v % VPR) * EPV;
+        const E* e = reinterpret_cast<const E*>(&r[I]);
+        const bool ok = row < nrows;
+#pragma unroll
+        for (int i = 0; i < EPV; i += 4)
+          store4<D>(dst + row * dst_ld + c0 + i, ok ? f32(e[i]) : 0.f, ok ? f32(e[i + 1]) : 0.f,
+                    ok ? f32(e[i + 2]) : 0.f, ok ? f32(e[i + 3]) : 0.f);
+      }
+    });
+  }
+  // fp32 tile stored as a split pair (hi, lo) of D (lo unused when D is fp32).
+  template <typename D>
+  __device__ __forceinline__ void store_split(D* hi, D* lo, int dst_ld) const {
+    static_assert(sizeof(E) == 4, "split store takes an fp32 tile");
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = threadIdx.x + I * NT;
+      if (NV % NT == 0 || v < NV) {
+        const int row = v / VPR, c0 = (v % VPR) * 4;
+        const float* x = reinterpret_cast<const float*>(&r[I]);
+        store4_split<D>(hi + row * dst_ld + c0, lo + row * dst_ld + c0, x[0], x[1], x[2], x[3]);
       }
     });
   }
@@ -349,13 +384,6 @@ struct WsBlock {
   static constexpr size_t U = (size_t)DV * CH;     // U^T [DV][CH]   float
   static constexpr size_t DS = (size_t)DK * DV;    // dS' [DV][DK]   float
   static constexpr size_t DU = (size_t)DV * CH;    // dU^T [DV][CH]  float
-  static constexpr size_t DAQK = (size_t)CH * CH;  // float
-  static constexpr size_t DQS = (size_t)CH * DK;   // float
-  static constexpr size_t DKH = (size_t)CH * DK;   // float
-  static constexpr size_t DW = (size_t)CH * DK;    // float
-  static constexpr size_t DTU = (size_t)CH * CH;   // float
-  static constexpr size_t DGAM = DK;               // float
-  static constexpr size_t DBV = CH;                // float
 };
 
 }  // namespace kda

@@ -38,13 +38,6 @@ struct Args {
   float* wsU;               // U^T, fp32 [DV][CH]
   float* wsdS;              // gradient of the state leaving each chunk, fp32 [DV][DK]
   float* wsdU;              // dU^T, fp32 [DV][CH]
-  float* wsdAqk;            // scale * tril(dO U^T), fp32 [CH][CH]
-  float* wsdQS;             // scale * dO S^T, fp32 [CH][DK]
-  float* wsdKh;             // U dS'^T, fp32 [CH][DK]
-  float* wsdW;              // -dU S^T, fp32 [CH][DK]
-  float* wsdTU;             // dU V^T diag(beta), fp32 [CH][CH]
-  float* wsdGam;            // rowsum over values of dS' * S, fp32 [DK]
-  float* wsdBv;             // rowsum(V * T^T dU), fp32 [CH]
   int dvs;                  // value-column slice width of the sequential passes
   int out_bf16;             // outputs and gradients stored as bf16 (else fp32)
 };
