@@ -29,6 +29,8 @@
 // columns b uses a reference row m in the middle of row block a and factors
 // exp(g_r - g_i) = exp(g_r - g_m) * exp(g_m - g_i), so no factor exceeds the
 // decay of 8 consecutive tokens.
+#include <algorithm>
+
 #include "kda_internal.hpp"
 
 namespace kda {
@@ -381,6 +383,340 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// prep for bf16 inputs: persistent, 8 waves
+// ---------------------------------------------------------------------------
+// One work-group per compute unit walks the chunk-heads item, item + grid, ...
+// (item = chunk * H + head).  The inputs of the next item are loaded into
+// registers while the current one is computed, so the loads overlap compute.
+// Wave w: row block a = w & 3 of the Gram blocks, with the (a + 1) column
+// blocks split between the two waves w and w + 4.  T = (I + A)^-1: the four
+// diagonal 16x16 blocks by substitution in one wave (each lane keeps one
+// column in registers, so no cross-lane traffic), then the off-diagonal
+// blocks level by level with fp32 MFMA: T_ab = -T_aa sum_k A_ak T_kb.
+template <int DK, int DV>
+struct Prep8Lds {
+  static constexpr int LDG = DK + 4;   // float [CH][LDG]  log_alpha, then g
+  static constexpr int LDK = DK + 8;   // bf16  [CH][LDK]  k, q
+  static constexpr int LDT = CH + 8;   // fp16  [*][LDT]   K+^T, V^T, Te
+  static constexpr int LDA = CH + 4;   // float [CH][LDA]  A, T
+  static constexpr size_t G = 0;
+  static constexpr size_t K = G + (size_t)CH * LDG * 4;
+  static constexpr size_t Q = K + (size_t)CH * LDK * 2;
+  static constexpr size_t GKQ_END = Q + (size_t)CH * LDK * 2;
+  // once the Gram blocks are done, T and Te take the place of g, k and q
+  static constexpr size_t T = 0;
+  static constexpr size_t TE = T + (size_t)CH * LDA * 4;
+  static_assert(TE + (size_t)CH * LDT * 2 <= GKQ_END, "T, Te alias g, k, q");
+  static constexpr size_t KPT = GKQ_END;                      // fp16  [DK][LDT]
+  static constexpr size_t VT = KPT + (size_t)DK * LDT * 2;    // fp16  [DV][LDT]
+  static constexpr size_t A = VT + (size_t)DV * LDT * 2;      // float [CH][LDA]  beta * strict Gram
+  static constexpr size_t X = A + (size_t)CH * LDA * 4;       // float [3][256]   off-diagonal partial sums
+  static constexpr size_t BETA = X + 3 * 256 * 4;             // float [CH]
+  static constexpr size_t RED = BETA + CH * 4;                // float [512]
+  static constexpr size_t BYTES = RED + 512 * 4;
+  static_assert(BYTES <= 163840, "prep LDS");
+};
+
+// C(16x16) += A(16x16) B(16x16), fp32 operands in LDS (row-major), fp32 MFMA.
+// Lane (r16, q4) supplies A[r16][4q4 + m] and B[4q4 + m][r16] to MFMA m.
+__device__ __forceinline__ f32x4 mm16_f32(const float* A, int lda, const float* B, int ldb, f32x4 c) {
+  const int l = lane_id(), r16 = l & 15, q4 = l >> 4;
+  const f32x4 av = *reinterpret_cast<const f32x4*>(A + r16 * lda + 4 * q4);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], B[(4 * q4 + m) * ldb + r16], c, 0, 0, 0);
+  return c;
+}
+
+template <int DK, int DV, bool BWD>
+__global__ __launch_bounds__(512) void kda_prep8(const Args a) {
+  using L = Prep8Lds<DK, DV>;
+  using E = bf16;
+  using OP = f16;
+  using WB = WsBlock<E, DK, DV>;
+  constexpr int NT = 512, NKS = DK / 32;
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
+  const int H = a.H;
+  const int n_items = a.max_chunks * H;
+  const size_t rk = (size_t)H * DK, rv = (size_t)H * DV;
+
+  float* sG = reinterpret_cast<float*>(smem + L::G);
+  E* sK = reinterpret_cast<E*>(smem + L::K);
+  E* sQ = reinterpret_cast<E*>(smem + L::Q);
+  float* sT = reinterpret_cast<float*>(smem + L::T);
+  OP* sTe = reinterpret_cast<OP*>(smem + L::TE);
+  OP* sKpT = reinterpret_cast<OP*>(smem + L::KPT);
+  OP* sVT = reinterpret_cast<OP*>(smem + L::VT);
+  float* sA = reinterpret_cast<float*>(smem + L::A);
+  float* sX = reinterpret_cast<float*>(smem + L::X);
+  float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
+  float* sRed = reinterpret_cast<float*>(smem + L::RED);
+
+  const E* gq = reinterpret_cast<const E*>(a.q);
+  const E* gk = reinterpret_cast<const E*>(a.k);
+  const E* gl = reinterpret_cast<const E*>(a.la);
+  const E* gv = reinterpret_cast<const E*>(a.v);
+  const E* gb = reinterpret_cast<const E*>(a.beta);
+
+  TileCopy<E, CH, DK, NT> pq, pk, pl;
+  TileCopy<E, CH, DV, NT> pv;
+  float pb = 0.f;
+  auto fetch = [&](int item, const ChunkInfo& c) __attribute__((always_inline)) {
+    const int h = item % H;
+    const size_t t0 = (size_t)c.t0;
+    pq.load(gq + t0 * rk + (size_t)h * DK, rk, c.len);
+    pk.load(gk + t0 * rk + (size_t)h * DK, rk, c.len);
+    pl.load(gl + t0 * rk + (size_t)h * DK, rk, c.len);
+    pv.load(gv + t0 * rv + (size_t)h * DV, rv, c.len);
+    pb = tid < c.len ? f32(gb[(t0 + tid) * H + h]) : 0.f;
+  };
+
+  int item = blockIdx.x;
+  ChunkInfo ci = item < n_items ? a.chunks[item / H] : ChunkInfo{0, 0, 0, 0};
+  if (ci.len > 0) fetch(item, ci);
+  while (ci.len > 0) {   // the same value in every thread
+    const size_t blk = (size_t)item;   // == chunk * H + head
+    const int len = ci.len;
+    OP* wW = reinterpret_cast<OP*>(a.wsW) + blk * WB::W;
+    OP* wKhT = reinterpret_cast<OP*>(a.wsKhT) + blk * WB::KHT;
+    OP* wQt = reinterpret_cast<OP*>(a.wsQt) + blk * WB::QT;
+    OP* wAqk = reinterpret_cast<OP*>(a.wsAqk) + blk * WB::AQK;
+    float* wGam = a.wsGam + blk * WB::GAM;
+
+    __syncthreads();  // the previous item's LDS reads are done
+    pk.template store_cvt<E>(sK, L::LDK, len);
+    pq.template store_cvt<E>(sQ, L::LDK, len);
+    pl.template store_cvt<float>(sG, L::LDG, len);
+    {
+      // V^T: each 16-byte piece is 8 value columns of one token
+      constexpr int VPR = DV / 8;
+      static_for<0, decltype(pv)::PER>([&](auto I) __attribute__((always_inline)) {
+        const int v = tid + I * NT;
+        if (decltype(pv)::NV % NT == 0 || v < decltype(pv)::NV) {
+          const int row = v / VPR, c0 = (v % VPR) * 8;
+          const E* e = reinterpret_cast<const E*>(&pv.r[I]);
+          const bool ok = row < len;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sVT[(c0 + i) * L::LDT + row] = cvt<OP>(ok ? f32(e[i]) : 0.f);
+        }
+      });
+    }
+    if (tid < CH) sBeta[tid] = pb;
+    const int nitem = item + (int)gridDim.x;
+    const ChunkInfo nci = nitem < n_items ? a.chunks[nitem / H] : ChunkInfo{0, 0, 0, 0};
+    if (nci.len > 0) fetch(nitem, nci);
+    __syncthreads();
+
+    // ---- cumulative sum of log_alpha over the chunk (per channel, NT / DK row parts)
+    constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
+    {
+      const int c = tid % DK, s = tid / DK;
+      float acc = 0.f;
+#pragma unroll
+      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
+        acc += sG[rr * L::LDG + c];
+        sG[rr * L::LDG + c] = acc;
+      }
+      sRed[s * DK + c] = acc;
+    }
+    __syncthreads();
+    {
+      const int c = tid % DK, s = tid / DK;
+      float off = 0.f;
+      for (int s2 = 0; s2 < s; ++s2) off += sRed[s2 * DK + c];
+#pragma unroll
+      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
+    }
+    __syncthreads();
+
+    // ---- elementwise: Qt (token rows), K+^T to LDS and Kh^T (channel rows), Gamma_C
+    {
+      constexpr int VA = DK / 8;   // 8-channel pieces per token row
+#pragma unroll
+      for (int i = 0; i < CH * VA / NT; ++i) {
+        const int v = tid + i * NT, r = v / VA, c0 = (v % VA) * 8;
+        float y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) y[u] = f32(sQ[r * L::LDK + c0 + u]) * __expf(sG[r * L::LDG + c0 + u]);
+        store4<OP>(wQt + r * DK + c0, y[0], y[1], y[2], y[3]);
+        store4<OP>(wQt + r * DK + c0 + 4, y[4], y[5], y[6], y[7]);
+        if constexpr (BWD) {
+          // Kh token-major in fp32 (the reverse pass multiplies it as a split operand)
+          float* wKhF = a.wsKhF + blk * WB::KHF;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            y[u] = f32(sK[r * L::LDK + c0 + u]) * __expf(sG[(CH - 1) * L::LDG + c0 + u] - sG[r * L::LDG + c0 + u]);
+          *reinterpret_cast<f32x4*>(wKhF + r * DK + c0) = f32x4{y[0], y[1], y[2], y[3]};
+          *reinterpret_cast<f32x4*>(wKhF + r * DK + c0 + 4) = f32x4{y[4], y[5], y[6], y[7]};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < DK * (CH / 8) / NT; ++i) {
+        const int v = tid + i * NT, c = v / (CH / 8), t0 = (v % (CH / 8)) * 8;
+        const float glast = sG[(CH - 1) * L::LDG + c];
+        float kp[8], kh[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float g = sG[(t0 + u) * L::LDG + c], kv = f32(sK[(t0 + u) * L::LDK + c]);
+          kp[u] = kv * __expf(g);
+          kh[u] = kv * __expf(glast - g);
+        }
+        store4<OP>(sKpT + c * L::LDT + t0, kp[0], kp[1], kp[2], kp[3]);
+        store4<OP>(sKpT + c * L::LDT + t0 + 4, kp[4], kp[5], kp[6], kp[7]);
+        store4<OP>(wKhT + c * CH + t0, kh[0], kh[1], kh[2], kh[3]);
+        store4<OP>(wKhT + c * CH + t0 + 4, kh[4], kh[5], kh[6], kh[7]);
+      }
+      if (tid < DK) wGam[tid] = __expf(sG[(CH - 1) * L::LDG + tid]);
+    }
+
+    // ---- decayed Gram blocks (split bf16 operands; reference row m = 16a + 8)
+    {
+      const int ab = w & 3, pp = w >> 2;
+      const int nb = ab + 1, split = (nb + 1) >> 1;
+      const int b0 = pp ? split : 0, b1 = pp ? nb : split;
+      const int ref = 16 * ab + 8;
+      if (b0 < b1) {
+        const int r = 16 * ab + r16;
+        SFrag<bf16> fk[NKS], fq[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int c0 = 32 * ks + 8 * q4;
+          float yk[8], yq[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float e = __expf(sG[r * L::LDG + c0 + u] - sG[ref * L::LDG + c0 + u]);
+            yk[u] = f32(sK[r * L::LDK + c0 + u]) * e;
+            yq[u] = f32(sQ[r * L::LDK + c0 + u]) * e;
+          }
+          fk[ks] = sfrag_from<bf16>(yk);
+          fq[ks] = sfrag_from<bf16>(yq);
+        }
+        for (int b = b0; b < b1; ++b) {
+          f32x4 akk = zero4(), aqk = zero4();
+          const int i = 16 * b + r16;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const int c0 = 32 * ks + 8 * q4;
+            float xr[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              xr[u] = f32(sK[i * L::LDK + c0 + u]) * __expf(sG[ref * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
+            const SFrag<bf16> fr = sfrag_from<bf16>(xr);
+            akk = mma_ss(fk[ks], fr, akk);
+            aqk = mma_ss(fq[ks], fr, aqk);
+          }
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int rr = 16 * ab + 4 * q4 + ii, cc = 16 * b + r16;
+            sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[ii] : 0.f;
+            wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[ii] : 0.f);
+            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[ii] : 0.f;
+          }
+        }
+      }
+      if (pp) {
+        for (int b = nb; b < 4; ++b) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int rr = 16 * ab + 4 * q4 + ii, cc = 16 * b + r16;
+            sA[rr * L::LDA + cc] = 0.f;
+            wAqk[rr * CH + cc] = cvt<OP>(0.f);
+            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = 0.f;
+          }
+        }
+      }
+    }
+    __syncthreads();  // A complete; g, k, q are dead (T and Te reuse their space)
+
+    // ---- T = (I + A)^-1
+    if (w == 0) {
+      // diagonal blocks: lane (block bb, column c) keeps column c of T_bb in registers
+      const int bb = l >> 4, c = l & 15;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float* nrow = sA + (16 * bb + r) * L::LDA + 16 * bb;
+        float s = 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < r; i4 += 4) {
+          const f32x4 nv = *reinterpret_cast<const f32x4*>(nrow + i4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (i4 + u < r) s += nv[u] * x[i4 + u];
+        }
+        x[r] = r == c ? 1.f : (r > c ? -s : 0.f);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(16 * bb + r) * L::LDA + 16 * bb + c] = x[r];
+    } else {
+      // blocks above the diagonal are zero
+      for (int o = tid - 64; o < 6 * 256; o += NT - 64) {
+        const int blkid = o >> 8, e = o & 255;
+        const int ra = blkid < 3 ? 0 : (blkid < 5 ? 1 : 2);
+        const int cb = blkid < 3 ? blkid + 1 : (blkid < 5 ? blkid - 1 : 3);
+        sT[(16 * ra + (e >> 4)) * L::LDA + 16 * cb + (e & 15)] = 0.f;
+      }
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+      const int nblk = 4 - d;
+      if (w < nblk) {
+        const int bc = w, ar = w + d;
+        f32x4 x = zero4();
+        for (int kb = bc; kb < ar; ++kb)
+          x = mm16_f32(sA + 16 * ar * L::LDA + 16 * kb, L::LDA, sT + 16 * kb * L::LDA + 16 * bc, L::LDA, x);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sX[w * 256 + (4 * q4 + ii) * 16 + r16] = x[ii];
+      }
+      __syncthreads();
+      if (w < nblk) {
+        const int bc = w, ar = w + d;
+        const f32x4 y = mm16_f32(sT + 16 * ar * L::LDA + 16 * ar, L::LDA, sX + w * 256, 16, zero4());
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sT[(16 * ar + 4 * q4 + ii) * L::LDA + 16 * bc + r16] = -y[ii];
+      }
+      __syncthreads();
+    }
+
+    // ---- Te = T diag(beta) in fp16; W = Te K+, U~ = Te V
+    for (int o = tid; o < CH * CH / 4; o += NT) {
+      const int rr = (4 * o) / CH, cc = (4 * o) % CH;
+      const f32x4 t = *reinterpret_cast<const f32x4*>(sT + rr * L::LDA + cc);
+      store4<OP>(sTe + rr * L::LDT + cc, t[0] * sBeta[cc], t[1] * sBeta[cc + 1], t[2] * sBeta[cc + 2], t[3] * sBeta[cc + 3]);
+      if constexpr (BWD) *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.wsT) + blk * WB::TT + rr * CH + cc) = t;
+    }
+    __syncthreads();
+    {
+      // W^T tiles: C'[ch][tok] = sum_i K+^T[ch][i] Te[tok][i]; lane gets W[tok][4 consecutive ch]
+      constexpr int NTI = (CH / 16) * (DK / 16);
+      for (int t = w; t < NTI; t += 8) {
+        const int mt = t % (CH / 16), nt = t / (CH / 16);
+        const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sKpT, L::LDT, 16 * nt + rr, k); },
+                                      [&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); },
+                                      zero4());
+        store4<OP>(wW + (16 * mt + r16) * DK + 16 * nt + 4 * q4, acc[0], acc[1], acc[2], acc[3]);
+      }
+      // U~ tiles: C[tok][dv]; lane holds 4 consecutive tokens of one value column -> U~^T rows
+      // (fp32 for the backward, where its rounding would reach the gradients)
+      constexpr int NTU = (CH / 16) * (DV / 16);
+      for (int t = w; t < NTU; t += 8) {
+        const int mt = t % (CH / 16), nt = t / (CH / 16);
+        const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); },
+                                      [&](int rr, int k) { return frag_row<OP>(sVT, L::LDT, 16 * nt + rr, k); },
+                                      zero4());
+        if constexpr (BWD)
+          *reinterpret_cast<f32x4*>(a.wsUtF + blk * WB::UTF + (16 * nt + r16) * CH + 16 * mt + 4 * q4) = acc;
+        else
+          store4<OP>(reinterpret_cast<OP*>(a.wsUt) + blk * WB::UT + (16 * nt + r16) * CH + 16 * mt + 4 * q4, acc[0],
+                     acc[1], acc[2], acc[3]);
+      }
+    }
+    item = nitem;
+    ci = nci;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // sequential state pass (forward outputs, or the per-chunk states for backward)
 // ---------------------------------------------------------------------------
 // One work-group walks the chunks of one (sequence, head, value slice of DVS
@@ -624,11 +960,31 @@ static hipError_t launch_state(const Args& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (the persistent prep runs one work-group on each).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <typename E, int DK, int DV, bool BWD>
 static hipError_t launch_prep(const Args& a, hipStream_t st) {
   if (a.max_chunks == 0 || a.H == 0) return hipSuccess;
-  KDA_TIMED(BWD ? "kda_prep_bwd" : "kda_prep", st,
-            hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
+  if constexpr (sizeof(E) == 2) {
+    const long long items = (long long)a.max_chunks * a.H;
+    const int grid = (int)std::min<long long>(items, device_cus());
+    KDA_TIMED(BWD ? "kda_prep_bwd" : "kda_prep", st,
+              hipLaunchKernelGGL((kda_prep8<DK, DV, BWD>), dim3(grid), dim3(512), 0, st, a));
+  } else {
+    KDA_TIMED(BWD ? "kda_prep_bwd" : "kda_prep", st,
+              hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
+  }
   return hipGetLastError();
 }
 
