@@ -54,16 +54,33 @@ def _counter_rows(path):
     return out
 
 
-def _short_name(name):
-    """rocprofv3 kernel name -> the timing name the library uses."""
-    for key, short in (("kda_prep", None), ("kda_state_rev", "kda_state_bwd_revpass"), ("kda_bwd_chunk", "kda_bwd_chunk"),
-                       ("kda_chunk_map", "kda_chunk_map"), ("kda_state", None)):
-        if key in name:
-            if short:
-                return short
-            if key == "kda_prep":
-                return "kda_prep_bwd" if ("Lb1E" in name or ", true>" in name) else "kda_prep"
-            return "kda_state_fwd" if ("Lb1E" in name or ", true>" in name) else "kda_state_bwd_fwdpass"
+def _bools(name):
+    """Trailing bool template arguments of a kernel name (mangled 'Lb1E' or demangled 'true')."""
+    import re
+    m = re.findall(r"Lb([01])E", name)
+    if m:
+        return [x == "1" for x in m]
+    return [x == "true" for x in re.findall(r"\b(true|false)\b", name)]
+
+
+def _short_name(name, train=True):
+    """rocprofv3 kernel name -> the timing name the library uses (train: the forward saves for
+    the backward, so the prep that keeps T etc. is the forward's)."""
+    if "kda_state_rev" in name:
+        return "kda_state_bwd_revpass"
+    if "kda_bwd_chunk" in name:
+        return "kda_bwd_chunk"
+    if "kda_chunk_map" in name:
+        return "kda_chunk_map"
+    if "kda_prep" in name:
+        bwd = (_bools(name) or [False])[-1]
+        return ("kda_prep_save" if train else "kda_prep_bwd") if bwd else "kda_prep"
+    if "kda_state" in name:
+        b = _bools(name)
+        out, save = (b[-2], b[-1]) if len(b) >= 2 else (True, False)
+        if out:
+            return "kda_state_fwd_save" if save else "kda_state_fwd"
+        return "kda_state_bwd_fwdpass"
     return None
 
 
@@ -148,6 +165,8 @@ def kernel_alg_bytes(name, w, tokens, n_seqs, eout=4):
     table = {
         "kda_prep": th * (ein * (3 * dk + dv) + ein),                     # reads q, k, log_alpha, v, beta
         "kda_prep_bwd": th * (ein * (3 * dk + dv) + ein),                 # same reads, backward recompute
+        "kda_prep_save": th * (ein * (3 * dk + dv) + ein),                # forward prep keeping the backward's data
+        "kda_state_fwd_save": th * eout * dv + 2 * state,                 # as kda_state_fwd
         "kda_state_fwd": th * eout * dv + 2 * state,                      # writes o; reads S0, writes S_T
         "kda_state_bwd_fwdpass": state,                                   # reads S0
         "kda_state_bwd_revpass": th * ein * dv + 2 * state,               # reads dO, dS_T; writes dS0
@@ -164,6 +183,8 @@ def kernel_alg_flops(name, w, tokens):
     per = {
         "kda_prep": 2 * C * dk + C * dk + C * dv,                          # Gram Akk, Aqk; W, U~
         "kda_prep_bwd": 2 * C * dk + C * dk + C * dv,
+        "kda_prep_save": 2 * C * dk + C * dk + C * dv,
+        "kda_state_fwd_save": 3 * 2 * dk * dv + C * dv,
         "kda_state_fwd": 3 * 2 * dk * dv + C * dv,                         # W S, Qt S, Kh^T U; Aqk U
         "kda_state_bwd_fwdpass": 2 * 2 * dk * dv,                          # W S, Kh^T U
         "kda_state_bwd_revpass": 3 * 2 * dk * dv + C * dv,                 # Kh dS', Qt^T dO, W^T dU; Aqk^T dO
@@ -208,6 +229,9 @@ def main() -> int:
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="bf16 outputs/gradients instead of fp32")
+    ap.add_argument("--recompute", action="store_true",
+                    help="self-contained backward (recomputes the forward) instead of the training step in which "
+                         "the forward keeps the backward's intermediates")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -281,12 +305,14 @@ def main() -> int:
                                                                             t["beta"]))
         dinit = torch.empty_like(fin)
 
+    train = not fwd_only and not args.recompute
+
     def step():
         kda.fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], init_state=init, cu_seqlens=cu, out=out,
-                final_state=fin, workspace=ws, out_dtype=odt)
+                final_state=fin, workspace=ws, out_dtype=odt, save_for_backward=train)
         if not fwd_only:
             kda.bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], d_out, init_state=init, d_final_state=d_fin,
-                    cu_seqlens=cu, workspace=ws, out_dtype=odt, grads=grads, d_init=dinit)
+                    cu_seqlens=cu, workspace=ws, out_dtype=odt, grads=grads, d_init=dinit, use_saved=train)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -355,7 +381,9 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": tokens, "sequences": n_seqs, "H": w.H, "dk": w.dk, "dv": w.dv,
-                   "out_dtype": "bf16" if args.out_bf16 else "f32", "pass": "fwd" if fwd_only else "fwd+bwd"},
+                   "out_dtype": "bf16" if args.out_bf16 else "f32", "pass": "fwd" if fwd_only else "fwd+bwd",
+                   "backward": None if fwd_only else ("recomputes the forward" if args.recompute
+                                                      else "uses the forward's saved intermediates")},
         "roofline": roof,
         "step_roofline": step_roof,
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in kt.items()},

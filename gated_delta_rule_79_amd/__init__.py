@@ -26,12 +26,13 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 _lib = None
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_FLAG_SAVE_FOR_BACKWARD, KDA_FLAG_USE_SAVED = 1, 2   # kda_desc.flags bits (include/kda.h)
 
 
 class kda_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("flags", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -107,9 +108,9 @@ def _dtype_code(dt) -> int:
     raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
 
 
-def make_desc(B, T, H, dk, dv, dtype_code, num_seqs=0, scale=None, out_code=KDA_F32) -> kda_desc:
+def make_desc(B, T, H, dk, dv, dtype_code, num_seqs=0, scale=None, out_code=KDA_F32, flags=0) -> kda_desc:
     return kda_desc(int(B), int(T), int(H), int(dk), int(dv), int(num_seqs), int(dtype_code), int(out_code),
-                    float(scale) if scale else 0.0)
+                    float(scale) if scale else 0.0, int(flags))
 
 
 def workspace_bytes(B, T, H, dk, dv, dtype, num_seqs=0, backward=False) -> int:
@@ -170,13 +171,19 @@ def _stream(dev):
 
 
 def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, output_final_state=True,
-        out=None, final_state=None, workspace=None, out_dtype=None):
+        out=None, final_state=None, workspace=None, out_dtype=None, save_for_backward=False):
     """Forward pass; returns (o [B,T,H,dv] in out_dtype (default float32), final_state float32
-    [N,H,dk,dv] or None).  out_dtype=torch.bfloat16 is allowed for bf16 inputs."""
+    [N,H,dk,dv] or None).  out_dtype=torch.bfloat16 is allowed for bf16 inputs.
+    save_for_backward=True leaves the backward's intermediates in `workspace` (which must then be
+    given, sized by workspace_bytes(..., backward=True)) for a following bwd(..., use_saved=True)."""
     import torch
     lib = load_library()
     desc, (B, T, H, dk, dv, N), dev, dt = _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale,
                                                    out_dtype)
+    if save_for_backward:
+        if workspace is None:
+            raise ValueError("save_for_backward needs the caller's workspace (it is reused by bwd)")
+        desc.flags = KDA_FLAG_SAVE_FOR_BACKWARD
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
     else:
@@ -185,8 +192,8 @@ def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, 
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _check("final_state", final_state, torch.float32, (N, H, dk, dv), dev)
-    need = lib.kda_workspace_bytes(ctypes.byref(desc), 0)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    need = lib.kda_workspace_bytes(ctypes.byref(desc), 1 if save_for_backward else 0)
+    if workspace is None or (not save_for_backward and workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = lib.kda_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state),
                      _ptr(out), _ptr(final_state), _ptr(cu_seqlens), _ptr(workspace),
@@ -197,13 +204,18 @@ def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, 
 
 
 def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu_seqlens=None, scale=None,
-        need_d_init=True, workspace=None, out_dtype=None, grads=None, d_init=None):
+        need_d_init=True, workspace=None, out_dtype=None, grads=None, d_init=None, use_saved=False):
     """Backward pass; returns (dq, dk, dv, dlog_alpha, dbeta in out_dtype (default float32),
-    d_init_state float32 or None)."""
+    d_init_state float32 or None).  use_saved=True: `workspace` holds what fwd(...,
+    save_for_backward=True) left there for the same inputs; the forward is not recomputed."""
     import torch
     lib = load_library()
     desc, (B, T, H, dk, dv, N), dev, odt = _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale,
                                                     out_dtype)
+    if use_saved:
+        if workspace is None:
+            raise ValueError("use_saved needs the workspace the forward wrote")
+        desc.flags = KDA_FLAG_USE_SAVED
     _check("d_out", d_out, q.dtype, (B, T, H, dv), dev)
     if d_final_state is not None:
         _check("d_final_state", d_final_state, torch.float32, (N, H, dk, dv), dev)
@@ -218,7 +230,7 @@ def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu
     elif dinit is not None:
         _check("d_init", dinit, torch.float32, (N, H, dk, dv), dev)
     need = lib.kda_workspace_bytes(ctypes.byref(desc), 1)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    if workspace is None or (not use_saved and workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = lib.kda_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state),
                      _ptr(cu_seqlens), _ptr(d_out), _ptr(d_final_state), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dla),

@@ -129,10 +129,12 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
 
 hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {
   const bool bf = d->dtype == KDA_BF16, obf = d->out_dtype == KDA_BF16;
+  const bool save = (d->flags & KDA_FLAG_SAVE_FOR_BACKWARD) != 0;
 #define KDA_CASE(DK, DV)                                                                        \
   if (d->dk == DK && d->dv == DV)                                                               \
-    return bf ? (obf ? kda::launch_fwd<bf16, bf16, DK, DV>(a, st) : kda::launch_fwd<bf16, float, DK, DV>(a, st)) \
-              : kda::launch_fwd<float, float, DK, DV>(a, st);
+    return bf ? (obf ? kda::launch_fwd<bf16, bf16, DK, DV>(a, st, save)                         \
+                     : kda::launch_fwd<bf16, float, DK, DV>(a, st, save))                       \
+              : kda::launch_fwd<float, float, DK, DV>(a, st, save);
   KDA_CASE(64, 64)
   KDA_CASE(64, 128)
   KDA_CASE(128, 64)
@@ -143,18 +145,20 @@ hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {
 
 hipError_t run_bwd(const kda_desc* d, const Args& a, hipStream_t st) {
   const bool bf = d->dtype == KDA_BF16, obf = d->out_dtype == KDA_BF16;
+  const bool saved = (d->flags & KDA_FLAG_USE_SAVED) != 0;
   if (bf) {
 #define KDA_CASE(DK, DV)                                                                        \
     if (d->dk == DK && d->dv == DV)                                                             \
-      return obf ? kda::launch_bwd<bf16, bf16, DK, DV>(a, st) : kda::launch_bwd<bf16, float, DK, DV>(a, st);
+      return obf ? kda::launch_bwd<bf16, bf16, DK, DV>(a, st, saved)                            \
+                 : kda::launch_bwd<bf16, float, DK, DV>(a, st, saved);
     KDA_CASE(64, 64)
     KDA_CASE(64, 128)
     KDA_CASE(128, 64)
     KDA_CASE(128, 128)
 #undef KDA_CASE
   } else {  // fp32 backward is built for dk = 64 (the host check rejects dk = 128)
-    if (d->dk == 64 && d->dv == 64) return kda::launch_bwd<float, float, 64, 64>(a, st);
-    if (d->dk == 64 && d->dv == 128) return kda::launch_bwd<float, float, 64, 128>(a, st);
+    if (d->dk == 64 && d->dv == 64) return kda::launch_bwd<float, float, 64, 64>(a, st, saved);
+    if (d->dk == 64 && d->dv == 128) return kda::launch_bwd<float, float, 64, 128>(a, st, saved);
   }
   return hipErrorInvalidValue;
 }
@@ -313,7 +317,10 @@ kda_status kda_fwd(const kda_desc* d, const void* q, const void* k, const void* 
   if (beta && ((uintptr_t)beta % (d->dtype == KDA_BF16 ? 2 : 4))) return KDA_ERROR_MISALIGNED;
   if (out && ((uintptr_t)out % (d->out_dtype == KDA_BF16 ? 2 : 4))) return KDA_ERROR_MISALIGNED;
   if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_MISALIGNED;
-  const Plan p = make_plan(d, false, N, mc);
+  if (d->flags & ~KDA_FLAG_SAVE_FOR_BACKWARD) return KDA_ERROR_INVALID_VALUE;
+  const bool save = (d->flags & KDA_FLAG_SAVE_FOR_BACKWARD) != 0;
+  if (save && d->dtype == KDA_F32 && d->dk == 128) return KDA_ERROR_NOT_SUPPORTED;  // no fp32 backward at dk = 128
+  const Plan p = make_plan(d, save, N, mc);
   if (!workspace || workspace_bytes < p.total) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cu_seqlens && env_int("KDA_DEBUG", 0) && !cu_ok(cu_seqlens, N, d->T, st)) return KDA_ERROR_INVALID_VALUE;
@@ -348,6 +355,7 @@ kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* 
   if ((beta && (uintptr_t)beta % es) || (dbeta && (uintptr_t)dbeta % eo)) return KDA_ERROR_MISALIGNED;
   if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_MISALIGNED;
   if (d->dtype == KDA_F32 && d->dk == 128) return KDA_ERROR_NOT_SUPPORTED;  // fp32 backward: dk = 64 only
+  if (d->flags & ~KDA_FLAG_USE_SAVED) return KDA_ERROR_INVALID_VALUE;
   const Plan p = make_plan(d, true, N, mc);
   if (!workspace || workspace_bytes < p.total) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -740,10 +740,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// `saved`: the workspace already holds the forward intermediates (kda_fwd with
+// KDA_FLAG_SAVE_FOR_BACKWARD on the same inputs), so the front half is skipped.
 template <typename E, typename O, int DK, int DV>
-hipError_t launch_bwd(const Args& a, hipStream_t st) {
-  hipError_t e = launch_bwd_front<E, DK, DV>(a, st);
-  if (e != hipSuccess) return e;
+hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved) {
+  hipError_t e = hipSuccess;
+  if (!saved) {
+    e = launch_bwd_front<E, DK, DV>(a, st);
+    if (e != hipSuccess) return e;
+  }
   constexpr int DVS = 16, NSL = DV / DVS;
   const int units = a.N * a.H;
   const int grid = (units + 7) / 8 * 8 * NSL;
@@ -760,7 +765,7 @@ hipError_t launch_bwd(const Args& a, hipStream_t st) {
   return hipSuccess;
 }
 
-#define KDA_INST(E, O, DK, DV) template hipError_t launch_bwd<E, O, DK, DV>(const Args&, hipStream_t);
+#define KDA_INST(E, O, DK, DV) template hipError_t launch_bwd<E, O, DK, DV>(const Args&, hipStream_t, bool);
 KDA_INST(bf16, float, 64, 64)
 KDA_INST(bf16, float, 64, 128)
 KDA_INST(bf16, float, 128, 64)

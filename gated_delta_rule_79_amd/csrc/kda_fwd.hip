@@ -725,7 +725,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
 // updates its 16x16 tiles of S.  S stays in fp32 registers; each chunk it is
 // copied to LDS in the operand type for the products that read it.  The next
 // chunk's matrices are loaded into registers while the current one computes.
-template <typename E, int DK, int DV, int DVS, bool OUT>
+template <typename E, int DK, int DV, int DVS, bool OUT, bool SAVE>
 struct StateLds {
   using OP = typename OpOf<E>::T;
   static constexpr int P = PADE<OP>;
@@ -735,7 +735,7 @@ struct StateLds {
   static constexpr size_t QT = W + (size_t)CH * LDK * sizeof(OP);                 // OP [CH][LDK]  (OUT)
   static constexpr size_t KHT = QT + (OUT ? (size_t)CH * LDK * sizeof(OP) : 0);   // OP [DK][LDT]
   static constexpr size_t AQK = KHT + (size_t)DK * LDT * sizeof(OP);              // OP [CH][LDT]  (OUT)
-  using UTT = typename std::conditional<OUT, OP, float>::type;                   // U~ element type
+  using UTT = typename std::conditional<SAVE, float, OP>::type;                  // U~ element type
   static constexpr size_t UT = AQK + (OUT ? (size_t)CH * LDT * sizeof(OP) : 0);   // UTT [DVS][CH]
   static constexpr size_t GAM = UT + (size_t)DVS * CH * sizeof(UTT);              // float [DK]
   static constexpr size_t ST = GAM + (size_t)DK * 4;                              // OP [DVS][LDK]  S^T
@@ -744,9 +744,9 @@ struct StateLds {
   static_assert(BYTES <= 163840, "state LDS");
 };
 
-template <typename E, typename O, int DK, int DV, int DVS, bool OUT>
+template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void kda_state(const Args a) {
-  using L = StateLds<E, DK, DV, DVS, OUT>;
+  using L = StateLds<E, DK, DV, DVS, OUT, SAVE>;
   using OP = typename L::OP;
   using WB = WsBlock<E, DK, DV>;
   constexpr int NT = 512, NSL = DV / DVS;
@@ -786,7 +786,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const OP* gQt = reinterpret_cast<const OP*>(a.wsQt);
   const OP* gAqk = reinterpret_cast<const OP*>(a.wsAqk);
   const OP* gKhT = reinterpret_cast<const OP*>(a.wsKhT);
-  const UTT* gUt = OUT ? reinterpret_cast<const UTT*>(a.wsUt) : reinterpret_cast<const UTT*>(a.wsUtF);
+  const UTT* gUt = SAVE ? reinterpret_cast<const UTT*>(a.wsUtF) : reinterpret_cast<const UTT*>(a.wsUt);
   const float* gGam = a.wsGam;
   OP* gS = reinterpret_cast<OP*>(a.wsS);
   float* gU = a.wsU;
@@ -854,7 +854,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       const int t = w + 8 * i, mt = t % MTS, nt = t / MTS;
       if (t < NST) {
         store4<OP>(sST + (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4, S[i][0], S[i][1], S[i][2], S[i][3]);
-        if constexpr (!OUT) {
+        if constexpr (SAVE) {
           // backward needs the state entering every chunk: OP [DV][DK] per chunk-head
           OP* dst = gS + blk_of(n) * WB::S + (size_t)(n0 + 16 * nt + r16) * DK + 16 * mt + 4 * q4;
           store4<OP>(dst, S[i][0], S[i][1], S[i][2], S[i][3]);
@@ -875,7 +875,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         load4<UTT>(sUt + (16 * nt + r16) * CH + 16 * w + 4 * q4, ut);
         store4<OP>(sUL + (16 * nt + r16) * L::LDT + 16 * w + 4 * q4, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2],
                    ut[3] - x[3]);
-        if constexpr (!OUT) {
+        if constexpr (SAVE) {
           // and U^T in fp32
           float* dst = gU + blk_of(n) * WB::U + (size_t)(n0 + 16 * nt + r16) * CH + 16 * w + 4 * q4;
           *reinterpret_cast<f32x4*>(dst) = f32x4{ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]};
@@ -948,15 +948,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
-template <typename E, typename O, int DK, int DV, int DVS, bool OUT>
+template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE>
 static hipError_t launch_state(const Args& a, hipStream_t st) {
   constexpr int NSL = DV / DVS;
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
   const int grid = groups * 8 * NSL;
   if (grid == 0) return hipSuccess;
-  KDA_TIMED(OUT ? "kda_state_fwd" : "kda_state_bwd_fwdpass", st,
-            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT>), dim3(grid), dim3(512), 0, st, a));
+  KDA_TIMED(OUT ? (SAVE ? "kda_state_fwd_save" : "kda_state_fwd") : "kda_state_bwd_fwdpass", st,
+            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT, SAVE>), dim3(grid), dim3(512), 0, st, a));
   return hipGetLastError();
 }
 
@@ -973,28 +973,39 @@ static int device_cus() {
   return cached[dev];
 }
 
+// BWD: also keep what the backward pass needs (T, the un-beta Gram, fp32 Kh and U~).
 template <typename E, int DK, int DV, bool BWD>
-static hipError_t launch_prep(const Args& a, hipStream_t st) {
+static hipError_t launch_prep(const Args& a, hipStream_t st, const char* name) {
   if (a.max_chunks == 0 || a.H == 0) return hipSuccess;
   if constexpr (sizeof(E) == 2) {
     const long long items = (long long)a.max_chunks * a.H;
     const int grid = (int)std::min<long long>(items, device_cus());
-    KDA_TIMED(BWD ? "kda_prep_bwd" : "kda_prep", st,
-              hipLaunchKernelGGL((kda_prep8<DK, DV, BWD>), dim3(grid), dim3(512), 0, st, a));
+    KDA_TIMED(name, st, hipLaunchKernelGGL((kda_prep8<DK, DV, BWD>), dim3(grid), dim3(512), 0, st, a));
   } else {
-    KDA_TIMED(BWD ? "kda_prep_bwd" : "kda_prep", st,
-              hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
+    KDA_TIMED(name, st, hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
   }
   return hipGetLastError();
 }
 
+// Forward pass; with `save` it also leaves in the workspace everything the
+// backward pass would otherwise recompute (T, G, fp32 Kh and U~, S entering
+// every chunk, U), so a following kda_bwd on the same workspace skips that work.
 template <typename E, typename O, int DK, int DV>
-hipError_t launch_fwd(const Args& a, hipStream_t st) {
+hipError_t launch_fwd(const Args& a, hipStream_t st, bool save) {
   hipError_t e = launch_chunk_map(a, st);
   if (e != hipSuccess) return e;
-  e = launch_prep<E, DK, DV, false>(a, st);
+  if (save) {
+    if constexpr (sizeof(E) == 4 && DK == 128) {
+      return hipErrorInvalidValue;   // no fp32 backward at dk = 128, so nothing to save for
+    } else {
+      e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_save");
+      if (e != hipSuccess) return e;
+      return launch_state<E, O, DK, DV, 16, true, true>(a, st);
+    }
+  }
+  e = launch_prep<E, DK, DV, false>(a, st, "kda_prep");
   if (e != hipSuccess) return e;
-  return launch_state<E, O, DK, DV, 16, true>(a, st);
+  return launch_state<E, O, DK, DV, 16, true, false>(a, st);
 }
 
 // front half of the backward pass: chunk map, chunk-local prep (also keeping
@@ -1003,13 +1014,13 @@ template <typename E, int DK, int DV>
 hipError_t launch_bwd_front(const Args& a, hipStream_t st) {
   hipError_t e = launch_chunk_map(a, st);
   if (e != hipSuccess) return e;
-  e = launch_prep<E, DK, DV, true>(a, st);
+  e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_bwd");
   if (e != hipSuccess) return e;
-  return launch_state<E, float, DK, DV, 16, false>(a, st);
+  return launch_state<E, float, DK, DV, 16, false, true>(a, st);
 }
 
 #define KDA_INST(E, DK, DV)                                                                   \
-  template hipError_t launch_fwd<E, float, DK, DV>(const Args&, hipStream_t);                 \
+  template hipError_t launch_fwd<E, float, DK, DV>(const Args&, hipStream_t, bool);           \
   template hipError_t launch_bwd_front<E, DK, DV>(const Args&, hipStream_t);
 KDA_INST(bf16, 64, 64)
 KDA_INST(bf16, 64, 128)
@@ -1020,7 +1031,7 @@ KDA_INST(float, 64, 128)
 KDA_INST(float, 128, 64)
 KDA_INST(float, 128, 128)
 #undef KDA_INST
-#define KDA_INST_BF16OUT(DK, DV) template hipError_t launch_fwd<bf16, bf16, DK, DV>(const Args&, hipStream_t);
+#define KDA_INST_BF16OUT(DK, DV) template hipError_t launch_fwd<bf16, bf16, DK, DV>(const Args&, hipStream_t, bool);
 KDA_INST_BF16OUT(64, 64)
 KDA_INST_BF16OUT(64, 128)
 KDA_INST_BF16OUT(128, 64)

@@ -55,8 +55,8 @@ void timing_end(hipStream_t st);
   } while (0)
 
 hipError_t launch_chunk_map(const Args& a, hipStream_t st);
-template <typename E, typename O, int DK, int DV> hipError_t launch_fwd(const Args& a, hipStream_t st);
+template <typename E, typename O, int DK, int DV> hipError_t launch_fwd(const Args& a, hipStream_t st, bool save);
 template <typename E, int DK, int DV> hipError_t launch_bwd_front(const Args& a, hipStream_t st);
-template <typename E, typename O, int DK, int DV> hipError_t launch_bwd(const Args& a, hipStream_t st);
+template <typename E, typename O, int DK, int DV> hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved);
 
 }  // namespace kda

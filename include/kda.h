@@ -82,7 +82,20 @@ typedef struct {
     kda_dtype out_dtype;/* storage dtype of out, dq, dk, dv, dlog_alpha, dbeta; KDA_BF16 is
                            allowed only when dtype is KDA_BF16                               */
     float scale;        /* output scale; 0 means dk^-1/2                                    */
+    int32_t flags;      /* KDA_FLAG_* bits below; 0 for a self-contained call               */
 } kda_desc;
+
+/* kda_fwd: also leave in the workspace everything kda_bwd would recompute
+ * (training step).  The workspace must then have kda_workspace_bytes(desc, 1)
+ * bytes.  Not available where kda_bwd is not (fp32 inputs with dk = 128). */
+#define KDA_FLAG_SAVE_FOR_BACKWARD 1
+/* kda_bwd: the workspace holds what a kda_fwd call with KDA_FLAG_SAVE_FOR_BACKWARD
+ * left there, for the same descriptor, inputs (q, k, v, log_alpha, beta,
+ * init_state, cu_seqlens) and workspace pointer, with nothing written to the
+ * workspace in between; the recomputation of the forward is skipped.  Results
+ * are bit-identical to a kda_bwd call without the flag.  Violating the
+ * precondition gives wrong gradients; it is not detected. */
+#define KDA_FLAG_USE_SAVED 2
 
 /* Bytes of device workspace kda_fwd (backward = 0) or kda_bwd (backward != 0)
  * needs for this problem; 0 if the descriptor is invalid. */
@@ -94,8 +107,9 @@ kda_status kda_fwd(const kda_desc *desc, const void *q, const void *k, const voi
                    void *out, float *final_state, const int32_t *cu_seqlens,
                    void *workspace, size_t workspace_bytes, void *stream);
 
-/* Backward pass: recomputes the forward internally (no saved activations).
- * d_final_state may be NULL (zero); d_init_state may be NULL (not written). */
+/* Backward pass: recomputes the forward internally, unless desc->flags has
+ * KDA_FLAG_USE_SAVED (see above).  d_final_state may be NULL (zero);
+ * d_init_state may be NULL (not written). */
 kda_status kda_bwd(const kda_desc *desc, const void *q, const void *k, const void *v,
                    const void *log_alpha, const void *beta, const float *init_state,
                    const int32_t *cu_seqlens, const void *d_out, const float *d_final_state,

@@ -135,3 +135,22 @@ def test_timing_is_empty_without_launches(lib):
     lib.kda_timing_enable(1)
     assert lib.kda_timing_read(8, None, None, None) == 0
     lib.kda_timing_enable(0)
+
+
+def test_flag_validation(lib):
+    """Unknown flag bits, a flag on the wrong call, and saving where no backward exists are rejected
+    before any launch."""
+    assert _fwd(lib, _desc(flags=kda.KDA_FLAG_USE_SAVED)) == S_INVALID
+    assert _fwd(lib, _desc(flags=4)) == S_INVALID
+    assert _bwd(lib, _desc(flags=kda.KDA_FLAG_SAVE_FOR_BACKWARD)) == S_INVALID
+    assert _bwd(lib, _desc(flags=8)) == S_INVALID
+    assert _fwd(lib, _desc(dtype=0, dk=128, flags=kda.KDA_FLAG_SAVE_FOR_BACKWARD)) == S_UNSUP
+
+
+def test_save_for_backward_needs_the_backward_workspace(lib):
+    fwd_need = lib.kda_workspace_bytes(ctypes.byref(_desc()), 0)
+    bwd_need = lib.kda_workspace_bytes(ctypes.byref(_desc()), 1)
+    assert bwd_need > fwd_need
+    d = _desc(flags=kda.KDA_FLAG_SAVE_FOR_BACKWARD)
+    assert _fwd(lib, d, wsb=fwd_need) == S_WS
+    assert _fwd(lib, d, wsb=bwd_need - 1) == S_WS

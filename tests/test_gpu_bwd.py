@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import kda_inputs as ki
-from kda_testutil import TOL, gpu_bwd, gpu_fwd, np_of, oracle_bwd, rel_err, to_gpu
+from kda_testutil import TOL, gpu_bwd, gpu_fwd, np_of, oracle_bwd, oracle_fwd, rel_err, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +139,30 @@ def test_fp32_repeated_after_other_work():
         errs = {n: rel_err(np_of(a)[0] if n != "d_init" else np_of(a), b) for n, a, b in zip(NAMES, grads, ref)}
         bad = {k: v for k, v in errs.items() if not v <= TOL["f32"]}
         assert not bad, f"call {it}: {bad}"
+
+
+@pytest.mark.parametrize("dtype,lengths,H,dk,dv", [("bf16", (300, 1, 129), 2, 128, 128), ("f32", (100, 64), 2, 64, 64),
+                                                   ("bf16", (70,), 3, 64, 128)],
+                         ids=["bf16-128x128", "f32-64x64", "bf16-64x128"])
+def test_saved_forward_matches_recompute(dtype, lengths, H, dk, dv):
+    """fwd(save_for_backward) + bwd(use_saved) gives the recomputing bwd's gradients bit for bit,
+    and an output within the parity bound."""
+    import torch
+    import gated_delta_rule_79_amd as kda
+    w = ki.small(dtype=dtype, lengths=lengths, H=H, dk=dk, dv=dv)
+    inp = ki.make_inputs(w, with_grads=True)
+    g = to_gpu(inp, dtype)
+    ref = gpu_bwd(g)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ws = torch.empty(kda.workspace_bytes(1, g["q"].shape[1], H, dk, dv, dt, num_seqs=len(lengths), backward=True),
+                     dtype=torch.uint8, device="cuda")
+    o, fin = kda.fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], init_state=g["init_state"],
+                     cu_seqlens=g["cu_seqlens"], workspace=ws, save_for_backward=True)
+    got = kda.bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["d_out"], init_state=g["init_state"],
+                  d_final_state=g["d_final_state"], cu_seqlens=g["cu_seqlens"], workspace=ws, use_saved=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, got, ref):
+        assert torch.equal(a, b), name
+    o_ref, f_ref = oracle_fwd(inp)
+    assert rel_err(np_of(o)[0], o_ref) <= TOL[dtype]
+    assert rel_err(np_of(fin), f_ref) <= TOL[dtype]
