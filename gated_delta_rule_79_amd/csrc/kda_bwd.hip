@@ -165,8 +165,9 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
       if (t < NST) {
         const int off = (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4;
         store4_split<OP>(sDSh + off, sDSl + off, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
-        float* dst = gdS + blk_of(n) * WB::DS + (size_t)(n0 + 16 * nt + r16) * DK + 16 * mt + 4 * q4;
-        *reinterpret_cast<f32x4*>(dst) = dS[i];
+        float* dst = gdS + blk_of(n) * WB::DS + (size_t)(16 * mt + 4 * q4) * DV + n0 + 16 * nt + r16;  // [DK][DV]
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = dS[i][ii];
       }
     }
     __syncthreads();
@@ -187,8 +188,9 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
         const f32x4 du = scale * x1 + x2;
         const int off = (16 * nt + r16) * L::LDT + 16 * w + 4 * q4;
         store4_split<OP>(sDUh + off, sDUl + off, du[0], du[1], du[2], du[3]);
-        float* dst = gdU + blk_of(n) * WB::DU + (size_t)(n0 + 16 * nt + r16) * CH + 16 * w + 4 * q4;
-        *reinterpret_cast<f32x4*>(dst) = du;
+        float* dst = gdU + blk_of(n) * WB::DU + (size_t)(16 * w + 4 * q4) * DV + n0 + 16 * nt + r16;  // [CH][DV]
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = du[ii];
       }
     }
     // scale Qt^T dO for this wave's state tiles (independent of dU)
@@ -277,20 +279,22 @@ struct BwdLds {
   static constexpr int QC = 32;                      // value columns per quarter
   static constexpr bool SPLIT = sizeof(OP) == 2;     // lo halves exist only for 2-byte operands
   static constexpr size_t OPB = sizeof(OP);
-  // phase A (leading dimensions in elements)
-  static constexpr int LSK = DK + PO;   // OP [QC][DK]  S^T, dS'^T quarters
-  static constexpr int LST = CH + PO;   // OP [QC][CH]  U^T, dU^T quarters
-  static constexpr int LSQ = QC + PO;   // OP [CH][QC]  dO, V quarters
+  // phase A: quarters with the value column contiguous, so every MFMA operand
+  // (contraction over the value dimension) is one 16-byte row read
+  static constexpr int LSV = QC + PO;   // OP [DK][LSV] S, dS';  [CH][LSV] U, dU, dO, V
+  static constexpr int LST = CH + PO;   // OP [QC][LST] dU^T (token contiguous, for T^T dU)
   static constexpr size_t A_S = 0;
-  static constexpr size_t A_DSH = A_S + (size_t)QC * LSK * OPB;
-  static constexpr size_t A_DSL = A_DSH + (size_t)QC * LSK * OPB;
-  static constexpr size_t A_UH = A_DSL + (SPLIT ? (size_t)QC * LSK * OPB : 0);
-  static constexpr size_t A_UL = A_UH + (size_t)QC * LST * OPB;
-  static constexpr size_t A_DUH = A_UL + (SPLIT ? (size_t)QC * LST * OPB : 0);
-  static constexpr size_t A_DUL = A_DUH + (size_t)QC * LST * OPB;
-  static constexpr size_t A_DO = A_DUL + (SPLIT ? (size_t)QC * LST * OPB : 0);
-  static constexpr size_t A_V = A_DO + (size_t)CH * LSQ * OPB;
-  static constexpr size_t A_END = A_V + (size_t)CH * LSQ * OPB;
+  static constexpr size_t A_DSH = A_S + (size_t)DK * LSV * OPB;
+  static constexpr size_t A_DSL = A_DSH + (size_t)DK * LSV * OPB;
+  static constexpr size_t A_UH = A_DSL + (SPLIT ? (size_t)DK * LSV * OPB : 0);
+  static constexpr size_t A_UL = A_UH + (size_t)CH * LSV * OPB;
+  static constexpr size_t A_DUH = A_UL + (SPLIT ? (size_t)CH * LSV * OPB : 0);
+  static constexpr size_t A_DUL = A_DUH + (size_t)CH * LSV * OPB;
+  static constexpr size_t A_DUTH = A_DUL + (SPLIT ? (size_t)CH * LSV * OPB : 0);
+  static constexpr size_t A_DUTL = A_DUTH + (size_t)QC * LST * OPB;
+  static constexpr size_t A_DO = A_DUTL + (SPLIT ? (size_t)QC * LST * OPB : 0);
+  static constexpr size_t A_V = A_DO + (size_t)CH * LSV * OPB;
+  static constexpr size_t A_END = A_V + (size_t)CH * LSV * OPB;
   // phase B (shares the first region with phase A)
   static constexpr int LDG = DK + 4;    // float [CH][LDG]  g, later dg
   static constexpr int LDK = DK + PE;   // E     [CH][LDK]  k, q
@@ -303,7 +307,7 @@ struct BwdLds {
   static constexpr size_t B_END = Q + (size_t)CH * LDK * sizeof(E);
   static constexpr size_t UNION = A_END > B_END ? A_END : B_END;
   // both phases
-  static constexpr size_t T = UNION;                                  // OP    [CH][LDT]
+  static constexpr size_t T = UNION;                                  // OP    [CH][LDT]  T^T
   static constexpr size_t A1 = T + (size_t)CH * LDT * OPB;            // float [CH][LDA]  scale tril(dO U^T)
   static constexpr size_t A2 = A1 + (size_t)CH * LDA * 4;             // float [CH][LDA]  dT, then dG
   static constexpr size_t DW = A2 + (size_t)CH * LDA * 4;             // OP    [CH][LDO]  dW (Y after it is dead)
@@ -316,6 +320,7 @@ struct BwdLds {
   static constexpr size_t DBP = BV + 2 * CH * 4;                      // float [2][CH] dbeta halves
   static constexpr size_t BYTES = DBP + 2 * CH * 4;
   static constexpr size_t Y = DW;                                     // OP [CH][LDT]
+  static_assert(LDT <= LDO, "Y fits in the dW region");
   static_assert(BYTES <= 163840, "backward chunk kernel LDS");
   static_assert(A_END % 16 == 0 && B_END % 16 == 0, "LDS regions stay 16-byte aligned");
 };
@@ -345,12 +350,14 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   OP* sUl = reinterpret_cast<OP*>(smem + L::A_UL);
   OP* sDUh = reinterpret_cast<OP*>(smem + L::A_DUH);
   OP* sDUl = reinterpret_cast<OP*>(smem + L::A_DUL);
+  OP* sDUTh = reinterpret_cast<OP*>(smem + L::A_DUTH);
+  OP* sDUTl = reinterpret_cast<OP*>(smem + L::A_DUTL);
   OP* sDO = reinterpret_cast<OP*>(smem + L::A_DO);
   OP* sV = reinterpret_cast<OP*>(smem + L::A_V);
   float* sG = reinterpret_cast<float*>(smem + L::G);
   E* sK = reinterpret_cast<E*>(smem + L::K);
   E* sQ = reinterpret_cast<E*>(smem + L::Q);
-  OP* sT = reinterpret_cast<OP*>(smem + L::T);
+  OP* sTT = reinterpret_cast<OP*>(smem + L::T);   // T^T: sTT[i][r] = T[r][i]
   float* sA1 = reinterpret_cast<float*>(smem + L::A1);
   float* sA2 = reinterpret_cast<float*>(smem + L::A2);
   OP* sDW = reinterpret_cast<OP*>(smem + L::DW);
@@ -380,28 +387,34 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   // phase B's inputs (q, k, log_alpha rows) are loaded during the last quarter of phase A
   TileCopy<E, CH, DK, NT> pk, pq, pl;
 
-  // ---- T -> LDS (operand type), beta
+  // ---- T^T -> LDS (operand type), beta
   {
     TileCopy<float, CH, CH, NT> tt;
     tt.load(gT, CH);
-    tt.template store_cvt<OP>(sT, L::LDT, CH);
+    static_for<0, decltype(tt)::PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = tid + I * NT;
+      const int row = v / (CH / 4), c0 = (v % (CH / 4)) * 4;
+      const float* x = reinterpret_cast<const float*>(&tt.r[I]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sTT[(c0 + u) * L::LDT + row] = cvt<OP>(x[u]);
+    });
   }
   if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
 
   // ---- phase A: contractions over the value dimension
   struct QStage {
-    TileCopy<OP, QC, DK, NT> s;
-    TileCopy<float, QC, DK, NT> ds;
-    TileCopy<float, QC, CH, NT> u, du;
+    TileCopy<OP, DK, QC, NT> s;
+    TileCopy<float, DK, QC, NT> ds;
+    TileCopy<float, CH, QC, NT> u, du;
     TileCopy<E, CH, QC, NT> dov, vv;
   };
   QStage qs;
   auto qload = [&](int qq) __attribute__((always_inline)) {
     const int cq = qq * QC;
-    qs.s.load(gS + (size_t)cq * DK, DK);
-    qs.ds.load(gdS + (size_t)cq * DK, DK);
-    qs.u.load(gU + (size_t)cq * CH, CH);
-    qs.du.load(gdU + (size_t)cq * CH, CH);
+    qs.s.load(gS + cq, DV);
+    qs.ds.load(gdS + cq, DV);
+    qs.u.load(gU + cq, DV);
+    qs.du.load(gdU + cq, DV);
     qs.dov.load(doh + cq, rv, len);   // rows past the chunk are not read; they are zeroed on store
     qs.vv.load(vh + cq, rv, len);
   };
@@ -417,12 +430,26 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   for (int qq = 0; qq < NQ; ++qq) {
     const int cq = qq * QC;
     __syncthreads();  // the previous quarter's LDS reads are done
-    qs.s.store(sS, L::LSK);
-    qs.ds.template store_split<OP>(sDSh, sDSl, L::LSK);
-    qs.u.template store_split<OP>(sUh, sUl, L::LST);
-    qs.du.template store_split<OP>(sDUh, sDUl, L::LST);
-    qs.dov.template store_cvt<OP>(sDO, L::LSQ, len);
-    qs.vv.template store_cvt<OP>(sV, L::LSQ, len);
+    qs.s.store(sS, L::LSV);
+    qs.ds.template store_split<OP>(sDSh, sDSl, L::LSV);
+    qs.u.template store_split<OP>(sUh, sUl, L::LSV);
+    qs.du.template store_split<OP>(sDUh, sDUl, L::LSV);
+    // dU^T copy (token contiguous) for T^T dU
+    static_for<0, decltype(qs.du)::PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = tid + I * NT;
+      if (decltype(qs.du)::NV % NT == 0 || v < decltype(qs.du)::NV) {
+        const int row = v / (QC / 4), c0 = (v % (QC / 4)) * 4;
+        const float* x = reinterpret_cast<const float*>(&qs.du.r[I]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const OP hi = cvt<OP>(x[u]);
+          sDUTh[(c0 + u) * L::LST + row] = hi;
+          if constexpr (L::SPLIT) sDUTl[(c0 + u) * L::LST + row] = cvt<OP>(x[u] - f32(hi));
+        }
+      }
+    });
+    qs.dov.template store_cvt<OP>(sDO, L::LSV, len);
+    qs.vv.template store_cvt<OP>(sV, L::LSV, len);
     if (qq + 1 < NQ) qload(qq + 1);
     __syncthreads();
     // value sums of dS' * S for channel c (NT / DK parts of the quarter's columns)
@@ -431,27 +458,27 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       const int c = tid % DK, p = tid / DK;
 #pragma unroll
       for (int col = p * CPP; col < (p + 1) * CPP; ++col) {
-        const int o = col * L::LSK + c;
+        const int o = c * L::LSV + col;
         const float ds = L::SPLIT ? f32(sDSh[o]) + f32(sDSl[o]) : f32(sDSh[o]);
         gp += ds * f32(sS[o]);
       }
     }
-    const Frag<OP> fdo = frag_row<OP>(sDO, L::LSQ, 16 * tw + r16, kq);
-    const SFrag<OP> fdu = sfrag_col_pair<OP>(sDUh, sDUl, L::LST, 16 * tw + r16, kq);
-    const SFrag<OP> fu = sfrag_col_pair<OP>(sUh, sUl, L::LST, 16 * tw + r16, kq);
+    const Frag<OP> fdo = frag_row<OP>(sDO, L::LSV, 16 * tw + r16, kq);
+    const SFrag<OP> fdu = sfrag_pair<OP>(sDUh, sDUl, L::LSV, 16 * tw + r16, kq);
+    const SFrag<OP> fu = sfrag_pair<OP>(sUh, sUl, L::LSV, 16 * tw + r16, kq);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int nt = 2 * hf + jj;
-      accA[jj] = mma_ps(fdo, sfrag_col_pair<OP>(sUh, sUl, L::LST, 16 * nt + r16, kq), accA[jj]);
-      accT[jj] = mma_sp(fdu, frag_row<OP>(sV, L::LSQ, 16 * nt + r16, kq), accT[jj]);
+      accA[jj] = mma_ps(fdo, sfrag_pair<OP>(sUh, sUl, L::LSV, 16 * nt + r16, kq), accA[jj]);
+      accT[jj] = mma_sp(fdu, frag_row<OP>(sV, L::LSV, 16 * nt + r16, kq), accT[jj]);
     }
 #pragma unroll
     for (int jj = 0; jj < NKH; ++jj) {
       const int nt = hf * NKH + jj;
-      const Frag<OP> fs = frag_col<OP>(sS, L::LSK, 16 * nt + r16, kq);
+      const Frag<OP> fs = frag_row<OP>(sS, L::LSV, 16 * nt + r16, kq);
       accQ[jj] = mma(fdo, fs, accQ[jj]);
       accW[jj] = mma_sp(fdu, fs, accW[jj]);
-      accK[jj] = mma_ss(fu, sfrag_col_pair<OP>(sDSh, sDSl, L::LSK, 16 * nt + r16, kq), accK[jj]);
+      accK[jj] = mma_ss(fu, sfrag_pair<OP>(sDSh, sDSl, L::LSV, 16 * nt + r16, kq), accK[jj]);
     }
     __builtin_amdgcn_sched_barrier(0);
     // dV = beta T^T dU for token tile tw and the quarter's column tile hf
@@ -459,11 +486,12 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       f32x4 x = zero4();
 #pragma unroll
       for (int k = 0; k < CH; k += 32)
-        x = mma_ps(frag_col<OP>(sT, L::LDT, 16 * tw + r16, k + kq), sfrag_pair<OP>(sDUh, sDUl, L::LST, 16 * hf + r16, k + kq), x);
+        x = mma_ps(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq),
+                   sfrag_pair<OP>(sDUTh, sDUTl, L::LST, 16 * hf + r16, k + kq), x);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * tw + 4 * q4 + ii, col = 16 * hf + r16;
-        float p = f32(sV[r * L::LSQ + col]) * x[ii];
+        float p = f32(sV[r * L::LSV + col]) * x[ii];
         p += __shfl_xor(p, 1);
         p += __shfl_xor(p, 2);
         p += __shfl_xor(p, 4);
@@ -544,7 +572,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     f32x4 x = zero4();
 #pragma unroll
     for (int k = 0; k < CH; k += 32)
-      x = mma(frag_col<OP>(sT, L::LDT, 16 * tw + r16, k + kq), frag_col<OP>(sDW, L::LDO, 16 * nt + r16, k + kq), x);
+      x = mma(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq), frag_col<OP>(sDW, L::LDO, 16 * nt + r16, k + kq), x);
     tdw[jj] = x;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -577,7 +605,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       float y8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) y8[u] = sA2[(16 * tw + r16) * L::LDA + k + kq + u];
-      x = mma(frag_from<OP>(y8), frag_row<OP>(sT, L::LDT, 16 * nt + r16, k + kq), x);
+      x = mma(frag_from<OP>(y8), frag_col<OP>(sTT, L::LDT, 16 * nt + r16, k + kq), x);
     }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) sY[(16 * tw + 4 * q4 + ii) * L::LDT + 16 * nt + r16] = cvt<OP>(x[ii]);
@@ -590,7 +618,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     f32x4 x = zero4();
 #pragma unroll
     for (int k = 0; k < CH; k += 32)
-      x = mma(frag_col<OP>(sT, L::LDT, 16 * tw + r16, k + kq), frag_col<OP>(sY, L::LDT, 16 * nt + r16, k + kq), x);
+      x = mma(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq), frag_col<OP>(sY, L::LDT, 16 * nt + r16, k + kq), x);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;

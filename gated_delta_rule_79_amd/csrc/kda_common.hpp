@@ -380,10 +380,10 @@ struct WsBlock {
   static constexpr size_t UTF = (size_t)DV * CH;   // U~^T [DV][CH]   float
   static constexpr size_t G = (size_t)CH * CH;     // un-beta strict Gram [CH][CH]   float
   static constexpr size_t KHF = (size_t)CH * DK;   // Kh  [CH][DK]   float
-  static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk [DV][DK]   OP
-  static constexpr size_t U = (size_t)DV * CH;     // U^T [DV][CH]   float
-  static constexpr size_t DS = (size_t)DK * DV;    // dS' [DV][DK]   float
-  static constexpr size_t DU = (size_t)DV * CH;    // dU^T [DV][CH]  float
+  static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk [DK][DV]   OP
+  static constexpr size_t U = (size_t)DV * CH;     // U [CH][DV]   float
+  static constexpr size_t DS = (size_t)DK * DV;    // dS' [DK][DV]   float
+  static constexpr size_t DU = (size_t)DV * CH;    // dU [CH][DV]  float
 };
 
 }  // namespace kda

@@ -855,9 +855,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       if (t < NST) {
         store4<OP>(sST + (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4, S[i][0], S[i][1], S[i][2], S[i][3]);
         if constexpr (SAVE) {
-          // backward needs the state entering every chunk: OP [DV][DK] per chunk-head
-          OP* dst = gS + blk_of(n) * WB::S + (size_t)(n0 + 16 * nt + r16) * DK + 16 * mt + 4 * q4;
-          store4<OP>(dst, S[i][0], S[i][1], S[i][2], S[i][3]);
+          // backward needs the state entering every chunk: OP [DK][DV] per chunk-head
+          OP* dst = gS + blk_of(n) * WB::S + (size_t)(16 * mt + 4 * q4) * DV + n0 + 16 * nt + r16;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = cvt<OP>(S[i][ii]);
         }
       }
     }
@@ -876,9 +877,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         store4<OP>(sUL + (16 * nt + r16) * L::LDT + 16 * w + 4 * q4, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2],
                    ut[3] - x[3]);
         if constexpr (SAVE) {
-          // and U^T in fp32
-          float* dst = gU + blk_of(n) * WB::U + (size_t)(n0 + 16 * nt + r16) * CH + 16 * w + 4 * q4;
-          *reinterpret_cast<f32x4*>(dst) = f32x4{ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]};
+          // and U in fp32, token-major [CH][DV]
+          float* dst = gU + blk_of(n) * WB::U + (size_t)(16 * w + 4 * q4) * DV + n0 + 16 * nt + r16;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = ut[ii] - x[ii];
         }
       }
     } else if constexpr (OUT) {

@@ -34,10 +34,10 @@ struct Args {
   float* wsUtF;             // U~^T in fp32 [DV][CH] (the backward's state pass reads it)
   float* wsG;               // un-beta strict Gram K+ K-^T
   float* wsKhF;             // Kh token-major, fp32
-  void* wsS;                // state entering each chunk, OP [DV][DK]
-  float* wsU;               // U^T, fp32 [DV][CH]
-  float* wsdS;              // gradient of the state leaving each chunk, fp32 [DV][DK]
-  float* wsdU;              // dU^T, fp32 [DV][CH]
+  void* wsS;                // state entering each chunk, OP [DK][DV]
+  float* wsU;               // U, fp32 [CH][DV]
+  float* wsdS;              // gradient of the state leaving each chunk, fp32 [DK][DV]
+  float* wsdU;              // dU, fp32 [CH][DV]
   int dvs;                  // value-column slice width of the sequential passes
   int out_bf16;             // outputs and gradients stored as bf16 (else fp32)
 };
