@@ -639,32 +639,48 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   O* dlo = reinterpret_cast<O*>(a.dla) + (size_t)ci.t0 * rk + (size_t)h * DK;
   float dgv[NKH][4];
   float khs[NKH];   // column sums over this lane's rows of dKh * Kh (for dg_C)
+  // TP channel tiles per pass share the split dAqk / dG fragments
+  constexpr int TP = 2;
 #pragma unroll
-  for (int jj = 0; jj < NKH; ++jj) {
-    const int cc = 16 * (hf * NKH + jj) + r16;
-    f32x4 dqg = zero4(), dkpg = zero4(), dkm = zero4();
+  for (int jp = 0; jp < NKH; jp += TP) {
+    f32x4 dqg[TP], dkpg[TP], dkm[TP];
+    int ccs[TP];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      dqg[t] = dkpg[t] = dkm[t] = zero4();
+      ccs[t] = 16 * (hf * NKH + jp + t) + r16;
+    }
     {
       const int ab = tw, ref = 16 * ab + 8;
       const int kmax = 16 * (ab + 1);  // columns i < kmax can be nonzero
-      const float gref = sG[ref * L::LDG + cc];
       for (int k = 0; k < kmax; k += 32) {
         const SFrag<SE> fa1 = sfrag_row<SE>(sA1, L::LDA, 16 * ab + r16, k + kq);
         const SFrag<SE> fa2 = sfrag_row<SE>(sA2, L::LDA, 16 * ab + r16, k + kq);
-        float xr[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = k + kq + u;
-          xr[u] = i < kmax ? f32(sK[i * L::LDK + cc]) * __expf(gref - sG[i * L::LDG + cc]) : 0.f;
+        for (int t = 0; t < TP; ++t) {
+          const int cc = ccs[t];
+          const float gref = sG[ref * L::LDG + cc];
+          float xr[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = k + kq + u;
+            xr[u] = i < kmax ? f32(sK[i * L::LDK + cc]) * __expf(gref - sG[i * L::LDG + cc]) : 0.f;
+          }
+          const SFrag<SE> fr = sfrag_from<SE>(xr);
+          dqg[t] = mma_ss(fa1, fr, dqg[t]);
+          dkpg[t] = mma_ss(fa2, fr, dkpg[t]);
         }
-        const SFrag<SE> fr = sfrag_from<SE>(xr);
-        dqg = mma_ss(fa1, fr, dqg);
-        dkpg = mma_ss(fa2, fr, dkpg);
       }
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gref);
-        dqg[ii] *= e;
-        dkpg[ii] *= e;
+      for (int t = 0; t < TP; ++t) {
+        const int cc = ccs[t];
+        const float gref = sG[ref * L::LDG + cc];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gref);
+          dqg[t][ii] *= e;
+          dkpg[t][ii] *= e;
+        }
       }
     }
     {
@@ -675,39 +691,48 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         const float* srcA = q4 < 2 ? sA1 : sA2;
         const int rbase = 16 * ab + 8 * (q4 & 1);
         const SFrag<SE> fa = sfrag_col_f32<SE>(srcA, L::LDA, 16 * b + r16, rbase);
-        const float gref = sG[ref * L::LDG + cc];
-        float xl8[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int rr = rbase + u;
-          const float src = q4 < 2 ? f32(sQ[rr * L::LDK + cc]) : f32(sK[rr * L::LDK + cc]);
-          xl8[u] = src * __expf(sG[rr * L::LDG + cc] - gref);
-        }
-        const f32x4 y = mma_ss(fa, sfrag_from<SE>(xl8), zero4());
+        for (int t = 0; t < TP; ++t) {
+          const int cc = ccs[t];
+          const float gref = sG[ref * L::LDG + cc];
+          float xl8[8];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * b + 4 * q4 + ii;
-          dkm[ii] += __expf(gref - sG[i * L::LDG + cc]) * y[ii];
+          for (int u = 0; u < 8; ++u) {
+            const int rr = rbase + u;
+            const float src = q4 < 2 ? f32(sQ[rr * L::LDK + cc]) : f32(sK[rr * L::LDK + cc]);
+            xl8[u] = src * __expf(sG[rr * L::LDG + cc] - gref);
+          }
+          const f32x4 y = mma_ss(fa, sfrag_from<SE>(xl8), zero4());
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int i = 16 * b + 4 * q4 + ii;
+            dkm[t][ii] += __expf(gref - sG[i * L::LDG + cc]) * y[ii];
+          }
         }
       }
     }
     // assembly (rows 16tw + 4q4 + ii)
-    khs[jj] = 0.f;
-    const float gl = sG[(CH - 1) * L::LDG + cc];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int rr = 16 * tw + 4 * q4 + ii;
-      const float g = sG[rr * L::LDG + cc];
-      const float eg = __expf(g);
-      const float kv = f32(sK[rr * L::LDK + cc]), qv = f32(sQ[rr * L::LDK + cc]);
-      const float dq = eg * scale * accQ[jj][ii] + dqg[ii];
-      const float dkp = eg * sBeta[rr] * tdw[jj][ii] + dkpg[ii];
-      const float dkh = __expf(gl - g) * accK[jj][ii];
-      dgv[jj][ii] = dq * qv + (dkp - dkm[ii] - dkh) * kv;
-      khs[jj] += dkh * kv;
-      if (rr < len) {
-        dqo[(size_t)rr * rk + cc] = cvt<O>(dq);
-        dko[(size_t)rr * rk + cc] = cvt<O>(dkp + dkm[ii] + dkh);
+    for (int t = 0; t < TP; ++t) {
+      const int jj = jp + t, cc = ccs[t];
+      khs[jj] = 0.f;
+      const float gl = sG[(CH - 1) * L::LDG + cc];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int rr = 16 * tw + 4 * q4 + ii;
+        const float g = sG[rr * L::LDG + cc];
+        const float eg = __expf(g);
+        const float kv = f32(sK[rr * L::LDK + cc]), qv = f32(sQ[rr * L::LDK + cc]);
+        const float dq = eg * scale * accQ[jj][ii] + dqg[t][ii];
+        const float dkp = eg * sBeta[rr] * tdw[jj][ii] + dkpg[t][ii];
+        const float dkmv = dkm[t][ii];
+        const float dkh = __expf(gl - g) * accK[jj][ii];
+        dgv[jj][ii] = dq * qv + (dkp - dkmv - dkh) * kv;
+        khs[jj] += dkh * kv;
+        if (rr < len) {
+          dqo[(size_t)rr * rk + cc] = cvt<O>(dq);
+          dko[(size_t)rr * rk + cc] = cvt<O>(dkp + dkmv + dkh);
+        }
       }
     }
   }

@@ -33,6 +33,10 @@
 
 #include "kda_internal.hpp"
 
+#ifndef KDA_STATE_PF
+#define KDA_STATE_PF 1
+#endif
+
 namespace kda {
 
 // ---------------------------------------------------------------------------
@@ -744,8 +748,11 @@ struct StateLds {
   static_assert(BYTES <= 163840, "state LDS");
 };
 
-template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void kda_state(const Args a) {
+// PF = 2: operands of chunk n+2 are in flight while chunk n+1 waits in
+// registers (one work-group per CU); PF = 1: one set of staging registers, so
+// the kernel fits 4 waves per SIMD and two work-groups share a CU.
+template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int PF>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4 : 1, PF == 1 ? 4 : 2))) void kda_state(const Args a) {
   using L = StateLds<E, DK, DV, DVS, OUT, SAVE>;
   using OP = typename L::OP;
   using WB = WsBlock<E, DK, DV>;
@@ -818,7 +825,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     TileCopy<UTT, DVS, CH, NT> ut;
     TileCopy<float, 1, DK, NT> gam;
   };
-  Stage st0, st1;
+  Stage st0;
+  [[maybe_unused]] Stage st1;
   auto blk_of = [&](int n) { return (size_t)(c0 + n) * H + h; };
   auto stage_load = [&](Stage& p, int n) __attribute__((always_inline)) {
     const size_t b = blk_of(n);
@@ -843,10 +851,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   };
 
   const size_t ro = (size_t)H * DV;
-  // one chunk: LDS holds chunk n; `ld` receives chunk n+2 (clamped, so its
+  // one chunk: LDS holds chunk n; `ld` receives chunk n+PF (clamped, so its
   // registers are always defined); `nx` holds chunk n+1 and goes to LDS at the end
   auto chunk = [&](int n, Stage& ld, const Stage& nx) __attribute__((always_inline)) {
-    stage_load(ld, min(n + 2, nch - 1));
+    stage_load(ld, min(n + PF, nch - 1));
 
     // S -> LDS in the operand type, transposed ([column][channel])
 #pragma unroll
@@ -928,11 +936,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   if (nch > 0) {
     stage_load(st0, 0);
     stage_store(st0);
-    stage_load(st1, min(1, nch - 1));
+    if constexpr (PF == 2) stage_load(st1, min(1, nch - 1));
   }
-  for (int n = 0; n < nch; n += 2) {
-    chunk(n, st0, st1);
-    if (n + 1 < nch) chunk(n + 1, st1, st0);
+  if constexpr (PF == 2) {
+    for (int n = 0; n < nch; n += 2) {
+      chunk(n, st0, st1);
+      if (n + 1 < nch) chunk(n + 1, st1, st0);
+    }
+  } else {
+    for (int n = 0; n < nch; ++n) chunk(n, st0, st0);
   }
 
   if (gFinal) {
@@ -957,8 +969,9 @@ static hipError_t launch_state(const Args& a, hipStream_t st) {
   const int groups = (units + 7) / 8;
   const int grid = groups * 8 * NSL;
   if (grid == 0) return hipSuccess;
+  constexpr int PF = KDA_STATE_PF;
   KDA_TIMED(OUT ? (SAVE ? "kda_state_fwd_save" : "kda_state_fwd") : "kda_state_bwd_fwdpass", st,
-            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT, SAVE>), dim3(grid), dim3(512), 0, st, a));
+            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT, SAVE, PF>), dim3(grid), dim3(512), 0, st, a));
   return hipGetLastError();
 }
 
