@@ -38,10 +38,11 @@ struct RevLds {
   static constexpr int P = PADE<OP>;
   static constexpr int LDK = DK + P;
   static constexpr int LDT = CH + P;
-  static constexpr int LDF = DK + 4;
+  static constexpr bool SPLIT = sizeof(OP) == 2;
   static constexpr size_t AQK = 0;                                          // OP    [CH][LDT]
-  static constexpr size_t KHF = AQK + (size_t)CH * LDT * sizeof(OP);        // float [CH][LDF]
-  static constexpr size_t QT = KHF + (size_t)CH * LDF * 4;                  // OP    [CH][LDK]
+  static constexpr size_t KHH = AQK + (size_t)CH * LDT * sizeof(OP);        // OP    [CH][LDK]  Kh (hi)
+  static constexpr size_t KHL = KHH + (size_t)CH * LDK * sizeof(OP);        // OP    [CH][LDK]  Kh (lo)
+  static constexpr size_t QT = KHL + (SPLIT ? (size_t)CH * LDK * sizeof(OP) : 0);  // OP [CH][LDK]
   static constexpr size_t W = QT + (size_t)CH * LDK * sizeof(OP);           // OP    [CH][LDK]
   static constexpr size_t GAM = W + (size_t)CH * LDK * sizeof(OP);          // float [DK]
   static constexpr size_t DOT = GAM + (size_t)DK * 4;                       // OP    [DVS][LDT]  dO^T slice
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   }
 
   OP* sAqk = reinterpret_cast<OP*>(smem + L::AQK);
-  float* sKhF = reinterpret_cast<float*>(smem + L::KHF);
+  OP* sKhH = reinterpret_cast<OP*>(smem + L::KHH);
+  OP* sKhL = reinterpret_cast<OP*>(smem + L::KHL);
   OP* sQt = reinterpret_cast<OP*>(smem + L::QT);
   OP* sW = reinterpret_cast<OP*>(smem + L::W);
   float* sGam = reinterpret_cast<float*>(smem + L::GAM);
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   OP* sDUl = reinterpret_cast<OP*>(smem + L::DUL);
 
   const OP* gAqk = reinterpret_cast<const OP*>(a.wsAqk);
-  const float* gKhF = a.wsKhF;
+  const char* gKh = reinterpret_cast<const char*>(a.wsKhF);   // per block: hi [CH][DK], then lo (split types)
   const OP* gQt = reinterpret_cast<const OP*>(a.wsQt);
   const OP* gW = reinterpret_cast<const OP*>(a.wsW);
   const float* gGam = a.wsGam;
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   constexpr int EPV = 16 / (int)sizeof(E), VPR = DVS / EPV, NVO = CH * VPR;
   struct Stage {
     TileCopy<OP, CH, CH, NT> aqk;
-    TileCopy<float, CH, DK, NT> khf;
+    TileCopy<OP, CH, DK, NT> khh;
+    TileCopy<OP, (L::SPLIT ? CH : 1), (L::SPLIT ? DK : 16 / sizeof(OP)), NT> khl;
     TileCopy<OP, CH, DK, NT> qt;
     TileCopy<OP, CH, DK, NT> w;
     TileCopy<float, 1, DK, NT> gam;
@@ -130,7 +133,9 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   auto stage_load = [&](Stage& p, int n) __attribute__((always_inline)) {
     const size_t b = blk_of(n);
     p.aqk.load(gAqk + b * WB::AQK, CH);
-    p.khf.load(gKhF + b * WB::KHF, DK);
+    const OP* kb = reinterpret_cast<const OP*>(gKh + b * WB::KHF * sizeof(float));
+    p.khh.load(kb, DK);
+    if constexpr (L::SPLIT) p.khl.load(kb + CH * DK, DK);
     p.qt.load(gQt + b * WB::QT, DK);
     p.w.load(gW + b * WB::W, DK);
     p.gam.load(gGam + b * WB::GAM, DK);
@@ -143,7 +148,8 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   };
   auto stage_store = [&](const Stage& p) __attribute__((always_inline)) {
     p.aqk.store(sAqk, L::LDT);
-    p.khf.store(sKhF, L::LDF);
+    p.khh.store(sKhH, L::LDK);
+    if constexpr (L::SPLIT) p.khl.store(sKhL, L::LDK);
     p.qt.store(sQt, L::LDK);
     p.w.store(sW, L::LDK);
     p.gam.store(sGam, DK);
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
                    frag_row<OP>(sDOT, L::LDT, 16 * nt + r16, k + 8 * q4), x1);
 #pragma unroll
         for (int k = 0; k < DK; k += 32)
-          x2 = mma_ss(sfrag_row<OP>(sKhF, L::LDF, 16 * w + r16, k + 8 * q4),
+          x2 = mma_ss(sfrag_pair<OP>(sKhH, sKhL, L::LDK, 16 * w + r16, k + 8 * q4),
                       sfrag_pair<OP>(sDSh, sDSl, L::LDK, 16 * nt + r16, k + 8 * q4), x2);
         const f32x4 du = scale * x1 + x2;
         const int off = (16 * nt + r16) * L::LDT + 16 * w + 4 * q4;

@@ -379,7 +379,8 @@ struct WsBlock {
   // backward only
   static constexpr size_t UTF = (size_t)DV * CH;   // U~^T [DV][CH]   float
   static constexpr size_t G = (size_t)CH * CH;     // un-beta strict Gram [CH][CH]   float
-  static constexpr size_t KHF = (size_t)CH * DK;   // Kh  [CH][DK]   float
+  static constexpr size_t KHF = (size_t)CH * DK;   // Kh  [CH][DK]   float-sized slot: fp32 Kh, or (split
+                                                   // types) fp16 hi [CH][DK] followed by fp16 lo [CH][DK]
   static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk [DK][DV]   OP
   static constexpr size_t U = (size_t)DV * CH;     // U [CH][DV]   float
   static constexpr size_t DS = (size_t)DK * DV;    // dS' [DK][DV]   float

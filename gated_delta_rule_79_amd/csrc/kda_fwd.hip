@@ -545,13 +545,15 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
         store4<OP>(wQt + r * DK + c0, y[0], y[1], y[2], y[3]);
         store4<OP>(wQt + r * DK + c0 + 4, y[4], y[5], y[6], y[7]);
         if constexpr (BWD) {
-          // Kh token-major in fp32 (the reverse pass multiplies it as a split operand)
-          float* wKhF = a.wsKhF + blk * WB::KHF;
+          // Kh token-major as a split pair of fp16 arrays (hi, then lo), the form in
+          // which the reverse pass multiplies it
+          OP* wKhH = reinterpret_cast<OP*>(a.wsKhF + blk * WB::KHF);
+          OP* wKhL = wKhH + CH * DK;
 #pragma unroll
           for (int u = 0; u < 8; ++u)
             y[u] = f32(sK[r * L::LDK + c0 + u]) * __expf(sG[(CH - 1) * L::LDG + c0 + u] - sG[r * L::LDG + c0 + u]);
-          *reinterpret_cast<f32x4*>(wKhF + r * DK + c0) = f32x4{y[0], y[1], y[2], y[3]};
-          *reinterpret_cast<f32x4*>(wKhF + r * DK + c0 + 4) = f32x4{y[4], y[5], y[6], y[7]};
+          store4_split<OP>(wKhH + r * DK + c0, wKhL + r * DK + c0, y[0], y[1], y[2], y[3]);
+          store4_split<OP>(wKhH + r * DK + c0 + 4, wKhL + r * DK + c0 + 4, y[4], y[5], y[6], y[7]);
         }
       }
 #pragma unroll
