@@ -808,7 +808,7 @@ hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved) {
     e = launch_bwd_front<E, DK, DV>(a, st);
     if (e != hipSuccess) return e;
   }
-  constexpr int DVS = 16, NSL = DV / DVS;
+  constexpr int DVS = sizeof(E) == 2 ? 64 : 32, NSL = DV / DVS;
   const int units = a.N * a.H;
   const int grid = (units + 7) / 8 * 8 * NSL;
   if (grid > 0) {
