@@ -178,23 +178,25 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
     }
     __syncthreads();
 
-    if (w < 4) {
-      // dU (token tile w) = scale Aqk^T dO + Kh dS'
+    // dU = scale Aqk^T dO + Kh dS' : tiles (token tile tt, value tile nt) dealt to all eight waves
+    constexpr int NDU = 4 * NTS, DPW = (NDU + 7) / 8;
 #pragma unroll
-      for (int nt = 0; nt < NTS; ++nt) {
+    for (int j = 0; j < DPW; ++j) {
+      const int u = w + 8 * j, tt = u % 4, nt = u / 4;
+      if (u < NDU) {
         f32x4 x1 = zero4(), x2 = zero4();
 #pragma unroll
         for (int k = 0; k < CH; k += 32)
-          x1 = mma(frag_col<OP>(sAqk, L::LDT, 16 * w + r16, k + 8 * q4),
+          x1 = mma(frag_col<OP>(sAqk, L::LDT, 16 * tt + r16, k + 8 * q4),
                    frag_row<OP>(sDOT, L::LDT, 16 * nt + r16, k + 8 * q4), x1);
 #pragma unroll
         for (int k = 0; k < DK; k += 32)
-          x2 = mma_ss(sfrag_pair<OP>(sKhH, sKhL, L::LDK, 16 * w + r16, k + 8 * q4),
+          x2 = mma_ss(sfrag_pair<OP>(sKhH, sKhL, L::LDK, 16 * tt + r16, k + 8 * q4),
                       sfrag_pair<OP>(sDSh, sDSl, L::LDK, 16 * nt + r16, k + 8 * q4), x2);
         const f32x4 du = scale * x1 + x2;
-        const int off = (16 * nt + r16) * L::LDT + 16 * w + 4 * q4;
+        const int off = (16 * nt + r16) * L::LDT + 16 * tt + 4 * q4;
         store4_split<OP>(sDUh + off, sDUl + off, du[0], du[1], du[2], du[3]);
-        float* dst = gdU + blk_of(n) * WB::DU + (size_t)(16 * w + 4 * q4) * DV + n0 + 16 * nt + r16;  // [CH][DV]
+        float* dst = gdU + blk_of(n) * WB::DU + (size_t)(16 * tt + 4 * q4) * DV + n0 + 16 * nt + r16;  // [CH][DV]
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = du[ii];
       }
