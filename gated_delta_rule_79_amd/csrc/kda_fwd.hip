@@ -33,6 +33,13 @@
 
 #include "kda_internal.hpp"
 
+// value columns per work-group of the state passes (bf16 inputs; fp32 uses 32)
+#ifndef KDA_SAVE_DVS
+#define KDA_SAVE_DVS 64
+#endif
+#ifndef KDA_FWD_DVS
+#define KDA_FWD_DVS 64
+#endif
 #ifndef KDA_STATE_PF
 #define KDA_STATE_PF 1
 #endif
@@ -1017,12 +1024,12 @@ hipError_t launch_fwd(const Args& a, hipStream_t st, bool save) {
     } else {
       e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_save");
       if (e != hipSuccess) return e;
-      return launch_state<E, O, DK, DV, 16, true, true>(a, st);
+      return launch_state<E, O, DK, DV, (sizeof(E) == 2 ? KDA_SAVE_DVS : 32), true, true>(a, st);
     }
   }
   e = launch_prep<E, DK, DV, false>(a, st, "kda_prep");
   if (e != hipSuccess) return e;
-  return launch_state<E, O, DK, DV, 16, true, false>(a, st);
+  return launch_state<E, O, DK, DV, (sizeof(E) == 2 ? KDA_FWD_DVS : 32), true, false>(a, st);
 }
 
 // front half of the backward pass: chunk map, chunk-local prep (also keeping
@@ -1033,7 +1040,7 @@ hipError_t launch_bwd_front(const Args& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_bwd");
   if (e != hipSuccess) return e;
-  return launch_state<E, float, DK, DV, 16, false, true>(a, st);
+  return launch_state<E, float, DK, DV, (sizeof(E) == 2 ? KDA_SAVE_DVS : 32), false, true>(a, st);
 }
 
 #define KDA_INST(E, DK, DV)                                                                   \
