@@ -801,6 +801,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <typename E, int DK, int DV, int DVS>
+static hipError_t launch_rev(const Args& a, hipStream_t st) {
+  constexpr int NSL = DV / DVS;
+  const int grid = (a.N * a.H + 7) / 8 * 8 * NSL;
+  KDA_TIMED("kda_state_bwd_revpass", st,
+            hipLaunchKernelGGL((kda_state_rev<E, DK, DV, DVS>), dim3(grid), dim3(512), 0, st, a));
+  return hipGetLastError();
+}
+
 // `saved`: the workspace already holds the forward intermediates (kda_fwd with
 // KDA_FLAG_SAVE_FOR_BACKWARD on the same inputs), so the front half is skipped.
 template <typename E, typename O, int DK, int DV>
@@ -810,13 +819,17 @@ hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved) {
     e = launch_bwd_front<E, DK, DV>(a, st);
     if (e != hipSuccess) return e;
   }
-  constexpr int DVS = sizeof(E) == 2 ? 64 : 32, NSL = DV / DVS;
   const int units = a.N * a.H;
-  const int grid = (units + 7) / 8 * 8 * NSL;
-  if (grid > 0) {
-    KDA_TIMED("kda_state_bwd_revpass", st,
-              hipLaunchKernelGGL((kda_state_rev<E, DK, DV, DVS>), dim3(grid), dim3(512), 0, st, a));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (units > 0) {
+    if constexpr (sizeof(E) == 2) {
+      if (pick_dvs(units, DV) == 64)
+        e = launch_rev<E, DK, DV, 64>(a, st);
+      else
+        e = launch_rev<E, DK, DV, 16>(a, st);
+    } else {
+      e = launch_rev<E, DK, DV, 32>(a, st);
+    }
+    if (e != hipSuccess) return e;
   }
   if (a.max_chunks > 0) {
     KDA_TIMED("kda_bwd_chunk", st,

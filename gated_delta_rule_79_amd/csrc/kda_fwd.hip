@@ -33,13 +33,6 @@
 
 #include "kda_internal.hpp"
 
-// value columns per work-group of the state passes (bf16 inputs; fp32 uses 32)
-#ifndef KDA_SAVE_DVS
-#define KDA_SAVE_DVS 64
-#endif
-#ifndef KDA_FWD_DVS
-#define KDA_FWD_DVS 64
-#endif
 #ifndef KDA_STATE_PF
 #define KDA_STATE_PF 1
 #endif
@@ -971,6 +964,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   }
 }
 
+// Compute units of the current device (the persistent prep runs one work-group on each).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Value columns per work-group of a sequential pass (bf16 inputs): the widest
+// slice that still gives every compute unit a work-group.  Wider slices stage the
+// per-chunk operands for more columns at once; a grid shorter than the CU count
+// leaves CUs idle while the longest chain runs.
+int pick_dvs(int units, int dv) {
+  return (dv >= 64 && (long long)units * (dv / 64) >= device_cus()) ? 64 : 16;
+}
+
 template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE>
 static hipError_t launch_state(const Args& a, hipStream_t st) {
   constexpr int NSL = DV / DVS;
@@ -984,17 +998,14 @@ static hipError_t launch_state(const Args& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (the persistent prep runs one work-group on each).
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+template <typename E, typename O, int DK, int DV, bool OUT, bool SAVE>
+static hipError_t launch_state_auto(const Args& a, hipStream_t st) {
+  if constexpr (sizeof(E) == 2) {
+    if (pick_dvs(a.N * a.H, DV) == 64) return launch_state<E, O, DK, DV, 64, OUT, SAVE>(a, st);
+    return launch_state<E, O, DK, DV, 16, OUT, SAVE>(a, st);
+  } else {
+    return launch_state<E, O, DK, DV, 32, OUT, SAVE>(a, st);
   }
-  return cached[dev];
 }
 
 // BWD: also keep what the backward pass needs (T, the un-beta Gram, fp32 Kh and U~).
@@ -1024,12 +1035,12 @@ hipError_t launch_fwd(const Args& a, hipStream_t st, bool save) {
     } else {
       e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_save");
       if (e != hipSuccess) return e;
-      return launch_state<E, O, DK, DV, (sizeof(E) == 2 ? KDA_SAVE_DVS : 32), true, true>(a, st);
+      return launch_state_auto<E, O, DK, DV, true, true>(a, st);
     }
   }
   e = launch_prep<E, DK, DV, false>(a, st, "kda_prep");
   if (e != hipSuccess) return e;
-  return launch_state<E, O, DK, DV, (sizeof(E) == 2 ? KDA_FWD_DVS : 32), true, false>(a, st);
+  return launch_state_auto<E, O, DK, DV, true, false>(a, st);
 }
 
 // front half of the backward pass: chunk map, chunk-local prep (also keeping
@@ -1040,7 +1051,7 @@ hipError_t launch_bwd_front(const Args& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_bwd");
   if (e != hipSuccess) return e;
-  return launch_state<E, float, DK, DV, (sizeof(E) == 2 ? KDA_SAVE_DVS : 32), false, true>(a, st);
+  return launch_state_auto<E, float, DK, DV, false, true>(a, st);
 }
 
 #define KDA_INST(E, DK, DV)                                                                   \

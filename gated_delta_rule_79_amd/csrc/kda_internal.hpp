@@ -55,6 +55,8 @@ void timing_end(hipStream_t st);
   } while (0)
 
 hipError_t launch_chunk_map(const Args& a, hipStream_t st);
+int device_cus();                  // compute units of the current device
+int pick_dvs(int units, int dv);   // value-slice width of the sequential passes (bf16 inputs)
 template <typename E, typename O, int DK, int DV> hipError_t launch_fwd(const Args& a, hipStream_t st, bool save);
 template <typename E, int DK, int DV> hipError_t launch_bwd_front(const Args& a, hipStream_t st);
 template <typename E, typename O, int DK, int DV> hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved);
