@@ -26,6 +26,7 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 _lib = None
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_ERROR_LAUNCH = 5   # kda_status value of a failed kernel launch (include/kda.h)
 KDA_FLAG_SAVE_FOR_BACKWARD, KDA_FLAG_USE_SAVED = 1, 2   # kda_desc.flags bits (include/kda.h)
 
 
@@ -38,7 +39,8 @@ class kda_desc(ctypes.Structure):
 class KdaError(RuntimeError):
     def __init__(self, fn, status):
         self.status = status
-        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+        detail = last_error() if status == KDA_ERROR_LAUNCH else ""
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})" + (f": {detail}" if detail else ""))
 
 
 def lib_path() -> str:
@@ -53,6 +55,10 @@ def load_library(path: str | None = None):
     p = path or _LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"libkda.so not found at {p}; build it with gated_delta_rule_79_amd.build.build()")
+    # torch ships its own HIP runtime; loading torch first makes libkda.so bind to
+    # that same runtime (a second runtime in the process cannot see the device
+    # memory and streams torch hands over).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     P = ctypes.c_void_p
     D = ctypes.POINTER(kda_desc)
@@ -64,6 +70,8 @@ def load_library(path: str | None = None):
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_timing_enable.argtypes = [ctypes.c_int]
     lib.kda_timing_enable.restype = None
     lib.kda_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -97,6 +105,14 @@ def status_string(status: int) -> str:
         return load_library().kda_status_string(int(status)).decode()
     except Exception:  # library missing: still give a readable message
         return f"status {status}"
+
+
+def last_error() -> str:
+    """The failing kernel launch and HIP error of this thread's last kda_fwd/kda_bwd call ("" if none)."""
+    try:
+        return load_library().kda_last_error().decode()
+    except Exception:  # library missing
+        return ""
 
 
 def _dtype_code(dt) -> int:

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -30,7 +31,7 @@ struct Plan {
   int N = 0;
   int max_chunks = 0;
   size_t esz = 0;
-  size_t chunks = 0, sc0 = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
+  size_t chunks = 0, sc0 = 0, so = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
   size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0;
   size_t total = 0;
 };
@@ -68,6 +69,7 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
   p.chunks = take((size_t)max_chunks * sizeof(ChunkInfo));
   p.sc0 = take((size_t)(N + 1) * sizeof(int32_t));
+  p.so = take((size_t)N * sizeof(int32_t));
   p.W = take(nb * CH * dk * e);    // operand type: fp16 for bf16 inputs, fp32 otherwise
   p.KhT = take(nb * dk * CH * e);
   p.Qt = take(nb * CH * dk * e);
@@ -110,6 +112,7 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
   char* b = static_cast<char*>(ws);
   a.chunks = reinterpret_cast<ChunkInfo*>(b + p.chunks);
   a.seq_chunk0 = reinterpret_cast<int32_t*>(b + p.sc0);
+  a.seq_order = reinterpret_cast<int32_t*>(b + p.so);
   a.wsW = b + p.W;
   a.wsKhT = b + p.KhT;
   a.wsQt = b + p.Qt;
@@ -205,9 +208,23 @@ TimingState& timing() {
   return t;
 }
 
+// First failing launch of the current kda_fwd/kda_bwd call on this host thread.
+thread_local char tl_error[256];
+void clear_error() { tl_error[0] = 0; }
+kda_status launch_status(hipError_t e) {
+  if (e == hipSuccess) return KDA_SUCCESS;
+  if (!tl_error[0]) std::snprintf(tl_error, sizeof tl_error, "%s (%s)", hipGetErrorName(e), hipGetErrorString(e));
+  return KDA_ERROR_LAUNCH;
+}
+
 }  // namespace
 
 namespace kda {
+void note_launch(const char* name) {
+  const hipError_t e = hipPeekAtLastError();
+  if (e == hipSuccess || tl_error[0]) return;
+  std::snprintf(tl_error, sizeof tl_error, "%s: %s (%s)", name, hipGetErrorName(e), hipGetErrorString(e));
+}
 void timing_begin(const char* name, hipStream_t st) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
@@ -289,6 +306,8 @@ const char* kda_status_string(kda_status s) {
   return "unknown status";
 }
 
+const char* kda_last_error(void) { return tl_error; }
+
 size_t kda_workspace_bytes(const kda_desc* d, int backward) {
   if (!d || !dims_ok(d)) return 0;
   int N, mc;
@@ -332,7 +351,8 @@ kda_status kda_fwd(const kda_desc* d, const void* q, const void* k, const void* 
   a.out = out; a.final_state = final_state;
   fill_ws(a, p, workspace);
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
-  return run_fwd(d, a, st) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+  clear_error();
+  return launch_status(run_fwd(d, a, st));
 }
 
 kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
@@ -369,7 +389,8 @@ kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* 
   a.dq = dq; a.dk_ = dk; a.dv_ = dv; a.dla = dlog_alpha; a.dbeta = dbeta; a.dinit = d_init_state;
   fill_ws(a, p, workspace);
   (void)hipGetLastError();
-  return run_bwd(d, a, st) == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH;
+  clear_error();
+  return launch_status(run_bwd(d, a, st));
 }
 
 }  // extern "C"

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
 
   int unit, sl;
   if (!xcd_unit(blockIdx.x, NSL, a.N * a.H, unit, sl)) return;
-  const int seq = unit / a.H, h = unit % a.H, H = a.H;
+  const int seq = a.seq_order[unit / a.H], h = unit % a.H, H = a.H;   // longest sequences first
   const int n0 = sl * DVS;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
   const int c0 = a.seq_chunk0[seq], nch = a.seq_chunk0[seq + 1] - c0;

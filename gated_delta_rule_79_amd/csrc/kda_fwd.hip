@@ -44,8 +44,11 @@ namespace kda {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void kda_chunk_map(const int32_t* __restrict__ cu, int N, int T,
                                                      ChunkInfo* __restrict__ chunks,
-                                                     int32_t* __restrict__ seq_chunk0, int max_chunks) {
+                                                     int32_t* __restrict__ seq_chunk0, int max_chunks,
+                                                     int32_t* __restrict__ seq_order) {
+  constexpr int MAX_SORT = 4096;
   __shared__ int32_t part[1024];
+  __shared__ int32_t nchk[MAX_SORT];
   const int tid = threadIdx.x;
   const int per = (N + 1023) / 1024;
   const int s0 = tid * per, s1 = min(N, s0 + per);
@@ -90,12 +93,27 @@ __global__ __launch_bounds__(1024) void kda_chunk_map(const int32_t* __restrict_
     }
     chunks[j] = ci;
   }
+  // Sequences by decreasing chunk count (ties by index).  The sequential passes
+  // take their units in this order, so the longest chains start first and the
+  // shorter ones fill the compute units around them.
+  if (N <= MAX_SORT) {
+    for (int s = tid; s < N; s += 1024) nchk[s] = sc0[s + 1] - sc0[s];
+    __syncthreads();
+    for (int s = tid; s < N; s += 1024) {
+      const int ns = nchk[s];
+      int rank = 0;
+      for (int s2 = 0; s2 < N; ++s2) rank += (nchk[s2] > ns) || (nchk[s2] == ns && s2 < s);
+      seq_order[rank] = s;
+    }
+  } else {
+    for (int s = tid; s < N; s += 1024) seq_order[s] = s;
+  }
 }
 
 hipError_t launch_chunk_map(const Args& a, hipStream_t st) {
   KDA_TIMED("kda_chunk_map", st,
             hipLaunchKernelGGL(kda_chunk_map, dim3(1), dim3(1024), 0, st, a.cu, a.N, a.T, a.chunks, a.seq_chunk0,
-                               a.max_chunks));
+                               a.max_chunks, a.seq_order));
   return hipGetLastError();
 }
 
@@ -766,7 +784,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
 
   int unit, sl;
   if (!xcd_unit(blockIdx.x, NSL, a.N * a.H, unit, sl)) return;
-  const int seq = unit / a.H, h = unit % a.H, H = a.H;
+  const int seq = a.seq_order[unit / a.H], h = unit % a.H, H = a.H;   // longest sequences first
   const int n0 = sl * DVS;
   const int l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
   const int c0 = a.seq_chunk0[seq], nch = a.seq_chunk0[seq + 1] - c0;
@@ -982,7 +1000,13 @@ int device_cus() {
 // per-chunk operands for more columns at once; a grid shorter than the CU count
 // leaves CUs idle while the longest chain runs.
 int pick_dvs(int units, int dv) {
+#ifdef KDA_FORCE_DVS
+  (void)units;
+  (void)dv;
+  return KDA_FORCE_DVS;
+#else
   return (dv >= 64 && (long long)units * (dv / 64) >= device_cus()) ? 64 : 16;
+#endif
 }
 
 template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE>

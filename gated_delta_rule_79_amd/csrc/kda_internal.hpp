@@ -28,6 +28,7 @@ struct Args {
   // workspace
   ChunkInfo* chunks;        // [max_chunks]
   int32_t* seq_chunk0;      // [N + 1]
+  int32_t* seq_order;       // [N] sequences by decreasing chunk count
   void *wsW, *wsKhT, *wsQt, *wsUt, *wsAqk, *wsT;  // per (chunk, head) blocks, see WsBlock
   float* wsGam;
   // backward only (per chunk-head blocks; see WsBlock for shapes and types)
@@ -45,12 +46,14 @@ struct Args {
 // Opt-in per-kernel timing (kda_timing_enable): a no-op unless enabled.
 void timing_begin(const char* name, hipStream_t st);
 void timing_end(hipStream_t st);
+void note_launch(const char* name);   // keeps the first failing launch of this call (kda_last_error)
 
 // Bracket one launch statement with the timing hooks.
 #define KDA_TIMED(name, st, launch) \
   do {                              \
     ::kda::timing_begin(name, st);  \
     launch;                         \
+    ::kda::note_launch(name);       \
     ::kda::timing_end(st);          \
   } while (0)
 

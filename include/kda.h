@@ -119,6 +119,12 @@ kda_status kda_bwd(const kda_desc *desc, const void *q, const void *k, const voi
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);
 
+/* Which kernel launch failed, and the HIP error it gave, when the last
+ * kda_fwd/kda_bwd call on this host thread returned KDA_ERROR_LAUNCH
+ * ("" if no launch failed).  The string belongs to the library and stays
+ * valid until the thread's next kda_fwd/kda_bwd call. */
+const char *kda_last_error(void);
+
 /* Measurement support (for benchmarks and profilers; not needed to compute).
  * kda_timing_enable(1) makes every later kernel launch of kda_fwd/kda_bwd
  * record a hipEvent pair around itself on the call's stream (clearing any

@@ -28,8 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kda_bwd", "kda_fwd", "kda_status_string", "kda_timing_enable",
-                                          "kda_timing_read", "kda_workspace_bytes"])
+    assert declared_functions() == sorted(["kda_bwd", "kda_fwd", "kda_last_error", "kda_status_string",
+                                          "kda_timing_enable", "kda_timing_read", "kda_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,6 +46,15 @@ def test_status_strings(lib):
     for s in range(6):
         assert lib.kda_status_string(s)
     assert b"unknown" in lib.kda_status_string(99)
+
+
+def test_last_error_is_empty_before_any_launch(lib):
+    import threading
+    got = []
+    t = threading.Thread(target=lambda: got.append(lib.kda_last_error()))
+    t.start()
+    t.join()
+    assert got == [b""]
 
 
 def _desc(**kw):
