@@ -346,7 +346,11 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   if (ci.len <= 0) return;
   const int len = ci.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
-  const int tw = w & 3, hf = w >> 2, kq = 8 * q4;
+  // token tile tw and column half hf of this wave.  Waves w and w + 4 share a
+  // SIMD; the second half takes the tiles in reverse order, so each SIMD pairs a
+  // tile near the top of the chunk with one near the bottom and the triangular
+  // products load the four SIMDs evenly.
+  const int hf = w >> 2, tw = hf ? 3 - (w & 3) : (w & 3), kq = 8 * q4;
   const size_t blk = (size_t)j * H + h;
   const size_t rk = (size_t)H * DK, rv = (size_t)H * DV;
   const float scale = a.scale;
@@ -392,24 +396,13 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const float* gGm = a.wsG + blk * WB::G;
   O* gdV = reinterpret_cast<O*>(a.dv_) + (size_t)ci.t0 * rv + (size_t)h * DV;
 
-  // phase B's inputs (q, k, log_alpha rows) are loaded during the last quarter of phase A
+  // phase B's inputs (q, k, log_alpha rows), loaded after phase A
   TileCopy<E, CH, DK, NT> pk, pq, pl;
+  // Gamma_C of the channel whose dg_C this thread finishes in the tail (read now:
+  // a load issued after the gradient stores would wait for them to drain)
+  const float gam_c = (tid >= 64 && tid < 64 + DK) ? a.wsGam[blk * WB::GAM + tid - 64] : 0.f;
 
-  // ---- T^T -> LDS (operand type), beta
-  {
-    TileCopy<float, CH, CH, NT> tt;
-    tt.load(gT, CH);
-    static_for<0, decltype(tt)::PER>([&](auto I) __attribute__((always_inline)) {
-      const int v = tid + I * NT;
-      const int row = v / (CH / 4), c0 = (v % (CH / 4)) * 4;
-      const float* x = reinterpret_cast<const float*>(&tt.r[I]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) sTT[(c0 + u) * L::LDT + row] = cvt<OP>(x[u]);
-    });
-  }
-  if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
-
-  // ---- phase A: contractions over the value dimension
+  // ---- phase A staging: contractions over the value dimension, a quarter of the columns at a time
   struct QStage {
     TileCopy<OP, DK, QC, NT> s;
     TileCopy<float, DK, QC, NT> ds;
@@ -426,6 +419,23 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     qs.dov.load(doh + cq, rv, len);   // rows past the chunk are not read; they are zeroed on store
     qs.vv.load(vh + cq, rv, len);
   };
+
+  // ---- T^T -> LDS (operand type), beta; the first quarter's loads are in flight meanwhile
+  {
+    TileCopy<float, CH, CH, NT> tt;
+    tt.load(gT, CH);
+    qload(0);
+    static_for<0, decltype(tt)::PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = tid + I * NT;
+      const int row = v / (CH / 4), c0 = (v % (CH / 4)) * 4;
+      const float* x = reinterpret_cast<const float*>(&tt.r[I]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sTT[(c0 + u) * L::LDT + row] = cvt<OP>(x[u]);
+    });
+  }
+  if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
+
+  // ---- phase A
   f32x4 accA[2], accT[2], accQ[NKH], accK[NKH], accW[NKH];
 #pragma unroll
   for (int i = 0; i < 2; ++i) accA[i] = accT[i] = zero4();
@@ -434,7 +444,6 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   float bv[4] = {0.f, 0.f, 0.f, 0.f};
   float gp = 0.f;
 
-  qload(0);
   for (int qq = 0; qq < NQ; ++qq) {
     const int cq = qq * QC;
     __syncthreads();  // the previous quarter's LDS reads are done
@@ -774,7 +783,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     // dg_C: the last row collects sum_r dKh * Kh and dGamma_C * Gamma_C
     const int c = tid - 64;
     const float s = (sRed[c] + sRed[DK + c]) + (sRed[2 * DK + c] + sRed[3 * DK + c]);
-    sG[(CH - 1) * L::LDG + c] += s + sDGam[c] * a.wsGam[blk * WB::GAM + c];
+    sG[(CH - 1) * L::LDG + c] += s + sDGam[c] * gam_c;
   }
   __syncthreads();
   // reverse cumulative sum over rows -> dlog_alpha
