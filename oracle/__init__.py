@@ -41,6 +41,8 @@ def _bind(path: str):
     lib.kda_oracle_bwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, ctypes.c_double, P, P,
                                    P, P, P, P, P, P, P, I, I]
     lib.kda_oracle_bwd.restype = I
+    lib.kda_oracle_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, P, ctypes.c_double, P, P, P, P, P]
+    lib.kda_oracle_decode.restype = I
     return lib
 
 
@@ -131,3 +133,28 @@ def kda_bwd(q, k, v, log_alpha, beta, cu_seqlens, d_out, init_state=None, d_fina
     if rc:
         raise RuntimeError(f"kda_oracle_bwd failed: {rc}")
     return dq, dkk, dvv, dla, db, dinit
+
+
+def kda_decode(q, k, v, log_alpha, beta, state_pool, state_indices=None, num_commit=None, scale=None, lib=None):
+    """Decode / replay step in float64: (out [B,T,H,dv], new pool [P,H,dk,dv]).
+
+    q,k,log_alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; state_pool [P,H,dk,dv].
+    state_indices [B] (None: sequence b uses slot b; outside [0, P): padding, outputs 0).
+    num_commit [B] (None: all T tokens): the pool slot receives the state after that many tokens.
+    """
+    lib = lib or load()
+    q, k, v, log_alpha, beta, pool = map(_f64, (q, k, v, log_alpha, beta, state_pool))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    P = pool.shape[0]
+    idx = np.ascontiguousarray(np.arange(B) if state_indices is None else state_indices, dtype=np.int32)
+    nc = None if num_commit is None else np.ascontiguousarray(num_commit, dtype=np.int32)
+    if scale is None:
+        scale = dk ** -0.5
+    out = np.full((B, T, H, dv), np.nan)
+    new_pool = pool.copy()
+    rc = lib.kda_oracle_decode(H, dk, dv, B, T, P, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                               float(scale), _ptr(pool), _ptr(idx), _ptr(nc), _ptr(out), _ptr(new_pool))
+    if rc:
+        raise RuntimeError(f"kda_oracle_decode failed: {rc}")
+    return out, new_pool

@@ -319,3 +319,61 @@ int kda_oracle_bwd(int H, int dk, int dv, int num_seqs, const int32_t *cu_seqlen
     j.units = units; j.n_units = units ? n_units : num_seqs * H;
     return run(&j, worker_bwd, nthreads);
 }
+
+/*
+ * Decode / replay step (same page: KDA keeps a fixed-size decoding state; the
+ * section on speculative decoding replays the state-update inputs of the
+ * accepted tokens from a committed state instead of keeping a snapshot per
+ * candidate).  B sequences with T tokens each, token-major [B][T][H][.];
+ * sequence b reads its state from pool slot idx[b] (padding when idx[b] is
+ * outside [0, pool_size): outputs 0, no state touched), runs the recurrence
+ * over its T tokens writing every o_t, and the state after its first
+ * n_commit[b] tokens (clamped to [0, T]; NULL means T) is written to slot
+ * idx[b] of pool_out.  pool_out must hold a copy of pool_in on entry; slots
+ * with nothing committed keep that copy.
+ */
+int kda_oracle_decode(int H, int dk, int dv, int B, int T, int pool_size,
+                      const double *q, const double *k, const double *v, const double *log_alpha,
+                      const double *beta, double scale, const double *pool_in,
+                      const int32_t *idx, const int32_t *n_commit, double *out, double *pool_out) {
+    if (H < 1 || dk < 1 || dv < 1 || B < 0 || T < 0 || pool_size < 0) return 1;
+    if (B > 0 && T > 0 && (!q || !k || !v || !log_alpha || !beta || !out)) return 1;
+    if (B > 0 && (!pool_in || !pool_out || !idx)) return 1;
+    const size_t sz = (size_t)dk * dv;
+    double *S = malloc(sz * sizeof(double));
+    double *P = malloc(sz * sizeof(double));
+    double *delta = malloc(dv * sizeof(double));
+    if (!S || !P || !delta) {
+        free(S); free(P); free(delta);
+        return 1;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int slot = idx[b];
+        const int pad = slot < 0 || slot >= pool_size;
+        int n = n_commit ? n_commit[b] : T;
+        if (n < 0) n = 0;
+        if (n > T) n = T;
+        for (int h = 0; h < H; ++h) {
+            if (!pad) memcpy(S, pool_in + ((size_t)slot * H + h) * sz, sz * sizeof(double));
+            for (int t = 0; t < T; ++t) {
+                const size_t tok = (size_t)b * T + t;
+                const size_t rk = (tok * H + h) * dk, rv = (tok * H + h) * dv;
+                if (pad) {
+                    for (int jj = 0; jj < dv; ++jj) out[rv + jj] = 0.0;
+                    continue;
+                }
+                token_step(dk, dv, log_alpha + rk, k + rk, v + rv, beta[tok * H + h], S, P, delta);
+                for (int jj = 0; jj < dv; ++jj) {
+                    double acc = 0.0;
+                    for (int c = 0; c < dk; ++c) acc += S[c * dv + jj] * q[rk + c];
+                    out[rv + jj] = scale * acc;
+                }
+                if (t + 1 == n) memcpy(pool_out + ((size_t)slot * H + h) * sz, S, sz * sizeof(double));
+            }
+        }
+    }
+    free(S);
+    free(P);
+    free(delta);
+    return 0;
+}

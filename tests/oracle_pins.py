@@ -325,4 +325,87 @@ def pin_backward_without_final_grad(lib):
 
 
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_autograd, pin_backward_without_final_grad]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+
+
+# ---------------------------------------------------------------------------
+# decode / replay pins (state pool indexed per sequence, prefix commit)
+# ---------------------------------------------------------------------------
+def _decode_case(rng, B, T, H, dk, dv, P, unit_k=False, gate=(0.5, 1.0)):
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    la = -np.logaddexp(0.0, -rng.normal(gate[0], gate[1], (B, T, H, dk)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    pool = rng.standard_normal((P, H, dk, dv))
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, state_pool=pool)
+
+
+def _decode(lib, c, **kw):
+    return oracle.kda_decode(c["q"], c["k"], c["v"], c["log_alpha"], c["beta"], c["state_pool"], lib=lib, **kw)
+
+
+def pin_decode_brute_force(lib):
+    """Outputs of every token and the committed prefix state == explicit transition products.
+
+    Slots are gathered through the index list (a permutation with one padding
+    entry); each sequence commits a different number of its tokens."""
+    rng = np.random.default_rng(RNG_SEED + 20)
+    B, T, H, dk, dv, P = 4, 4, 2, 5, 3, 6
+    c = _decode_case(rng, B, T, H, dk, dv, P)
+    idx = np.array([3, -1, 0, 5], np.int32)
+    ncommit = np.array([4, 2, 0, 1], np.int32)
+    o, pool = _decode(lib, c, state_indices=idx, num_commit=ncommit, scale=0.41)
+    I = np.eye(dk)
+    want_pool = c["state_pool"].copy()
+    for b in range(B):
+        for h in range(H):
+            if idx[b] < 0:
+                _close(o[b, :, h], np.zeros((T, dv)), 0.0, "padding outputs")
+                continue
+            S = c["state_pool"][idx[b], h].copy()
+            for t in range(T):
+                kt, bt = c["k"][b, t, h], c["beta"][b, t, h]
+                M = (I - bt * np.outer(kt, kt)) @ np.diag(np.exp(c["log_alpha"][b, t, h]))
+                S = M @ S + bt * np.outer(kt, c["v"][b, t, h])
+                _close(o[b, t, h], 0.41 * S.T @ c["q"][b, t, h], 1e-12, f"output b={b} t={t}")
+                if t + 1 == ncommit[b]:
+                    want_pool[idx[b], h] = S
+    _close(pool, want_pool, 1e-12, "committed pool")
+
+
+def pin_decode_commit_then_replay(lib):
+    """Commit a prefix, then replay the rest from the written slot: same outputs and final state
+    as one call over all tokens; committing nothing leaves the pool bit-identical."""
+    rng = np.random.default_rng(RNG_SEED + 21)
+    B, T, H, dk, dv, P = 3, 4, 2, 4, 6, 3
+    c = _decode_case(rng, B, T, H, dk, dv, P, unit_k=True)
+    o_all, pool_all = _decode(lib, c)
+    o_none, pool_none = _decode(lib, c, num_commit=np.zeros(B, np.int32))
+    _close(pool_none, c["state_pool"], 0.0, "nothing committed")
+    _close(o_none, o_all, 0.0, "outputs do not depend on the commit count")
+    o_a, pool_a = _decode(lib, c, num_commit=np.full(B, 2, np.int32))
+    rest = {n: c[n][:, 2:] for n in ("q", "k", "v", "log_alpha", "beta")}
+    rest["state_pool"] = pool_a
+    o_b, pool_b = _decode(lib, rest)
+    _close(o_b, o_all[:, 2:], 1e-13, "replayed outputs")
+    _close(pool_b, pool_all, 1e-13, "replayed final state")
+
+
+def pin_decode_pure_decay(lib):
+    """beta = 0: the committed state is Diag(exp(sum log a)) S_0 in closed form."""
+    rng = np.random.default_rng(RNG_SEED + 22)
+    B, T, H, dk, dv, P = 2, 3, 1, 4, 2, 2
+    c = _decode_case(rng, B, T, H, dk, dv, P, gate=(1.0, 2.0))
+    c["beta"][:] = 0.0
+    o, pool = _decode(lib, c, state_indices=np.array([1, 0], np.int32))
+    for b, slot in ((0, 1), (1, 0)):
+        decay = np.exp(np.sum(c["log_alpha"][b, :, 0], axis=0))
+        _close(pool[slot, 0], decay[:, None] * c["state_pool"][slot, 0], 1e-13, "pure decay state")
+        S = np.exp(np.sum(c["log_alpha"][b, :2, 0], axis=0))[:, None] * c["state_pool"][slot, 0]
+        _close(o[b, 1, 0], dk ** -0.5 * S.T @ c["q"][b, 1, 0], 1e-13, "pure decay output")
+
+
+DECODE_PINS = [pin_decode_brute_force, pin_decode_commit_then_replay, pin_decode_pure_decay]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS

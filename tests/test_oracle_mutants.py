@@ -34,6 +34,11 @@ MUTANTS = [
     ("bwd_dq_old_state", "acc += St[c * dv + jj] * dot[jj];", "acc += Sp[c * dv + jj] * dot[jj];", 0),
     ("bwd_dk_drop_pd", "j->dk_[rk + c] = bt * gd - pd;", "j->dk_[rk + c] = bt * gd;", 0),
     ("bwd_dP_drop_rank1", "dP[c * dv + jj] = G[c * dv + jj] - kt[c] * dd[jj];", "dP[c * dv + jj] = G[c * dv + jj];", 0),
+    ("decode_commit_off_by_one", "if (t + 1 == n) memcpy(pool_out", "if (t == n) memcpy(pool_out", 0),
+    ("decode_slot_ignores_index", "const int slot = idx[b];", "const int slot = b;", 0),
+    ("decode_output_reads_old_state", "for (int c = 0; c < dk; ++c) acc += S[c * dv + jj] * q[rk + c];",
+     "for (int c = 0; c < dk; ++c) acc += P[c * dv + jj] * q[rk + c];", 0),
+    ("decode_drop_scale", "out[rv + jj] = scale * acc;", "out[rv + jj] = acc;", 0),
     ("bwd_segment_recompute_off_by_one", "const double *Sp = states + (size_t)(t - a) * sz;",
      "const double *Sp = states + (size_t)(t - a + (t > a)) * sz;", 0),
 ]
