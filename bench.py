@@ -31,7 +31,14 @@ FP32_PEAK_TFLOPS = 157.3
 METRIC = "KDA fwd(+bwd) tokens/s and % MFMA/HBM roofline, H=16 d=128 bf16, T=4K\u2013128K"
 
 CSRC = os.path.join(ROOT, "gated_delta_rule_79_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")   # training-step workload
+
+
+def traffic_file(workload):
+    """Counter summary of a workload: the training step's file, or one named after the workload."""
+    if workload.startswith("decode_"):
+        return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    return TRAFFIC_FILE
 
 
 def sources_digest():
@@ -72,6 +79,8 @@ def _short_name(name, train=True):
         return "kda_bwd_chunk"
     if "kda_chunk_map" in name:
         return "kda_chunk_map"
+    if "kda_decode_step" in name:
+        return "kda_decode_step"
     if "kda_prep" in name:
         bwd = (_bools(name) or [False])[-1]
         return ("kda_prep_save" if train else "kda_prep_bwd") if bwd else "kda_prep"
@@ -110,7 +119,7 @@ def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
                            "fetch_scale": scale_f, "write_scale": scale_w},
            "kernels": kernels}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
         f.write("\n")
     return doc
@@ -119,7 +128,7 @@ def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed counters, or None when absent or stale."""
     try:
-        doc = json.load(open(TRAFFIC_FILE))
+        doc = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if doc.get("workload") != workload or doc.get("sources_sha256") != sources_digest():
@@ -220,6 +229,83 @@ def cpu_baseline(inp, w, with_bwd):
     }
 
 
+DECODE_METRIC = "KDA decode/replay step tokens/s and % HBM roofline, H=16 d=128 bf16, fp32 state pool"
+
+
+def decode_bench(args, dev) -> int:
+    """One step = one kda_decode call: B sequences advance T tokens from pool slots and commit them."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_79_amd as kda
+    import kda_inputs as ki
+    B, T = (int(x) for x in args.decode.split(","))
+    H, dk, dv = 16, 128, 128
+    P = B
+    eout = 2 if args.out_bf16 else 4
+    odt = torch.bfloat16 if args.out_bf16 else torch.float32
+    print(f"[bench] decode inputs B={B} T={T}", file=sys.stderr, flush=True)
+    inp = ki.decode_inputs(B, T, H, dk, dv, P, dtype="bf16", seed=99)
+    idx_np = np.random.default_rng(99).permutation(P)[:B].astype(np.int32)
+    t = {n: torch.from_numpy(inp[n]).to(dev, torch.bfloat16) for n in ("q", "k", "v", "log_alpha", "beta")}
+    pool = torch.from_numpy(inp["state_pool"]).to(dev)
+    idx = torch.from_numpy(idx_np).to(dev)
+    out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
+
+    def step():
+        kda.decode(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], pool, state_indices=idx, out=out,
+                   out_dtype=odt)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} decode steps", file=sys.stderr, flush=True)
+    kda.timing_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    kt = kda.timing_read()
+    kda.timing_enable(False)
+    tot_ms, n_launch = kt["kda_decode_step"]
+    avg_ms = tot_ms / max(n_launch, 1)
+    # algorithmic bytes: each (sequence, head) state read and written once (fp32), the tokens' q, k,
+    # log_alpha, v, beta read (bf16) and outputs written, plus the index list
+    ab = B * H * (2 * dk * dv * 4 + T * (2 * (3 * dk + dv) + 2 + eout * dv)) + 4 * B
+    ach = ab / (avg_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic("kda_decode_step", f"decode_B{B}_T{T}"),
+            "kernel": "kda_decode_step", "avg_launch_ms": round(avg_ms, 5), "launches": n_launch,
+            "alg_bytes_per_launch": int(ab)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = min(B, 64)
+        t0 = time.perf_counter()
+        oracle.kda_decode(inp["q"][:nb], inp["k"][:nb], inp["v"][:nb], inp["log_alpha"][:nb], inp["beta"][:nb],
+                          inp["state_pool"], state_indices=idx_np[:nb])
+        dt_cpu = time.perf_counter() - t0
+        cpu = {"value": round(nb * T / dt_cpu, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {nb} of the {B} sequences, all {H} heads, {T} tokens each (float64, one thread), "
+                         f"{dt_cpu:.1f} s"}
+    line = {
+        "metric": DECODE_METRIC, "value": round(B * T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode_B{B}_T{T}", "sequences": B, "tokens_per_sequence": T, "H": H, "dk": dk,
+                   "dv": dv, "out_dtype": "bf16" if args.out_bf16 else "f32", "commit": "all tokens"},
+        "roofline": roof, "kernels_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in kt.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +318,9 @@ def main() -> int:
     ap.add_argument("--recompute", action="store_true",
                     help="self-contained backward (recomputes the forward) instead of the training step in which "
                          "the forward keeps the backward's intermediates")
+    ap.add_argument("--decode", default=None, metavar="B,T",
+                    help="time the decode / replay step instead: B sequences x T tokens (e.g. 512,4), H=16, "
+                         "d=128, bf16, states gathered from a pool through a permuted index list, all T committed")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -240,7 +329,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.ingest_counters:
         import kda_inputs as ki
-        doc = ingest_counters(*args.ingest_counters, copy_bytes=1024 << 20, workload=ki.config(args.config).name)
+        wl = ("decode_B{}_T{}".format(*args.decode.split(",")) if args.decode else ki.config(args.config).name)
+        doc = ingest_counters(*args.ingest_counters, copy_bytes=1024 << 20, workload=wl)
         print(json.dumps(doc["calibration"]))
         for k, v in sorted(doc["kernels"].items()):
             print(f"{k:24s} read {v['read_bytes'] / 1e9:8.3f} GB  write {v['write_bytes'] / 1e9:8.3f} GB")
@@ -272,6 +362,8 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
         return 0
     kda.load_library()
+    if args.decode:
+        return decode_bench(args, dev)
 
     w = ki.config(args.config)
     fwd_only = args.fwd_only or not w.backward

@@ -70,6 +70,8 @@ def load_library(path: str | None = None):
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_decode.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P]
+    lib.kda_decode.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_timing_enable.argtypes = [ctypes.c_int]
@@ -255,3 +257,47 @@ def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu
     if rc:
         raise KdaError("kda_bwd", rc)
     return dq, dkk, dvv, dla, db, dinit
+
+
+DECODE_MAX_TOKENS = 16   # KDA_DECODE_MAX_TOKENS (include/kda.h)
+
+
+def decode(q, k, v, log_alpha, beta, state_pool, state_indices=None, num_commit=None, scale=None,
+           out=None, out_dtype=None):
+    """Decode / replay step: advance B sequences by T tokens each from states in `state_pool`.
+
+    q, k, log_alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (float32 or bfloat16);
+    state_pool float32 [P,H,dk,dv], updated in place; state_indices int32 [B] (None: slot b;
+    outside [0, P): padding); num_commit int32 [B] (None: T): the slot receives the state after
+    that many tokens.  Returns out [B,T,H,dv] (every token's output, out_dtype default float32)."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on the GPU")
+    dt = q.dtype
+    for name, t, shape in (("k", k, (B, T, H, dk)), ("log_alpha", log_alpha, (B, T, H, dk)),
+                           ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H))):
+        _check(name, t, dt, shape, dev)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [P, H, dk, dv]")
+    _check("state_pool", state_pool, torch.float32, (state_pool.shape[0], H, dk, dv), dev)
+    for name, t in (("state_indices", state_indices), ("num_commit", num_commit)):
+        if t is not None:
+            _check(name, t, torch.int32, (B,), dev)
+    odt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
+    else:
+        _check("out", out, odt, (B, T, H, dv), dev)
+    desc = make_desc(B, T, H, dk, dv, _dtype_code(dt), 0, scale, _dtype_code(odt))
+    rc = lib.kda_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                        _ptr(state_pool), int(state_pool.shape[0]), _ptr(state_indices), _ptr(num_commit),
+                        _ptr(out), _stream(dev))
+    if rc:
+        raise KdaError("kda_decode", rc)
+    return out

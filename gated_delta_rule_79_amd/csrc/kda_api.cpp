@@ -166,6 +166,21 @@ hipError_t run_bwd(const kda_desc* d, const Args& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+hipError_t run_decode(const kda_desc* d, const kda::DecodeArgs& a, hipStream_t st) {
+  const bool bf = d->dtype == KDA_BF16, obf = d->out_dtype == KDA_BF16;
+#define KDA_CASE(DK, DV)                                                                        \
+  if (d->dk == DK && d->dv == DV)                                                               \
+    return bf ? (obf ? kda::launch_decode<bf16, bf16, DK, DV>(a, st)                            \
+                     : kda::launch_decode<bf16, float, DK, DV>(a, st))                          \
+              : kda::launch_decode<float, float, DK, DV>(a, st);
+  KDA_CASE(64, 64)
+  KDA_CASE(64, 128)
+  KDA_CASE(128, 64)
+  KDA_CASE(128, 128)
+#undef KDA_CASE
+  return hipErrorInvalidValue;
+}
+
 void base_args(Args& a, const kda_desc* d, int N, int max_chunks) {
   std::memset(&a, 0, sizeof a);
   a.B = d->B;
@@ -391,6 +406,34 @@ kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* 
   (void)hipGetLastError();
   clear_error();
   return launch_status(run_bwd(d, a, st));
+}
+
+kda_status kda_decode(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
+                      const void* beta, float* state_pool, int32_t pool_size, const int32_t* state_indices,
+                      const int32_t* num_commit, void* out, void* stream) {
+  if (!d) return KDA_ERROR_INVALID_VALUE;
+  if (!dims_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
+  if (d->B < 0 || d->T < 0 || d->T > KDA_DECODE_MAX_TOKENS || d->H < 1 || d->H > 65535) return KDA_ERROR_INVALID_VALUE;
+  if ((long long)d->B * d->T * d->H >= (1LL << 31) || (long long)d->B * d->H >= (1LL << 31)) return KDA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(d->scale) || d->flags != 0 || pool_size < 0) return KDA_ERROR_INVALID_VALUE;
+  if (d->B == 0 || d->T == 0) return KDA_SUCCESS;
+  if (!q || !k || !v || !log_alpha || !beta || !out || !state_pool) return KDA_ERROR_INVALID_VALUE;
+  if (!state_indices && pool_size < d->B) return KDA_ERROR_INVALID_VALUE;
+  const void* al16[] = {q, k, v, log_alpha, out, state_pool};
+  for (const void* p : al16)
+    if (!aligned16(p)) return KDA_ERROR_MISALIGNED;
+  if ((uintptr_t)beta % (d->dtype == KDA_BF16 ? 2 : 4)) return KDA_ERROR_MISALIGNED;
+  if (((uintptr_t)state_indices & 3u) || ((uintptr_t)num_commit & 3u)) return KDA_ERROR_MISALIGNED;
+
+  kda::DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+  a.pool = state_pool; a.idx = state_indices; a.ncommit = num_commit; a.out = out;
+  a.B = d->B; a.T = d->T; a.H = d->H; a.pool_size = pool_size;
+  a.scale = d->scale != 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
+  (void)hipGetLastError();
+  clear_error();
+  return launch_status(run_decode(d, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -43,6 +43,17 @@ struct Args {
   int out_bf16;             // outputs and gradients stored as bf16 (else fp32)
 };
 
+// Decode / replay step (kda_decode).
+struct DecodeArgs {
+  const void *q, *k, *v, *la, *beta;   // [B][T][H][.] in the input dtype
+  float* pool;                         // [pool_size][H][DK][DV], updated in place
+  const int32_t* idx;                  // [B] pool slot per sequence; null: slot b
+  const int32_t* ncommit;              // [B] tokens whose state is committed; null: T
+  void* out;                           // [B][T][H][DV] in the output dtype
+  int B, T, H, pool_size;
+  float scale;
+};
+
 // Opt-in per-kernel timing (kda_timing_enable): a no-op unless enabled.
 void timing_begin(const char* name, hipStream_t st);
 void timing_end(hipStream_t st);
@@ -63,5 +74,6 @@ int pick_dvs(int units, int dv);   // value-slice width of the sequential passes
 template <typename E, typename O, int DK, int DV> hipError_t launch_fwd(const Args& a, hipStream_t st, bool save);
 template <typename E, int DK, int DV> hipError_t launch_bwd_front(const Args& a, hipStream_t st);
 template <typename E, typename O, int DK, int DV> hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved);
+template <typename E, typename O, int DK, int DV> hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kda

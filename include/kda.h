@@ -116,6 +116,36 @@ kda_status kda_bwd(const kda_desc *desc, const void *q, const void *k, const voi
                    void *dq, void *dk, void *dv, void *dlog_alpha, void *dbeta,
                    float *d_init_state, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Decode / replay step (same page: KDA keeps a fixed-size decoding state; its
+ * section on speculative decoding keeps that state consistent after rejected
+ * draft tokens by replaying the accepted tokens' state-update inputs from a
+ * committed state, with no per-candidate snapshot).
+ *
+ * Advances B = desc->B sequences by T = desc->T tokens each (0 <= T <=
+ * KDA_DECODE_MAX_TOKENS), one token at a time, from states kept in a pool:
+ *   q, k, log_alpha : [B, T, H, dk] (desc->dtype);  v : [B, T, H, dv];  beta : [B, T, H]
+ *   out             : [B, T, H, dv] (desc->out_dtype), every token's o_t
+ *   state_pool      : float32 [pool_size, H, dk, dv], updated in place
+ *   state_indices   : int32 [B] in device memory, pool slot of each sequence;
+ *                     NULL means slot b (then pool_size >= B).  A value outside
+ *                     [0, pool_size) marks a padding entry: its outputs are
+ *                     written as 0 and no state is read or written.
+ *   num_commit      : int32 [B] in device memory, NULL meaning T for all.  The
+ *                     state after the first num_commit[b] tokens (clamped to
+ *                     [0, T]) is written back to the slot; 0 leaves it
+ *                     untouched.  Outputs always follow all T tokens.
+ * A verification pass over draft tokens commits 0; the replay of the accepted
+ * prefix commits its length (or passes only the accepted tokens).
+ * desc->num_seqs is ignored and desc->flags must be 0.  Non-padding slots must
+ * be distinct within one call (two sequences on one slot race).  No
+ * workspace: the call uses only the buffers passed in.  The 16-byte alignment
+ * rule applies to q, k, v, log_alpha, out and state_pool; state_indices and
+ * num_commit need 4-byte alignment. */
+#define KDA_DECODE_MAX_TOKENS 16
+kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const void *v,
+                      const void *log_alpha, const void *beta, float *state_pool, int32_t pool_size,
+                      const int32_t *state_indices, const int32_t *num_commit, void *out, void *stream);
+
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);
 

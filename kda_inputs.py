@@ -29,7 +29,7 @@ import zlib
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "config", "make_inputs", "bf16_round", "bf16_bits",
-           "bits_to_f32", "lengths_to_cu"]
+           "bits_to_f32", "lengths_to_cu", "decode_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -176,3 +176,25 @@ def small(dtype="f32", lengths=(100,), H=2, dk=64, dv=64, gate_mu=3.0, gate_sd=1
     return Workload(name="small", dtype=dtype, B=1, T=0, H=H, dk=dk, dv=dv, gate_mu=gate_mu,
                     gate_sd=gate_sd, init_sd=init_sd, lengths=tuple(int(x) for x in lengths),
                     backward=backward, seed=seed)
+
+
+def decode_inputs(B, T, H, dk, dv, pool_size, dtype="bf16", gate_mu=3.0, gate_sd=1.0, state_sd=0.5,
+                  seed=4321) -> dict:
+    """Inputs of a decode / replay step: B sequences of T tokens each, token-major
+    [B,T,H,.] (same value recipe as the workloads above), and a float32 state
+    pool [pool_size,H,dk,dv] ~ N(0, state_sd) standing in for states left by
+    earlier tokens."""
+    def draw(name, shape, mu=0.0, sd=1.0):
+        return _rng(seed, "decode_" + name).standard_normal(size=shape, dtype=np.float32) * np.float32(sd) \
+            + np.float32(mu)
+
+    q = _unit_rows(draw("q", (B, T, H, dk)))
+    k = _unit_rows(draw("k", (B, T, H, dk)))
+    v = draw("v", (B, T, H, dv))
+    x = draw("gate_x", (B, T, H, dk), gate_mu, gate_sd).astype(np.float64)
+    log_alpha = -np.logaddexp(0.0, -x)          # logsigmoid(x)
+    beta = 1.0 / (1.0 + np.exp(-draw("beta_logit", (B, T, H)).astype(np.float64)))
+    out = {name: np.ascontiguousarray(_store(a, dtype)) for name, a in
+           (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta))}
+    out["state_pool"] = np.ascontiguousarray(draw("state", (pool_size, H, dk, dv), 0.0, state_sd))
+    return out

@@ -28,7 +28,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kda_bwd", "kda_fwd", "kda_last_error", "kda_status_string",
+    assert declared_functions() == sorted(["kda_bwd", "kda_decode", "kda_fwd", "kda_last_error", "kda_status_string",
                                           "kda_timing_enable", "kda_timing_read", "kda_workspace_bytes"])
 
 
@@ -163,3 +163,31 @@ def test_save_for_backward_needs_the_backward_workspace(lib):
     d = _desc(flags=kda.KDA_FLAG_SAVE_FOR_BACKWARD)
     assert _fwd(lib, d, wsb=fwd_need) == S_WS
     assert _fwd(lib, d, wsb=bwd_need - 1) == S_WS
+
+
+def _dec(lib, d, q=A, out=A, pool=A, pool_size=4, idx=None, nc=None, beta=A):
+    return lib.kda_decode(ctypes.byref(d) if d is not None else None, P(q), P(A), P(A), P(A), P(beta), P(pool),
+                          pool_size, P(idx), P(nc), P(out), None)
+
+
+def test_decode_validation(lib):
+    """kda_decode rejects bad arguments before any launch; empty batches succeed without one."""
+    ok = dict(B=4, T=4, H=2, dk=128, dv=128)
+    assert _dec(lib, None) == S_INVALID
+    assert _dec(lib, _desc(**dict(ok, T=17))) == S_INVALID          # more than KDA_DECODE_MAX_TOKENS
+    assert _dec(lib, _desc(**dict(ok, T=-1))) == S_INVALID
+    assert _dec(lib, _desc(**dict(ok, B=-1))) == S_INVALID
+    assert _dec(lib, _desc(**dict(ok, flags=1))) == S_INVALID
+    assert _dec(lib, _desc(**dict(ok, dk=96))) == S_UNSUP
+    assert _dec(lib, _desc(**dict(ok, dtype=0, out_dtype=1))) == S_UNSUP
+    assert _dec(lib, _desc(**ok), pool_size=3) == S_INVALID           # slot b needs pool_size >= B
+    assert _dec(lib, _desc(**ok), pool_size=-1, idx=A) == S_INVALID
+    assert _dec(lib, _desc(**ok), out=0) == S_INVALID
+    assert _dec(lib, _desc(**ok), pool=0) == S_INVALID
+    assert _dec(lib, _desc(**ok), q=A + 8) == S_ALIGN
+    assert _dec(lib, _desc(**ok), pool=A + 4) == S_ALIGN
+    assert _dec(lib, _desc(**ok), idx=A + 2) == S_ALIGN
+    assert _dec(lib, _desc(**ok), nc=A + 1) == S_ALIGN
+    assert _dec(lib, _desc(**ok), beta=A + 1) == S_ALIGN
+    assert _dec(lib, _desc(**dict(ok, B=0)), q=0, out=0, pool=0) == S_OK
+    assert _dec(lib, _desc(**dict(ok, T=0)), q=0, out=0) == S_OK
