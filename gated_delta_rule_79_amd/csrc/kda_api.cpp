@@ -77,7 +77,7 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
   p.Aqk = take(nb * CH * CH * e);
   p.Gam = take(nb * dk * 4);
   if (bwd) {
-    p.T = take(nb * CH * CH * 4);
+    p.T = take(nb * CH * CH * e);   // operand type
     p.UtF = take(nb * dv * CH * 4);
     p.G = take(nb * CH * CH * 4);
     p.KhF = take(nb * CH * dk * 4);

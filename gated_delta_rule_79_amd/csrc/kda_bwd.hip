@@ -392,7 +392,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const float* gdS = a.wsdS + blk * WB::DS;
   const float* gU = a.wsU + blk * WB::U;
   const float* gdU = a.wsdU + blk * WB::DU;
-  const float* gT = reinterpret_cast<const float*>(a.wsT) + blk * WB::TT;
+  const OP* gT = reinterpret_cast<const OP*>(a.wsT) + blk * WB::TT;
   const float* gGm = a.wsG + blk * WB::G;
   O* gdV = reinterpret_cast<O*>(a.dv_) + (size_t)ci.t0 * rv + (size_t)h * DV;
 
@@ -422,15 +422,18 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 
   // ---- T^T -> LDS (operand type), beta; the first quarter's loads are in flight meanwhile
   {
-    TileCopy<float, CH, CH, NT> tt;
+    TileCopy<OP, CH, CH, NT> tt;
     tt.load(gT, CH);
     qload(0);
+    constexpr int EPV = 16 / (int)sizeof(OP);
     static_for<0, decltype(tt)::PER>([&](auto I) __attribute__((always_inline)) {
       const int v = tid + I * NT;
-      const int row = v / (CH / 4), c0 = (v % (CH / 4)) * 4;
-      const float* x = reinterpret_cast<const float*>(&tt.r[I]);
+      if (decltype(tt)::NV % NT == 0 || v < decltype(tt)::NV) {
+        const int row = v / (CH / EPV), c0 = (v % (CH / EPV)) * EPV;
+        const OP* x = reinterpret_cast<const OP*>(&tt.r[I]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sTT[(c0 + u) * L::LDT + row] = cvt<OP>(x[u]);
+        for (int u = 0; u < EPV; ++u) sTT[(c0 + u) * L::LDT + row] = x[u];
+      }
     });
   }
   if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
@@ -469,15 +472,32 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     qs.vv.template store_cvt<OP>(sV, L::LSV, len);
     if (qq + 1 < NQ) qload(qq + 1);
     __syncthreads();
-    // value sums of dS' * S for channel c (NT / DK parts of the quarter's columns)
+    // value sums of dS' * S for channel c (NT / DK parts of the quarter's columns; 16-byte
+    // rows where a part spans whole fragments)
     {
       constexpr int NPART = NT / DK, CPP = QC / NPART;
       const int c = tid % DK, p = tid / DK;
+      if constexpr (CPP % 8 == 0) {
 #pragma unroll
-      for (int col = p * CPP; col < (p + 1) * CPP; ++col) {
-        const int o = c * L::LSV + col;
-        const float ds = L::SPLIT ? f32(sDSh[o]) + f32(sDSl[o]) : f32(sDSh[o]);
-        gp += ds * f32(sS[o]);
+        for (int col = p * CPP; col < (p + 1) * CPP; col += 8) {
+          const Frag<OP> s8 = frag_row<OP>(sS, L::LSV, c, col);
+          const Frag<OP> h8 = frag_row<OP>(sDSh, L::LSV, c, col);
+          if constexpr (L::SPLIT) {
+            const Frag<OP> l8 = frag_row<OP>(sDSl, L::LSV, c, col);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) gp += (f32(h8.v[u]) + f32(l8.v[u])) * f32(s8.v[u]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) gp += f32(h8.v[u]) * f32(s8.v[u]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int col = p * CPP; col < (p + 1) * CPP; ++col) {
+          const int o = c * L::LSV + col;
+          const float ds = L::SPLIT ? f32(sDSh[o]) + f32(sDSl[o]) : f32(sDSh[o]);
+          gp += ds * f32(sS[o]);
+        }
       }
     }
     const Frag<OP> fdo = frag_row<OP>(sDO, L::LSV, 16 * tw + r16, kq);

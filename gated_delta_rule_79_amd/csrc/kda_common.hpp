@@ -374,7 +374,7 @@ struct WsBlock {
   static constexpr size_t QT = (size_t)CH * DK;    // Qt  [CH][DK]   OP
   static constexpr size_t UT = (size_t)DV * CH;    // U~^T[DV][CH]   OP
   static constexpr size_t AQK = (size_t)CH * CH;   // Aqk [CH][CH]   OP
-  static constexpr size_t TT = (size_t)CH * CH;    // T   [CH][CH]   float (backward only)
+  static constexpr size_t TT = (size_t)CH * CH;    // T   [CH][CH]   OP (backward only)
   static constexpr size_t GAM = DK;                // Gamma_C [DK]   float
   // backward only
   static constexpr size_t UTF = (size_t)DV * CH;   // U~^T [DV][CH]   float

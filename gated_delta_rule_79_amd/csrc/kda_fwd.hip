@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
     const int rr = o / CH, cc = o % CH;
     const float t = sT[rr * L::LDA + cc];
     sTe[rr * L::LDT + cc] = cvt<OP>(t * sBeta[cc]);
-    if constexpr (BWD) reinterpret_cast<float*>(a.wsT)[blk * WB::TT + o] = t;
+    if constexpr (BWD) reinterpret_cast<OP*>(a.wsT)[blk * WB::TT + o] = cvt<OP>(t);   // an MFMA operand only
   }
   __syncthreads();
   {
@@ -707,7 +707,8 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       const int rr = (4 * o) / CH, cc = (4 * o) % CH;
       const f32x4 t = *reinterpret_cast<const f32x4*>(sT + rr * L::LDA + cc);
       store4<OP>(sTe + rr * L::LDT + cc, t[0] * sBeta[cc], t[1] * sBeta[cc + 1], t[2] * sBeta[cc + 2], t[3] * sBeta[cc + 3]);
-      if constexpr (BWD) *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.wsT) + blk * WB::TT + rr * CH + cc) = t;
+      if constexpr (BWD)   // the backward uses T only as an MFMA operand
+        store4<OP>(reinterpret_cast<OP*>(a.wsT) + blk * WB::TT + rr * CH + cc, t[0], t[1], t[2], t[3]);
     }
     __syncthreads();
     {
