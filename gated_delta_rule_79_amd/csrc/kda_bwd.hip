@@ -308,7 +308,11 @@ struct BwdLds {
   static constexpr int LDK = DK + PE;   // E     [CH][LDK]  k, q
   static constexpr int LDO = DK + PO;   // OP    [CH][LDO]  dW, K+
   static constexpr int LDT = CH + PO;   // OP    [CH][LDT]  T, Y
-  static constexpr int LDA = CH + 4;    // float [CH][LDA]  dAqk, dT / dG
+  static constexpr int LDA = CH + 4;    // float [CH][LDA]  dT
+  using SE = typename std::conditional<sizeof(E) == 4, float, bf16>::type;   // gated-product operands
+  static constexpr bool SSPLIT = sizeof(SE) == 2;
+  static constexpr int LDQ = CH + PADE<SE>;   // SE [..][LDQ]  split dAqk / dG rows, decayed q/k tables
+  static constexpr int LDR = CH + 4;          // float [..][LDR]  decayed k table
   static constexpr size_t G = 0;
   static constexpr size_t K = G + (size_t)CH * LDG * 4;
   static constexpr size_t Q = K + (size_t)CH * LDK * sizeof(E);
@@ -316,9 +320,12 @@ struct BwdLds {
   static constexpr size_t UNION = A_END > B_END ? A_END : B_END;
   // both phases
   static constexpr size_t T = UNION;                                  // OP    [CH][LDT]  T^T
-  static constexpr size_t A1 = T + (size_t)CH * LDT * OPB;            // float [CH][LDA]  scale tril(dO U^T)
-  static constexpr size_t A2 = A1 + (size_t)CH * LDA * 4;             // float [CH][LDA]  dT, then dG
-  static constexpr size_t DW = A2 + (size_t)CH * LDA * 4;             // OP    [CH][LDO]  dW (Y after it is dead)
+  static constexpr size_t QSZ = (size_t)CH * LDQ * sizeof(SE);       // one SE [CH][LDQ] array
+  static constexpr size_t A1 = T + (size_t)CH * LDT * OPB;            // SE hi, lo [CH][LDQ]  scale tril(dO U^T)
+  static constexpr size_t A2 = A1 + (SSPLIT ? 2 : 1) * QSZ;           // float [CH][LDA] dT, then SE hi, lo dG
+  static constexpr size_t A2SZ = (size_t)CH * LDA * 4 > (SSPLIT ? 2 : 1) * QSZ ? (size_t)CH * LDA * 4
+                                                                              : (SSPLIT ? 2 : 1) * QSZ;
+  static constexpr size_t DW = A2 + A2SZ;                             // OP    [CH][LDO]  dW (Y after it is dead)
   static constexpr size_t KP = DW + (size_t)CH * LDO * OPB;           // OP    [CH][LDO]  K+
   static constexpr size_t BETA = KP + (size_t)CH * LDO * OPB;         // float [CH]
   static constexpr size_t RED = BETA + CH * 4;                        // float [512]  scan / column-sum partials
@@ -326,9 +333,24 @@ struct BwdLds {
   static constexpr size_t DGAM = GAMP + 512 * 4;                      // float [DK]
   static constexpr size_t BV = DGAM + DK * 4;                         // float [2][CH] rowsum(V * T^T dU) halves
   static constexpr size_t DBP = BV + 2 * CH * 4;                      // float [2][CH] dbeta halves
-  static constexpr size_t BYTES = DBP + 2 * CH * 4;
+  static constexpr size_t END0 = DBP + 2 * CH * 4;
   static constexpr size_t Y = DW;                                     // OP [CH][LDT]
   static_assert(LDT <= LDO, "Y fits in the dW region");
+  // gated products, per pass of 32 channels: decayed q and k tables (split SE,
+  // [channel][token]) and the decayed-k table for the row side (float,
+  // [channel][token]).  They reuse the dW and K+ regions (dead by then) where
+  // those are large enough (dk = 128), else they follow the rest.
+  static constexpr int TC = 32;
+  static constexpr size_t TQSZ = (size_t)TC * LDQ * sizeof(SE);
+  static constexpr size_t TAB_SZ = 2 * (SSPLIT ? 2 : 1) * TQSZ + (size_t)TC * LDR * 4;
+  static constexpr bool TAB_REUSE = TAB_SZ <= 2 * (size_t)CH * LDO * OPB;
+  static constexpr size_t QCH = TAB_REUSE ? DW : END0;
+  static constexpr size_t QCL = QCH + TQSZ;                             // lo halves: split types only
+  static constexpr size_t KCH = QCH + (SSPLIT ? 2 : 1) * TQSZ;
+  static constexpr size_t KCL = KCH + TQSZ;
+  static constexpr size_t KR = KCH + (SSPLIT ? 2 : 1) * TQSZ;
+  static constexpr size_t BYTES = TAB_REUSE ? END0 : END0 + TAB_SZ;
+  static_assert(KR % 16 == 0 && KCH % 16 == 0 && QCH % 16 == 0, "table rows stay 16-byte aligned");
   static_assert(BYTES <= 163840, "backward chunk kernel LDS");
   static_assert(A_END % 16 == 0 && B_END % 16 == 0, "LDS regions stay 16-byte aligned");
 };
@@ -338,7 +360,6 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   using L = BwdLds<E, DK, DV>;
   using OP = typename L::OP;
   using WB = WsBlock<E, DK, DV>;
-  using SE = typename std::conditional<sizeof(E) == 4, float, bf16>::type;   // gated products: split bf16
   constexpr int NT = 512, NKT = DK / 16, NKH = NKT / 2, QC = L::QC, NQ = DV / QC;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int j = blockIdx.x, h = blockIdx.y, H = a.H;
@@ -370,8 +391,27 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   E* sK = reinterpret_cast<E*>(smem + L::K);
   E* sQ = reinterpret_cast<E*>(smem + L::Q);
   OP* sTT = reinterpret_cast<OP*>(smem + L::T);   // T^T: sTT[i][r] = T[r][i]
-  float* sA1 = reinterpret_cast<float*>(smem + L::A1);
-  float* sA2 = reinterpret_cast<float*>(smem + L::A2);
+  using SE = typename L::SE;   // gated-product operands: split bf16 (fp32 on the fp32 path)
+  SE* sA1h = reinterpret_cast<SE*>(smem + L::A1);   // scale tril(dO U^T), split
+  SE* sA1l = sA1h + CH * L::LDQ;
+  float* sA2 = reinterpret_cast<float*>(smem + L::A2);   // dT
+  SE* sA2h = reinterpret_cast<SE*>(smem + L::A2);   // dG, split (after dT is dead)
+  SE* sA2l = sA2h + CH * L::LDQ;
+  SE* tQh = reinterpret_cast<SE*>(smem + L::QCH);
+  SE* tQl = reinterpret_cast<SE*>(smem + L::QCL);
+  SE* tKh = reinterpret_cast<SE*>(smem + L::KCH);
+  SE* tKl = reinterpret_cast<SE*>(smem + L::KCL);
+  float* tKR = reinterpret_cast<float*>(smem + L::KR);
+  // x as a split pair hi + lo (hi only on the fp32 path)
+  auto put_split = [&](SE* hi, SE* lo, int idx, float x) __attribute__((always_inline)) {
+    if constexpr (L::SSPLIT) {
+      const SE hv = (SE)x;
+      hi[idx] = hv;
+      lo[idx] = (SE)(x - (float)hv);
+    } else {
+      hi[idx] = x;
+    }
+  };
   OP* sDW = reinterpret_cast<OP*>(smem + L::DW);
   OP* sY = reinterpret_cast<OP*>(smem + L::Y);
   OP* sKp = reinterpret_cast<OP*>(smem + L::KP);
@@ -550,7 +590,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int cc = 16 * (2 * hf + jj) + r16;
-      sA1[rr * L::LDA + cc] = cc <= rr ? scale * accA[jj][ii] : 0.f;
+      put_split(sA1h, sA1l, rr * L::LDQ + cc, cc <= rr ? scale * accA[jj][ii] : 0.f);
     }
 #pragma unroll
     for (int jj = 0; jj < NKH; ++jj) sDW[rr * L::LDO + 16 * (hf * NKH + jj) + r16] = cvt<OP>(-accW[jj][ii]);
@@ -661,97 +701,106 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;
       const float da = cc < rr ? -x[ii] : 0.f;
       dbeta[ii] += da * gGram[jj][ii];
-      sA2[rr * L::LDA + cc] = sBeta[rr] * da;
+      put_split(sA2h, sA2l, rr * L::LDQ + cc, sBeta[rr] * da);
     }
   }
   __syncthreads();
 
   // ---- per channel tile of half hf: gated products, then the assembly of dq, dk, dg.
-  // Gated products use per-block reference rows (split bf16 operands):
-  // row side, block a = tw: dq_g = e^{g_r - g_m} (dAqk . R_a), dkp_g = e^{g_r - g_m} (dG . R_a),
-  // R_a[i] = k_i e^{g_m - g_i}; column side, block b = tw:
-  // dkm = sum_{a >= b} e^{g_m(a) - g_i} ((dAqk_a^T q_a + dG_a^T k_a) e^{g_a - g_m(a)})
+  // Decayed products use per-block reference rows m(b) = 16b + 8 (split bf16 operands):
+  // row side, block a = tw: dq_g = e^{g_r - g_m(a)} (dAqk . R_a), dkp_g = e^{g_r - g_m(a)} (dG . R_a),
+  // R_a[i] = k_i e^{g_m(a) - g_i}; column side, block b = tw:
+  // dkm = e^{g_m(b) - g_i} sum_{a >= b} e^{g_m(a) - g_m(b)} (dAqk_a^T q~_a + dG_a^T k~_a),
+  // q~_r = q_r e^{g_r - g_m(blk r)}, k~ likewise.  One pass per channel tile: the pass's
+  // 32 channels (tile jj of both halves) get tables of q~, k~ (split, [channel][token]) and
+  // k_i e^{g_m(blk i) - g_i} (fp32), so every operand is a 16-byte LDS row read and the
+  // exponentials are taken once per element and pass.
   O* dqo = reinterpret_cast<O*>(a.dq) + (size_t)ci.t0 * rk + (size_t)h * DK;
   O* dko = reinterpret_cast<O*>(a.dk_) + (size_t)ci.t0 * rk + (size_t)h * DK;
   O* dlo = reinterpret_cast<O*>(a.dla) + (size_t)ci.t0 * rk + (size_t)h * DK;
   float dgv[NKH][4];
   float khs[NKH];   // column sums over this lane's rows of dKh * Kh (for dg_C)
-  // TP channel tiles per pass share the split dAqk / dG fragments
-  constexpr int TP = 2;
-#pragma unroll
-  for (int jp = 0; jp < NKH; jp += TP) {
-    f32x4 dqg[TP], dkpg[TP], dkm[TP];
-    int ccs[TP];
-#pragma unroll
-    for (int t = 0; t < TP; ++t) {
-      dqg[t] = dkpg[t] = dkm[t] = zero4();
-      ccs[t] = 16 * (hf * NKH + jp + t) + r16;
-    }
+  constexpr int TC = L::TC;
+  static_assert(TC == 2 * 16 && NT == TC * (CH / 4), "table build: one thread per (channel, 4 tokens)");
+  // (dk = 128 keeps the pass loop rolled: unrolled, it no longer fits the registers)
+#pragma unroll(DK == 128 ? 1 : NKH)
+  for (int jj = 0; jj < NKH; ++jj) {
+    if (jj > 0) __syncthreads();   // the previous pass's table reads are done
     {
-      const int ab = tw, ref = 16 * ab + 8;
-      const int kmax = 16 * (ab + 1);  // columns i < kmax can be nonzero
+      const int cl = tid % TC, r0 = 4 * (tid / TC);
+      const int c = 16 * ((cl >> 4) * NKH + jj) + (cl & 15);   // channel tile jj of half cl >> 4
+      const float gm = sG[(16 * (r0 >> 4) + 8) * L::LDG + c];
+      float kr[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u;
+        const float g = sG[r * L::LDG + c];
+        const float e = __expf(g - gm);
+        const float kv = f32(sK[r * L::LDK + c]);
+        put_split(tQh, tQl, cl * L::LDQ + r, f32(sQ[r * L::LDK + c]) * e);
+        put_split(tKh, tKl, cl * L::LDQ + r, kv * e);
+        kr[u] = kv * __expf(gm - g);
+      }
+      *reinterpret_cast<f32x4*>(tKR + cl * L::LDR + r0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+    }
+    __syncthreads();
+    const int cl = 16 * hf + r16, cc = 16 * (hf * NKH + jj) + r16;
+    f32x4 dqg = zero4(), dkpg = zero4(), dkm = zero4();
+    {
+      const int ab = tw, kmax = 16 * (ab + 1);   // columns i < kmax can be nonzero
+      const float gma = sG[(16 * ab + 8) * L::LDG + cc];
       for (int k = 0; k < kmax; k += 32) {
-        const SFrag<SE> fa1 = sfrag_row<SE>(sA1, L::LDA, 16 * ab + r16, k + kq);
-        const SFrag<SE> fa2 = sfrag_row<SE>(sA2, L::LDA, 16 * ab + r16, k + kq);
+        const SFrag<SE> fa1 = sfrag_pair<SE>(sA1h, sA1l, L::LDQ, 16 * ab + r16, k + kq);
+        const SFrag<SE> fa2 = sfrag_pair<SE>(sA2h, sA2l, L::LDQ, 16 * ab + r16, k + kq);
+        const int i0 = k + kq, bb = i0 >> 4;
+        float xr[8];
+        if (i0 < kmax) {
+          const float f = bb == ab ? 1.f : __expf(gma - sG[(16 * bb + 8) * L::LDG + cc]);
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + cl * L::LDR + i0);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(tKR + cl * L::LDR + i0 + 4);
 #pragma unroll
-        for (int t = 0; t < TP; ++t) {
-          const int cc = ccs[t];
-          const float gref = sG[ref * L::LDG + cc];
-          float xr[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int i = k + kq + u;
-            xr[u] = i < kmax ? f32(sK[i * L::LDK + cc]) * __expf(gref - sG[i * L::LDG + cc]) : 0.f;
+          for (int u = 0; u < 4; ++u) {
+            xr[u] = v0[u] * f;
+            xr[u + 4] = v1[u] * f;
           }
-          const SFrag<SE> fr = sfrag_from<SE>(xr);
-          dqg[t] = mma_ss(fa1, fr, dqg[t]);
-          dkpg[t] = mma_ss(fa2, fr, dkpg[t]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) xr[u] = 0.f;
         }
+        const SFrag<SE> fr = sfrag_from<SE>(xr);
+        dqg = mma_ss(fa1, fr, dqg);
+        dkpg = mma_ss(fa2, fr, dkpg);
       }
 #pragma unroll
-      for (int t = 0; t < TP; ++t) {
-        const int cc = ccs[t];
-        const float gref = sG[ref * L::LDG + cc];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gref);
-          dqg[t][ii] *= e;
-          dkpg[t][ii] *= e;
-        }
+      for (int ii = 0; ii < 4; ++ii) {
+        const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gma);
+        dqg[ii] *= e;
+        dkpg[ii] *= e;
       }
     }
     {
       const int b = tw;
+      const float gmb = sG[(16 * b + 8) * L::LDG + cc];
+      // A[m = i][k = r'] : r' < 16 -> dAqk[16a + r'][i], r' >= 16 -> dG[16a + r' - 16][i];
+      // B[k = r'][n] : q~ rows of block a for r' < 16, k~ rows for r' >= 16
+      const SE* aH = q4 < 2 ? sA1h : sA2h;
+      const SE* aL = q4 < 2 ? sA1l : sA2l;
+      const SE* bH = q4 < 2 ? tQh : tKh;
+      const SE* bL = q4 < 2 ? tQl : tKl;
       for (int ab = b; ab < 4; ++ab) {
-        const int ref = 16 * ab + 8;
-        // A[m = i][k = r'] : r' < 16 -> dAqk[16a + r'][i], r' >= 16 -> dG[16a + r' - 16][i]
-        const float* srcA = q4 < 2 ? sA1 : sA2;
         const int rbase = 16 * ab + 8 * (q4 & 1);
-        const SFrag<SE> fa = sfrag_col_f32<SE>(srcA, L::LDA, 16 * b + r16, rbase);
+        const SFrag<SE> fa = sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase);
+        const SFrag<SE> fb = sfrag_pair<SE>(bH, bL, L::LDQ, cl, rbase);
+        const f32x4 y = mma_ss(fa, fb, zero4());
+        const float f = ab == b ? 1.f : __expf(sG[(16 * ab + 8) * L::LDG + cc] - gmb);
 #pragma unroll
-        for (int t = 0; t < TP; ++t) {
-          const int cc = ccs[t];
-          const float gref = sG[ref * L::LDG + cc];
-          float xl8[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int rr = rbase + u;
-            const float src = q4 < 2 ? f32(sQ[rr * L::LDK + cc]) : f32(sK[rr * L::LDK + cc]);
-            xl8[u] = src * __expf(sG[rr * L::LDG + cc] - gref);
-          }
-          const f32x4 y = mma_ss(fa, sfrag_from<SE>(xl8), zero4());
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int i = 16 * b + 4 * q4 + ii;
-            dkm[t][ii] += __expf(gref - sG[i * L::LDG + cc]) * y[ii];
-          }
-        }
+        for (int ii = 0; ii < 4; ++ii) dkm[ii] += f * y[ii];
       }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) dkm[ii] *= __expf(gmb - sG[(16 * b + 4 * q4 + ii) * L::LDG + cc]);
     }
     // assembly (rows 16tw + 4q4 + ii)
-#pragma unroll
-    for (int t = 0; t < TP; ++t) {
-      const int jj = jp + t, cc = ccs[t];
+    {
       khs[jj] = 0.f;
       const float gl = sG[(CH - 1) * L::LDG + cc];
 #pragma unroll
@@ -760,9 +809,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         const float g = sG[rr * L::LDG + cc];
         const float eg = __expf(g);
         const float kv = f32(sK[rr * L::LDK + cc]), qv = f32(sQ[rr * L::LDK + cc]);
-        const float dq = eg * scale * accQ[jj][ii] + dqg[t][ii];
-        const float dkp = eg * sBeta[rr] * tdw[jj][ii] + dkpg[t][ii];
-        const float dkmv = dkm[t][ii];
+        const float dq = eg * scale * accQ[jj][ii] + dqg[ii];
+        const float dkp = eg * sBeta[rr] * tdw[jj][ii] + dkpg[ii];
+        const float dkmv = dkm[ii];
         const float dkh = __expf(gl - g) * accK[jj][ii];
         dgv[jj][ii] = dq * qv + (dkp - dkmv - dkh) * kv;
         khs[jj] += dkh * kv;
