@@ -158,3 +158,74 @@ def kda_decode(q, k, v, log_alpha, beta, state_pool, state_indices=None, num_com
     if rc:
         raise RuntimeError(f"kda_oracle_decode failed: {rc}")
     return out, new_pool
+
+
+# ---------------------------------------------------------------------------
+# Fused input preparation (the step upstream of the recurrence in the same
+# page's KDA workloads): q and k are L2-normalised per (token, head) over the
+# key channels, and the decay comes from a raw gate x as log alpha =
+# logsigmoid(x).  The pages fix neither an epsilon nor the gate's
+# parametrisation beyond that form; the library's reading is
+#     l2n(x) = x / sqrt(sum(x^2) + L2N_EPS),   log alpha = -log(1 + exp(-x)).
+# The functions below compose those maps with kda_fwd / kda_bwd / kda_decode
+# in float64, and take the backward through them by the chain rule:
+#     d raw_q = s (d q^ - q^ (q^ . d q^)),  s = (sum(q^2) + eps)^-1/2
+#     d x     = d log_alpha * sigmoid(-x)
+# ---------------------------------------------------------------------------
+L2N_EPS = 1e-6
+
+
+def l2n(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2N_EPS)
+
+
+def l2n_backward(x, g):
+    """Gradient with respect to x of <g, l2n(x)>."""
+    x = np.asarray(x, dtype=np.float64)
+    s = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2N_EPS)
+    xh = x * s
+    return s * (g - xh * np.sum(xh * g, axis=-1, keepdims=True))
+
+
+def logsigmoid(x):
+    return -np.logaddexp(0.0, -np.asarray(x, dtype=np.float64))
+
+
+def logsigmoid_backward(x, g):
+    """Gradient with respect to x of <g, logsigmoid(x)>."""
+    return np.asarray(g, dtype=np.float64) * np.exp(logsigmoid(-np.asarray(x, dtype=np.float64)))
+
+
+def _prep(q, k, gate, qk_l2norm, gate_logsigmoid):
+    return (l2n(q) if qk_l2norm else q, l2n(k) if qk_l2norm else k,
+            logsigmoid(gate) if gate_logsigmoid else gate)
+
+
+def kda_fwd_prepped(q, k, v, gate, beta, cu_seqlens, init_state=None, scale=None, qk_l2norm=True,
+                    gate_logsigmoid=True, units=None, nthreads=None, lib=None):
+    """kda_fwd on l2n(q), l2n(k) and log alpha = logsigmoid(gate) (each map only when asked)."""
+    qh, kh, la = _prep(q, k, gate, qk_l2norm, gate_logsigmoid)
+    return kda_fwd(qh, kh, v, la, beta, cu_seqlens, init_state=init_state, scale=scale, units=units,
+                   nthreads=nthreads, lib=lib)
+
+
+def kda_bwd_prepped(q, k, v, gate, beta, cu_seqlens, d_out, init_state=None, d_final_state=None, scale=None,
+                    qk_l2norm=True, gate_logsigmoid=True, units=None, nthreads=None, lib=None):
+    """Gradients with respect to the raw q, k and gate (and v, beta, init_state) of the prepped forward."""
+    qh, kh, la = _prep(q, k, gate, qk_l2norm, gate_logsigmoid)
+    dq, dk, dv, dla, db, dinit = kda_bwd(qh, kh, v, la, beta, cu_seqlens, d_out, init_state=init_state,
+                                         d_final_state=d_final_state, scale=scale, units=units,
+                                         nthreads=nthreads, lib=lib)
+    if qk_l2norm:
+        dq, dk = l2n_backward(q, dq), l2n_backward(k, dk)
+    if gate_logsigmoid:
+        dla = logsigmoid_backward(gate, dla)
+    return dq, dk, dv, dla, db, dinit
+
+
+def kda_decode_prepped(q, k, v, gate, beta, state_pool, state_indices=None, num_commit=None, scale=None,
+                       qk_l2norm=True, gate_logsigmoid=True, lib=None):
+    qh, kh, la = _prep(q, k, gate, qk_l2norm, gate_logsigmoid)
+    return kda_decode(qh, kh, v, la, beta, state_pool, state_indices=state_indices, num_commit=num_commit,
+                      scale=scale, lib=lib)

@@ -408,4 +408,83 @@ def pin_decode_pure_decay(lib):
 
 
 DECODE_PINS = [pin_decode_brute_force, pin_decode_commit_then_replay, pin_decode_pure_decay]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS
+
+
+# ---------------------------------------------------------------------------
+# fused input preparation: raw q, k (L2-normalised inside) and a raw gate x
+# (log alpha = logsigmoid(x) inside)
+# ---------------------------------------------------------------------------
+def _raw_case(rng, lengths, H, dk, dv):
+    c = _rand_case(rng, lengths, H, dk, dv, unit_k=False, gate=(0.5, 1.5))
+    c["q"] *= rng.uniform(0.5, 3.0, size=c["q"].shape[:2] + (1,))
+    c["k"] *= rng.uniform(0.5, 3.0, size=c["k"].shape[:2] + (1,))
+    c["gate"] = rng.normal(1.0, 2.0, c["log_alpha"].shape)
+    return c
+
+
+def _fused_loss(lib, c, dO, dS):
+    o, fin = oracle.kda_fwd_prepped(c["q"], c["k"], c["v"], c["gate"], c["beta"], c["cu_seqlens"],
+                                    init_state=c["init_state"], scale=0.6, nthreads=1, lib=lib)
+    return float(np.sum(o * dO) + np.sum(fin * dS))
+
+
+def pin_fused_prep_finite_differences(lib):
+    """Gradients with respect to the raw q, k and gate == central differences of the composed forward."""
+    rng = np.random.default_rng(RNG_SEED + 30)
+    c = _raw_case(rng, [5, 3], H=1, dk=4, dv=3)
+    dO = rng.standard_normal(c["v"].shape)
+    dS = rng.standard_normal(c["init_state"].shape)
+    g = oracle.kda_bwd_prepped(c["q"], c["k"], c["v"], c["gate"], c["beta"], c["cu_seqlens"], dO,
+                               init_state=c["init_state"], d_final_state=dS, scale=0.6, nthreads=1, lib=lib)
+    h = 1e-6
+    for name, grad in (("q", g[0]), ("k", g[1]), ("gate", g[3])):
+        x = c[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _fused_loss(lib, c, dO, dS)
+            x[idx] = old - h
+            lm = _fused_loss(lib, c, dO, dS)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        _close(grad, num, 1e-6, f"d{name} vs central differences")
+
+
+def pin_fused_prep_row_scale_invariance(lib):
+    """Scaling a token's q or k row up by c >= 1 changes nothing but the epsilon term (relative <= 1e-6 / |row|^2)."""
+    rng = np.random.default_rng(RNG_SEED + 31)
+    c = _raw_case(rng, [9], H=2, dk=6, dv=4)
+    o1, f1 = oracle.kda_fwd_prepped(c["q"], c["k"], c["v"], c["gate"], c["beta"], c["cu_seqlens"],
+                                    init_state=c["init_state"], lib=lib)
+    sc = rng.uniform(2.0, 50.0, size=c["q"].shape[:2] + (1,))
+    sc2 = rng.uniform(2.0, 50.0, size=c["q"].shape[:2] + (1,))
+    o2, f2 = oracle.kda_fwd_prepped(c["q"] * sc, c["k"] * sc2, c["v"], c["gate"], c["beta"], c["cu_seqlens"],
+                                    init_state=c["init_state"], lib=lib)
+    _close(o2, o1, 1e-4, "outputs under row scaling")
+    _close(f2, f1, 1e-4, "final state under row scaling")
+
+
+def pin_fused_prep_gate_limits(lib):
+    """A saturated gate (x = 40) is no decay: equal to the plain recurrence with log alpha = 0 and
+    unit-normalised rows; with beta = 0 the state decays by the product of sigmoid(x) exactly."""
+    rng = np.random.default_rng(RNG_SEED + 32)
+    c = _raw_case(rng, [7], H=1, dk=4, dv=3)
+    c["gate"][:] = 40.0
+    o1, f1 = oracle.kda_fwd_prepped(c["q"], c["k"], c["v"], c["gate"], c["beta"], c["cu_seqlens"],
+                                    init_state=c["init_state"], qk_l2norm=False, lib=lib)
+    o2, f2 = oracle.kda_fwd(c["q"], c["k"], c["v"], np.zeros_like(c["gate"]), c["beta"], c["cu_seqlens"],
+                            init_state=c["init_state"], lib=lib)
+    _close(o1, o2, 1e-12, "saturated gate outputs")
+    _close(f1, f2, 1e-12, "saturated gate state")
+    c = _raw_case(rng, [6], H=1, dk=4, dv=3)
+    c["beta"][:] = 0.0
+    _, f = oracle.kda_fwd_prepped(c["q"], c["k"], c["v"], c["gate"], c["beta"], c["cu_seqlens"],
+                                  init_state=c["init_state"], lib=lib)
+    decay = np.prod(1.0 / (1.0 + np.exp(-c["gate"][:, 0])), axis=0)
+    _close(f[0, 0], decay[:, None] * c["init_state"][0, 0], 1e-13, "pure decay by sigmoid products")
+
+
+FUSED_PREP_PINS = [pin_fused_prep_finite_differences, pin_fused_prep_row_scale_invariance,
+                   pin_fused_prep_gate_limits]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS + FUSED_PREP_PINS
