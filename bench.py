@@ -203,20 +203,22 @@ def kernel_alg_flops(name, w, tokens):
     return per * tokens * w.H
 
 
-def cpu_baseline(inp, w, with_bwd):
-    """The float64 oracle (untuned) on a bounded sample: heads 0-1 of every sequence, fwd (+bwd)."""
+def cpu_baseline(inp, w, with_bwd, prepped=False):
+    """The float64 oracle (untuned) on a bounded sample: heads 0-1 of every sequence, fwd (+bwd).
+    prepped: the inputs are raw and the oracle applies the same input preparation."""
     import oracle
     n_seq = len(inp["lengths"])
     heads = [0, 1]
     units = [(s, h) for h in heads for s in range(n_seq)]
     threads = oracle.default_threads()
+    fwd = oracle.kda_fwd_prepped if prepped else oracle.kda_fwd
+    bwd = oracle.kda_bwd_prepped if prepped else oracle.kda_bwd
     t0 = time.perf_counter()
-    oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"],
-                   init_state=inp["init_state"], units=units, nthreads=threads)
+    fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"],
+        init_state=inp["init_state"], units=units, nthreads=threads)
     if with_bwd:
-        oracle.kda_bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"], inp["d_out"],
-                       init_state=inp["init_state"], d_final_state=inp["d_final_state"], units=units,
-                       nthreads=threads)
+        bwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"], inp["d_out"],
+            init_state=inp["init_state"], d_final_state=inp["d_final_state"], units=units, nthreads=threads)
     dt = time.perf_counter() - t0
     token_heads = sum(inp["lengths"]) * len(heads)
     return {
@@ -318,6 +320,8 @@ def main() -> int:
     ap.add_argument("--recompute", action="store_true",
                     help="self-contained backward (recomputes the forward) instead of the training step in which "
                          "the forward keeps the backward's intermediates")
+    ap.add_argument("--fused-prep", action="store_true",
+                    help="raw q, k and gate inputs: L2 norm and logsigmoid inside the kernels (forward and backward)")
     ap.add_argument("--decode", default=None, metavar="B,T",
                     help="time the decode / replay step instead: B sequences x T tokens (e.g. 512,4), H=16, "
                          "d=128, bf16, states gathered from a pool through a permuted index list, all T committed")
@@ -368,7 +372,8 @@ def main() -> int:
     w = ki.config(args.config)
     fwd_only = args.fwd_only or not w.backward
     print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
-    inp = ki.make_inputs(w, with_grads=not fwd_only)
+    inp = ki.make_inputs(w, with_grads=not fwd_only, raw=args.fused_prep)
+    prep = dict(qk_l2norm=True, gate_logsigmoid=True) if args.fused_prep else {}
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     odt = torch.bfloat16 if args.out_bf16 else torch.float32
     t = {k: torch.from_numpy(inp[k]).to(dev, dt).unsqueeze(0) for k in ("q", "k", "v", "log_alpha", "beta")}
@@ -388,7 +393,7 @@ def main() -> int:
         d_fin = torch.from_numpy(inp["d_final_state"]).to(dev)
     B, T = t["q"].shape[0], t["q"].shape[1]
     ws = torch.empty(kda.workspace_bytes(B, T, w.H, w.dk, w.dv, dt, num_seqs=n_seqs if varlen else 0,
-                                         backward=not fwd_only), dtype=torch.uint8, device=dev)
+                                         backward=not fwd_only, **prep), dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, w.H, w.dv), dtype=odt, device=dev)
     fin = torch.empty((n_seqs, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     grads = None
@@ -401,10 +406,10 @@ def main() -> int:
 
     def step():
         kda.fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], init_state=init, cu_seqlens=cu, out=out,
-                final_state=fin, workspace=ws, out_dtype=odt, save_for_backward=train)
+                final_state=fin, workspace=ws, out_dtype=odt, save_for_backward=train, **prep)
         if not fwd_only:
             kda.bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], d_out, init_state=init, d_final_state=d_fin,
-                    cu_seqlens=cu, workspace=ws, out_dtype=odt, grads=grads, d_init=dinit, use_saved=train)
+                    cu_seqlens=cu, workspace=ws, out_dtype=odt, grads=grads, d_init=dinit, use_saved=train, **prep)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -457,7 +462,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp, w, not fwd_only)
+        cpu = cpu_baseline(inp, w, not fwd_only, prepped=args.fused_prep)
 
     line = {
         "metric": METRIC,
@@ -475,7 +480,8 @@ def main() -> int:
         "config": {"workload": w.name, "tokens": tokens, "sequences": n_seqs, "H": w.H, "dk": w.dk, "dv": w.dv,
                    "out_dtype": "bf16" if args.out_bf16 else "f32", "pass": "fwd" if fwd_only else "fwd+bwd",
                    "backward": None if fwd_only else ("recomputes the forward" if args.recompute
-                                                      else "uses the forward's saved intermediates")},
+                                                      else "uses the forward's saved intermediates"),
+                   "input_prep": "fused (raw q, k, gate)" if args.fused_prep else "inputs already prepared"},
         "roofline": roof,
         "step_roofline": step_roof,
         "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in kt.items()},

@@ -28,6 +28,11 @@ _lib = None
 KDA_F32, KDA_BF16 = 0, 1
 KDA_ERROR_LAUNCH = 5   # kda_status value of a failed kernel launch (include/kda.h)
 KDA_FLAG_SAVE_FOR_BACKWARD, KDA_FLAG_USE_SAVED = 1, 2   # kda_desc.flags bits (include/kda.h)
+KDA_FLAG_QK_L2NORM, KDA_FLAG_GATE_LOGSIGMOID = 4, 8     # fused input preparation
+
+
+def _prep_flags(qk_l2norm, gate_logsigmoid):
+    return (KDA_FLAG_QK_L2NORM if qk_l2norm else 0) | (KDA_FLAG_GATE_LOGSIGMOID if gate_logsigmoid else 0)
 
 
 class kda_desc(ctypes.Structure):
@@ -131,10 +136,11 @@ def make_desc(B, T, H, dk, dv, dtype_code, num_seqs=0, scale=None, out_code=KDA_
                     float(scale) if scale else 0.0, int(flags))
 
 
-def workspace_bytes(B, T, H, dk, dv, dtype, num_seqs=0, backward=False) -> int:
+def workspace_bytes(B, T, H, dk, dv, dtype, num_seqs=0, backward=False, qk_l2norm=False,
+                    gate_logsigmoid=False) -> int:
     import torch
     code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
-    d = make_desc(B, T, H, dk, dv, code, num_seqs)
+    d = make_desc(B, T, H, dk, dv, code, num_seqs, flags=_prep_flags(qk_l2norm, gate_logsigmoid))
     return int(load_library().kda_workspace_bytes(ctypes.byref(d), 1 if backward else 0))
 
 
@@ -189,19 +195,23 @@ def _stream(dev):
 
 
 def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, output_final_state=True,
-        out=None, final_state=None, workspace=None, out_dtype=None, save_for_backward=False):
+        out=None, final_state=None, workspace=None, out_dtype=None, save_for_backward=False, qk_l2norm=False,
+        gate_logsigmoid=False):
     """Forward pass; returns (o [B,T,H,dv] in out_dtype (default float32), final_state float32
     [N,H,dk,dv] or None).  out_dtype=torch.bfloat16 is allowed for bf16 inputs.
     save_for_backward=True leaves the backward's intermediates in `workspace` (which must then be
-    given, sized by workspace_bytes(..., backward=True)) for a following bwd(..., use_saved=True)."""
+    given, sized by workspace_bytes(..., backward=True)) for a following bwd(..., use_saved=True).
+    qk_l2norm / gate_logsigmoid: q, k arrive raw and are L2-normalised inside; log_alpha holds a raw
+    gate x (log alpha = logsigmoid(x) inside)."""
     import torch
     lib = load_library()
     desc, (B, T, H, dk, dv, N), dev, dt = _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale,
                                                    out_dtype)
+    desc.flags = _prep_flags(qk_l2norm, gate_logsigmoid)
     if save_for_backward:
         if workspace is None:
             raise ValueError("save_for_backward needs the caller's workspace (it is reused by bwd)")
-        desc.flags = KDA_FLAG_SAVE_FOR_BACKWARD
+        desc.flags |= KDA_FLAG_SAVE_FOR_BACKWARD
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
     else:
@@ -222,7 +232,8 @@ def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, 
 
 
 def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu_seqlens=None, scale=None,
-        need_d_init=True, workspace=None, out_dtype=None, grads=None, d_init=None, use_saved=False):
+        need_d_init=True, workspace=None, out_dtype=None, grads=None, d_init=None, use_saved=False,
+        qk_l2norm=False, gate_logsigmoid=False):
     """Backward pass; returns (dq, dk, dv, dlog_alpha, dbeta in out_dtype (default float32),
     d_init_state float32 or None).  use_saved=True: `workspace` holds what fwd(...,
     save_for_backward=True) left there for the same inputs; the forward is not recomputed."""
@@ -230,10 +241,11 @@ def bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final_state=None, cu
     lib = load_library()
     desc, (B, T, H, dk, dv, N), dev, odt = _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale,
                                                     out_dtype)
+    desc.flags = _prep_flags(qk_l2norm, gate_logsigmoid)
     if use_saved:
         if workspace is None:
             raise ValueError("use_saved needs the workspace the forward wrote")
-        desc.flags = KDA_FLAG_USE_SAVED
+        desc.flags |= KDA_FLAG_USE_SAVED
     _check("d_out", d_out, q.dtype, (B, T, H, dv), dev)
     if d_final_state is not None:
         _check("d_final_state", d_final_state, torch.float32, (N, H, dk, dv), dev)
@@ -263,7 +275,7 @@ DECODE_MAX_TOKENS = 16   # KDA_DECODE_MAX_TOKENS (include/kda.h)
 
 
 def decode(q, k, v, log_alpha, beta, state_pool, state_indices=None, num_commit=None, scale=None,
-           out=None, out_dtype=None):
+           out=None, out_dtype=None, qk_l2norm=False, gate_logsigmoid=False):
     """Decode / replay step: advance B sequences by T tokens each from states in `state_pool`.
 
     q, k, log_alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (float32 or bfloat16);
@@ -294,7 +306,8 @@ def decode(q, k, v, log_alpha, beta, state_pool, state_indices=None, num_commit=
         out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
     else:
         _check("out", out, odt, (B, T, H, dv), dev)
-    desc = make_desc(B, T, H, dk, dv, _dtype_code(dt), 0, scale, _dtype_code(odt))
+    desc = make_desc(B, T, H, dk, dv, _dtype_code(dt), 0, scale, _dtype_code(odt),
+                     flags=_prep_flags(qk_l2norm, gate_logsigmoid))
     rc = lib.kda_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                         _ptr(state_pool), int(state_pool.shape[0]), _ptr(state_indices), _ptr(num_commit),
                         _ptr(out), _stream(dev))

@@ -25,6 +25,7 @@ using kda::CH;
 using kda::ChunkInfo;
 
 constexpr size_t ALIGN = 256;
+constexpr int32_t KDA_PREP_FLAGS = KDA_FLAG_QK_L2NORM | KDA_FLAG_GATE_LOGSIGMOID;
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Plan {
@@ -32,7 +33,7 @@ struct Plan {
   int max_chunks = 0;
   size_t esz = 0;
   size_t chunks = 0, sc0 = 0, so = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
-  size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0;
+  size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0, DQK = 0;
   size_t total = 0;
 };
 
@@ -85,6 +86,7 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
     p.U = take(nb * dv * CH * 4);
     p.dS = take(nb * dk * dv * 4);
     p.dU = take(nb * dv * CH * 4);
+    if (d->flags & KDA_FLAG_QK_L2NORM) p.DQK = take(nb * 2 * CH * dk * 4);   // dq^, dk^ before the norm's chain rule
   }
   p.total = o;
   return p;
@@ -128,6 +130,7 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
   a.wsU = fptr(p.U);
   a.wsdS = fptr(p.dS);
   a.wsdU = fptr(p.dU);
+  a.wsDQK = fptr(p.DQK);
 }
 
 hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {
@@ -183,6 +186,8 @@ hipError_t run_decode(const kda_desc* d, const kda::DecodeArgs& a, hipStream_t s
 
 void base_args(Args& a, const kda_desc* d, int N, int max_chunks) {
   std::memset(&a, 0, sizeof a);
+  a.qk_norm = (d->flags & KDA_FLAG_QK_L2NORM) != 0;
+  a.gate_ls = (d->flags & KDA_FLAG_GATE_LOGSIGMOID) != 0;
   a.B = d->B;
   a.T = d->T;
   a.H = d->H;
@@ -351,7 +356,7 @@ kda_status kda_fwd(const kda_desc* d, const void* q, const void* k, const void* 
   if (beta && ((uintptr_t)beta % (d->dtype == KDA_BF16 ? 2 : 4))) return KDA_ERROR_MISALIGNED;
   if (out && ((uintptr_t)out % (d->out_dtype == KDA_BF16 ? 2 : 4))) return KDA_ERROR_MISALIGNED;
   if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_MISALIGNED;
-  if (d->flags & ~KDA_FLAG_SAVE_FOR_BACKWARD) return KDA_ERROR_INVALID_VALUE;
+  if (d->flags & ~(KDA_FLAG_SAVE_FOR_BACKWARD | KDA_PREP_FLAGS)) return KDA_ERROR_INVALID_VALUE;
   const bool save = (d->flags & KDA_FLAG_SAVE_FOR_BACKWARD) != 0;
   if (save && d->dtype == KDA_F32 && d->dk == 128) return KDA_ERROR_NOT_SUPPORTED;  // no fp32 backward at dk = 128
   const Plan p = make_plan(d, save, N, mc);
@@ -390,7 +395,7 @@ kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* 
   if ((beta && (uintptr_t)beta % es) || (dbeta && (uintptr_t)dbeta % eo)) return KDA_ERROR_MISALIGNED;
   if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_MISALIGNED;
   if (d->dtype == KDA_F32 && d->dk == 128) return KDA_ERROR_NOT_SUPPORTED;  // fp32 backward: dk = 64 only
-  if (d->flags & ~KDA_FLAG_USE_SAVED) return KDA_ERROR_INVALID_VALUE;
+  if (d->flags & ~(KDA_FLAG_USE_SAVED | KDA_PREP_FLAGS)) return KDA_ERROR_INVALID_VALUE;
   const Plan p = make_plan(d, true, N, mc);
   if (!workspace || workspace_bytes < p.total) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -415,7 +420,7 @@ kda_status kda_decode(const kda_desc* d, const void* q, const void* k, const voi
   if (!dims_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
   if (d->B < 0 || d->T < 0 || d->T > KDA_DECODE_MAX_TOKENS || d->H < 1 || d->H > 65535) return KDA_ERROR_INVALID_VALUE;
   if ((long long)d->B * d->T * d->H >= (1LL << 31) || (long long)d->B * d->H >= (1LL << 31)) return KDA_ERROR_INVALID_VALUE;
-  if (!std::isfinite(d->scale) || d->flags != 0 || pool_size < 0) return KDA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(d->scale) || (d->flags & ~KDA_PREP_FLAGS) || pool_size < 0) return KDA_ERROR_INVALID_VALUE;
   if (d->B == 0 || d->T == 0) return KDA_SUCCESS;
   if (!q || !k || !v || !log_alpha || !beta || !out || !state_pool) return KDA_ERROR_INVALID_VALUE;
   if (!state_indices && pool_size < d->B) return KDA_ERROR_INVALID_VALUE;
@@ -431,6 +436,8 @@ kda_status kda_decode(const kda_desc* d, const void* q, const void* k, const voi
   a.pool = state_pool; a.idx = state_indices; a.ncommit = num_commit; a.out = out;
   a.B = d->B; a.T = d->T; a.H = d->H; a.pool_size = pool_size;
   a.scale = d->scale != 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
+  a.qk_norm = (d->flags & KDA_FLAG_QK_L2NORM) != 0;
+  a.gate_ls = (d->flags & KDA_FLAG_GATE_LOGSIGMOID) != 0;
   (void)hipGetLastError();
   clear_error();
   return launch_status(run_decode(d, a, static_cast<hipStream_t>(stream)));

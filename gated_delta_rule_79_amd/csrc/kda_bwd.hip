@@ -333,7 +333,9 @@ struct BwdLds {
   static constexpr size_t DGAM = GAMP + 512 * 4;                      // float [DK]
   static constexpr size_t BV = DGAM + DK * 4;                         // float [2][CH] rowsum(V * T^T dU) halves
   static constexpr size_t DBP = BV + 2 * CH * 4;                      // float [2][CH] dbeta halves
-  static constexpr size_t END0 = DBP + 2 * CH * 4;
+  static constexpr size_t NRM = DBP + 2 * CH * 4;                     // float [2][CH] 1/|q_r|, 1/|k_r| (qk_norm)
+  static constexpr size_t NDOT = NRM + 2 * CH * 4;                    // float [2][2][CH] q^.dq^, k^.dk^ halves
+  static constexpr size_t END0 = NDOT + 4 * CH * 4;
   static constexpr size_t Y = DW;                                     // OP [CH][LDT]
   static_assert(LDT <= LDO, "Y fits in the dW region");
   // gated products, per pass of 32 channels: decayed q and k tables (split SE,
@@ -355,7 +357,9 @@ struct BwdLds {
   static_assert(A_END % 16 == 0 && B_END % 16 == 0, "LDS regions stay 16-byte aligned");
 };
 
-template <typename E, typename O, int DK, int DV>
+// QKN: q and k rows are L2-normalised on load and dq, dk go through the norm's
+// chain rule at the end (KDA_FLAG_QK_L2NORM).
+template <typename E, typename O, int DK, int DV, bool QKN>
 __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   using L = BwdLds<E, DK, DV>;
   using OP = typename L::OP;
@@ -421,6 +425,18 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   float* sDGam = reinterpret_cast<float*>(smem + L::DGAM);
   float* sBv = reinterpret_cast<float*>(smem + L::BV);
   float* sDbp = reinterpret_cast<float*>(smem + L::DBP);
+  float* sNrm = reinterpret_cast<float*>(smem + L::NRM);
+  float* sDot = reinterpret_cast<float*>(smem + L::NDOT);
+  constexpr bool qk_norm = QKN;
+  // normalised q and k values: raw row element times the row's 1/|x| (1 without QKN)
+  auto qn = [&](int r, int c) __attribute__((always_inline)) {
+    if constexpr (QKN) return f32(sQ[r * L::LDK + c]) * sNrm[r];
+    else return f32(sQ[r * L::LDK + c]);
+  };
+  auto kn = [&](int r, int c) __attribute__((always_inline)) {
+    if constexpr (QKN) return f32(sK[r * L::LDK + c]) * sNrm[CH + r];
+    else return f32(sK[r * L::LDK + c]);
+  };
 
   const E* qh = reinterpret_cast<const E*>(a.q) + (size_t)ci.t0 * rk + (size_t)h * DK;
   const E* kh = reinterpret_cast<const E*>(a.k) + (size_t)ci.t0 * rk + (size_t)h * DK;
@@ -602,9 +618,25 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) gGram[jj][ii] = gGm[(16 * tw + 4 * q4 + ii) * CH + 16 * (2 * hf + jj) + r16];
+  if constexpr (qk_norm) {   // each row's 1/|x|; the raw rows stay in LDS and every use scales them
+    float scq[decltype(pq)::PER], sck[decltype(pk)::PER];
+    pq.row_inv_norms(L2N_EPS, scq);
+    pk.row_inv_norms(L2N_EPS, sck);
+#pragma unroll
+    for (int I = 0; I < decltype(pq)::PER; ++I) {
+      int row;
+      if (pq.row_leader(I, row)) {
+        sNrm[row] = scq[I];
+        sNrm[CH + row] = sck[I];
+      }
+    }
+  }
   pk.template store_cvt<E>(sK, L::LDK, len);
   pq.template store_cvt<E>(sQ, L::LDK, len);
-  pl.template store_cvt<float>(sG, L::LDG, len);
+  if (a.gate_ls)   // raw gate x -> log alpha = logsigmoid(x)
+    pl.template store_map<float>(sG, L::LDG, len, [](float x) { return logsigmoid(x); });
+  else
+    pl.template store_cvt<float>(sG, L::LDG, len);
   __syncthreads();
   if (tid < DK) {
     float s = 0.f;
@@ -635,7 +667,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   __syncthreads();
   for (int o = tid; o < CH * DK; o += NT) {
     const int rr = o / DK, cc = o % DK;
-    sKp[rr * L::LDO + cc] = cvt<OP>(f32(sK[rr * L::LDK + cc]) * __expf(sG[rr * L::LDG + cc]));
+    sKp[rr * L::LDO + cc] = cvt<OP>(kn(rr, cc) * __expf(sG[rr * L::LDG + cc]));
   }
   __syncthreads();
 
@@ -654,7 +686,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;
-      dbeta[ii] += f32(sK[rr * L::LDK + cc]) * __expf(sG[rr * L::LDG + cc]) * x[ii];
+      dbeta[ii] += kn(rr, cc) * __expf(sG[rr * L::LDG + cc]) * x[ii];
     }
   }
   // ---- dT = (dW K+^T + dU V^T) diag(beta), column tiles 2hf, 2hf+1 -> sA2
@@ -720,6 +752,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   O* dlo = reinterpret_cast<O*>(a.dla) + (size_t)ci.t0 * rk + (size_t)h * DK;
   float dgv[NKH][4];
   float khs[NKH];   // column sums over this lane's rows of dKh * Kh (for dg_C)
+  float qdot[4] = {0.f, 0.f, 0.f, 0.f}, kdot[4] = {0.f, 0.f, 0.f, 0.f};   // q^.dq^, k^.dk^ (qk_norm)
+  float* wDQ = qk_norm ? a.wsDQK + blk * (2 * CH * DK) : nullptr;
+  float* wDK = qk_norm ? wDQ + CH * DK : nullptr;
   constexpr int TC = L::TC;
   static_assert(TC == 2 * 16 && NT == TC * (CH / 4), "table build: one thread per (channel, 4 tokens)");
   // (dk = 128 keeps the pass loop rolled: unrolled, it no longer fits the registers)
@@ -736,8 +771,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         const int r = r0 + u;
         const float g = sG[r * L::LDG + c];
         const float e = __expf(g - gm);
-        const float kv = f32(sK[r * L::LDK + c]);
-        put_split(tQh, tQl, cl * L::LDQ + r, f32(sQ[r * L::LDK + c]) * e);
+        const float kv = kn(r, c);
+        put_split(tQh, tQl, cl * L::LDQ + r, qn(r, c) * e);
         put_split(tKh, tKl, cl * L::LDQ + r, kv * e);
         kr[u] = kv * __expf(gm - g);
       }
@@ -808,16 +843,22 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         const int rr = 16 * tw + 4 * q4 + ii;
         const float g = sG[rr * L::LDG + cc];
         const float eg = __expf(g);
-        const float kv = f32(sK[rr * L::LDK + cc]), qv = f32(sQ[rr * L::LDK + cc]);
+        const float kv = kn(rr, cc), qv = qn(rr, cc);
         const float dq = eg * scale * accQ[jj][ii] + dqg[ii];
         const float dkp = eg * sBeta[rr] * tdw[jj][ii] + dkpg[ii];
         const float dkmv = dkm[ii];
         const float dkh = __expf(gl - g) * accK[jj][ii];
         dgv[jj][ii] = dq * qv + (dkp - dkmv - dkh) * kv;
         khs[jj] += dkh * kv;
-        if (rr < len) {
+        const float dkt = dkp + dkmv + dkh;
+        if constexpr (qk_norm) {   // gradients of the normalised rows; the chain rule follows below
+          wDQ[rr * DK + cc] = dq;
+          wDK[rr * DK + cc] = dkt;
+          qdot[ii] += qv * dq;
+          kdot[ii] += kv * dkt;
+        } else if (rr < len) {
           dqo[(size_t)rr * rk + cc] = cvt<O>(dq);
-          dko[(size_t)rr * rk + cc] = cvt<O>(dkp + dkmv + dkh);
+          dko[(size_t)rr * rk + cc] = cvt<O>(dkt);
         }
       }
     }
@@ -831,6 +872,22 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     p += __shfl_xor(p, 4);
     p += __shfl_xor(p, 8);
     if (r16 == 0) sDbp[hf * CH + 16 * tw + 4 * q4 + ii] = p;
+  }
+  if constexpr (qk_norm) {   // row dots: reduce over the 16 column lanes; halves meet in LDS
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      float pq = qdot[ii], pk = kdot[ii];
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        pq += __shfl_xor(pq, m);
+        pk += __shfl_xor(pk, m);
+      }
+      if (r16 == 0) {
+        sDot[hf * CH + 16 * tw + 4 * q4 + ii] = pq;
+        sDot[2 * CH + hf * CH + 16 * tw + 4 * q4 + ii] = pk;
+      }
+    }
+    __threadfence_block();   // the workspace rows of dq^, dk^ are read by other threads below
   }
   __syncthreads();  // all reads of g are done before dg overwrites it
 #pragma unroll
@@ -871,7 +928,25 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
     for (int rr = (s + 1) * RPS - 1; rr >= s * RPS; --rr) {
       acc += sG[rr * L::LDG + c];
-      if (rr < len) dlo[(size_t)rr * rk + c] = cvt<O>(acc);
+      if (rr < len) dlo[(size_t)rr * rk + c] = cvt<O>(a.gate_ls ? acc * sigmoid_neg(f32(lh[(size_t)rr * rk + c])) : acc);
+    }
+  }
+  if constexpr (qk_norm) {
+    // d x = (1/|x|) (d x^ - x^ (x^ . d x^)) for the raw q and k rows
+    for (int o = tid; o < 2 * CH * DK / 4; o += NT) {
+      const int which = o / (CH * DK / 4), e = 4 * (o % (CH * DK / 4));
+      const int rr = e / DK, c0 = e % DK;
+      if (rr >= len) continue;
+      const float* src = which ? wDK : wDQ;
+      const E* xh = which ? sK : sQ;
+      const f32x4 g = *reinterpret_cast<const f32x4*>(src + rr * DK + c0);
+      const float dot = sDot[2 * CH * which + rr] + sDot[2 * CH * which + CH + rr];
+      const float sc = sNrm[CH * which + rr];
+      O* dst = (which ? dko : dqo) + (size_t)rr * rk + c0;
+      float y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = sc * (g[u] - f32(xh[rr * L::LDK + c0 + u]) * sc * dot);
+      store4<O>(dst, y[0], y[1], y[2], y[3]);
     }
   }
 }
@@ -910,8 +985,12 @@ hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved) {
     if (e != hipSuccess) return e;
   }
   if (a.max_chunks > 0) {
-    KDA_TIMED("kda_bwd_chunk", st,
-              hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV>), dim3(a.max_chunks, a.H), dim3(512), 0, st, a));
+    if (a.qk_norm)
+      KDA_TIMED("kda_bwd_chunk", st,
+                hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV, true>), dim3(a.max_chunks, a.H), dim3(512), 0, st, a));
+    else
+      KDA_TIMED("kda_bwd_chunk", st,
+                hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV, false>), dim3(a.max_chunks, a.H), dim3(512), 0, st, a));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

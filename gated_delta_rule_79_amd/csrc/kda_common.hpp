@@ -278,7 +278,46 @@ struct TileCopy {
       }
     });
   }
+  // Store f(x) converted to D; rows >= nrows are stored as zeros.
+  template <typename D, typename F>
+  __device__ __forceinline__ void store_map(D* dst, int dst_ld, int nrows, F f) const {
+    constexpr int EPV = 16 / (int)sizeof(E);
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = threadIdx.x + I * NT;
+      if (NV % NT == 0 || v < NV) {
+        const int row = v / VPR, c0 = (v % VPR) * EPV;
+        const E* e = reinterpret_cast<const E*>(&r[I]);
+        const bool ok = row < nrows;
+#pragma unroll
+        for (int i = 0; i < EPV; i += 4)
+          store4<D>(dst + row * dst_ld + c0 + i, ok ? f(f32(e[i])) : 0.f, ok ? f(f32(e[i + 1])) : 0.f,
+                    ok ? f(f32(e[i + 2])) : 0.f, ok ? f(f32(e[i + 3])) : 0.f);
+      }
+    });
+  }
   // fp32 tile stored as a split pair (hi, lo) of D (lo unused when D is fp32).
+  // 1 / sqrt(sum x^2 + eps) of the row each held vector belongs to (the row's VPR
+  // vectors sit in VPR consecutive lanes, so a butterfly over those lanes sums
+  // it); the rows themselves are left as loaded.
+  __device__ __forceinline__ void row_inv_norms(float eps, float (&scale)[PER]) const {
+    static_assert(VPR <= 64 && (VPR & (VPR - 1)) == 0 && NT % VPR == 0, "a row spans a power-of-two lane group");
+    constexpr int EPV = 16 / (int)sizeof(E);
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const E* e = reinterpret_cast<const E*>(&r[I]);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) ss += f32(e[i]) * f32(e[i]);
+#pragma unroll
+      for (int m = 1; m < VPR; m <<= 1) ss += __shfl_xor(ss, m);
+      scale[I] = 1.0f / sqrtf(ss + eps);
+    });
+  }
+  // Thread that writes row `row`'s entry of a per-row array (the first lane of its group).
+  __device__ __forceinline__ bool row_leader(int I, int& row) const {
+    const int v = threadIdx.x + I * NT;
+    row = v / VPR;
+    return v % VPR == 0 && v < NV;
+  }
   template <typename D>
   __device__ __forceinline__ void store_split(D* hi, D* lo, int dst_ld) const {
     static_assert(sizeof(E) == 4, "split store takes an fp32 tile");
@@ -316,6 +355,10 @@ __device__ __forceinline__ void copy_out(E* __restrict__ dst, size_t dst_ld, con
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
+// Fused input preparation (kda.h: KDA_FLAG_QK_L2NORM, KDA_FLAG_GATE_LOGSIGMOID).
+constexpr float L2N_EPS = 1e-6f;
+__device__ __forceinline__ float logsigmoid(float x) { return fminf(x, 0.f) - log1pf(__expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_neg(float x) { return 1.f / (1.f + __expf(x)); }   // sigmoid(-x)
 template <typename E> __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
   if constexpr (sizeof(E) == 4) {
     *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};

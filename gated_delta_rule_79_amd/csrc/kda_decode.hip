@@ -100,7 +100,8 @@ __global__ __launch_bounds__(DEC_NT) void kda_decode_step(const DecodeArgs a) {
     const size_t g = ((size_t)(b * T + t) * H + h) * DK + c;
     sQ[t][c] = f32(q[g]);
     sK[t][c] = f32(k[g]);
-    sA[t][c] = __expf(f32(la[g]));
+    const float x = f32(la[g]);
+    sA[t][c] = a.gate_ls ? 1.f / (1.f + __expf(-x)) : __expf(x);   // alpha = sigmoid(x) for a raw gate
   }
   for (int o = tid; o < T * DV; o += DEC_NT) {
     const int t = o / DV, j = o % DV;
@@ -108,6 +109,18 @@ __global__ __launch_bounds__(DEC_NT) void kda_decode_step(const DecodeArgs a) {
   }
   if (tid < T) sB[tid] = f32(reinterpret_cast<const E*>(a.beta)[(size_t)(b * T + tid) * H + h]);
   __syncthreads();
+  if (a.qk_norm) {   // q, k rows to unit L2 norm (fp32), one wave per row
+    for (int row = w; row < 2 * T; row += DEC_NW) {
+      float* x = row < T ? sQ[row] : sK[row - T];
+      float ss = 0.f;
+      for (int c = lane; c < DK; c += 64) ss += x[c] * x[c];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      const float sc = 1.0f / sqrtf(ss + L2N_EPS);
+      for (int c = lane; c < DK; c += 64) x[c] *= sc;
+    }
+    __syncthreads();
+  }
   for (int t = w; t < T; t += DEC_NW) {   // k_t . q_t, one wave per token
     float p = 0.f;
     for (int c = lane; c < DK; c += 64) p += sQ[t][c] * sK[t][c];

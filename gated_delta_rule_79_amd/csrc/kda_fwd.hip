@@ -145,7 +145,8 @@ struct PrepLds {
   static_assert(BYTES <= 163840, "prep LDS");
 };
 
-template <typename E, int DK, int DV, bool BWD>
+// QKN: q and k rows are L2-normalised on load (KDA_FLAG_QK_L2NORM).
+template <typename E, int DK, int DV, bool BWD, bool QKN>
 __global__ __launch_bounds__(256) void kda_prep(const Args a) {
   using L = PrepLds<E, DK, DV>;
   using OP = typename L::OP;
@@ -197,6 +198,34 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
   }
 #pragma unroll
   for (int vs = 0; vs < NVS; ++vs) load8<E>(vh + r * rv + 32 * vs + 8 * q4, rv_ok, xv[vs]);
+  if constexpr (QKN) {   // row r's channels sit in this lane and the lanes 16 and 32 away
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        sq += xq[ks][u] * xq[ks][u];
+        sk += xk[ks][u] * xk[ks][u];
+      }
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 16);
+    sk += __shfl_xor(sk, 32);
+    const float nq = 1.0f / sqrtf(sq + L2N_EPS), nk = 1.0f / sqrtf(sk + L2N_EPS);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        xq[ks][u] *= nq;   // this kernel serves fp32 inputs: the normalised rows stay exact
+        xk[ks][u] *= nk;
+      }
+  }
+  if (a.gate_ls && rv_ok) {   // rows past the chunk stay 0 (no decay)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xl[ks][u] = logsigmoid(xl[ks][u]);
+  }
   const float bet = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
   if (tid < CH) sBeta[tid] = bet;
 #pragma unroll
@@ -435,7 +464,8 @@ struct Prep8Lds {
   static constexpr size_t X = A + (size_t)CH * LDA * 4;       // float [3][256]   off-diagonal partial sums
   static constexpr size_t BETA = X + 3 * 256 * 4;             // float [CH]
   static constexpr size_t RED = BETA + CH * 4;                // float [512]
-  static constexpr size_t BYTES = RED + 512 * 4;
+  static constexpr size_t NRM = RED + 512 * 4;                // float [2][CH]  1/|q_r|, 1/|k_r| (QKN)
+  static constexpr size_t BYTES = NRM + 2 * CH * 4;
   static_assert(BYTES <= 163840, "prep LDS");
 };
 
@@ -449,7 +479,9 @@ __device__ __forceinline__ f32x4 mm16_f32(const float* A, int lda, const float* 
   return c;
 }
 
-template <int DK, int DV, bool BWD>
+// GATE: log_alpha holds a raw gate x (KDA_FLAG_GATE_LOGSIGMOID).  Both options
+// are compile-time so the plain kernel keeps its register budget.
+template <int DK, int DV, bool BWD, bool QKN, bool GATE>
 __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   using L = Prep8Lds<DK, DV>;
   using E = bf16;
@@ -473,6 +505,12 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   float* sX = reinterpret_cast<float*>(smem + L::X);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sRed = reinterpret_cast<float*>(smem + L::RED);
+  // row scales of q and k: 1/|row| with KDA_FLAG_QK_L2NORM (the raw rows stay in
+  // LDS and every use multiplies by the scale, so normalisation adds no rounding)
+  float* sNq = reinterpret_cast<float*>(smem + L::NRM);
+  float* sNk = sNq + CH;
+  auto nq = [&](int r) __attribute__((always_inline)) { if constexpr (QKN) return sNq[r]; else return 1.f; };
+  auto nk = [&](int r) __attribute__((always_inline)) { if constexpr (QKN) return sNk[r]; else return 1.f; };
 
   const E* gq = reinterpret_cast<const E*>(a.q);
   const E* gk = reinterpret_cast<const E*>(a.k);
@@ -506,9 +544,25 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
     float* wGam = a.wsGam + blk * WB::GAM;
 
     __syncthreads();  // the previous item's LDS reads are done
+    if constexpr (QKN) {
+      float scq[decltype(pq)::PER], sck[decltype(pk)::PER];
+      pq.row_inv_norms(L2N_EPS, scq);
+      pk.row_inv_norms(L2N_EPS, sck);
+#pragma unroll
+      for (int I = 0; I < decltype(pq)::PER; ++I) {
+        int row;
+        if (pq.row_leader(I, row)) {
+          sNq[row] = scq[I];
+          sNk[row] = sck[I];
+        }
+      }
+    }
     pk.template store_cvt<E>(sK, L::LDK, len);
     pq.template store_cvt<E>(sQ, L::LDK, len);
-    pl.template store_cvt<float>(sG, L::LDG, len);
+    if constexpr (GATE)   // raw gate x -> log alpha = logsigmoid(x)
+      pl.template store_map<float>(sG, L::LDG, len, [](float x) { return logsigmoid(x); });
+    else
+      pl.template store_cvt<float>(sG, L::LDG, len);
     {
       // V^T: each 16-byte piece is 8 value columns of one token
       constexpr int VPR = DV / 8;
@@ -559,7 +613,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
         const int v = tid + i * NT, r = v / VA, c0 = (v % VA) * 8;
         float y[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) y[u] = f32(sQ[r * L::LDK + c0 + u]) * __expf(sG[r * L::LDG + c0 + u]);
+        for (int u = 0; u < 8; ++u) y[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * __expf(sG[r * L::LDG + c0 + u]);
         store4<OP>(wQt + r * DK + c0, y[0], y[1], y[2], y[3]);
         store4<OP>(wQt + r * DK + c0 + 4, y[4], y[5], y[6], y[7]);
         if constexpr (BWD) {
@@ -569,7 +623,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
           OP* wKhL = wKhH + CH * DK;
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            y[u] = f32(sK[r * L::LDK + c0 + u]) * __expf(sG[(CH - 1) * L::LDG + c0 + u] - sG[r * L::LDG + c0 + u]);
+            y[u] = f32(sK[r * L::LDK + c0 + u]) * nk(r) * __expf(sG[(CH - 1) * L::LDG + c0 + u] - sG[r * L::LDG + c0 + u]);
           store4_split<OP>(wKhH + r * DK + c0, wKhL + r * DK + c0, y[0], y[1], y[2], y[3]);
           store4_split<OP>(wKhH + r * DK + c0 + 4, wKhL + r * DK + c0 + 4, y[4], y[5], y[6], y[7]);
         }
@@ -581,7 +635,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
         float kp[8], kh[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float g = sG[(t0 + u) * L::LDG + c], kv = f32(sK[(t0 + u) * L::LDK + c]);
+          const float g = sG[(t0 + u) * L::LDG + c], kv = f32(sK[(t0 + u) * L::LDK + c]) * nk(t0 + u);
           kp[u] = kv * __expf(g);
           kh[u] = kv * __expf(glast - g);
         }
@@ -609,8 +663,8 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const float e = __expf(sG[r * L::LDG + c0 + u] - sG[ref * L::LDG + c0 + u]);
-            yk[u] = f32(sK[r * L::LDK + c0 + u]) * e;
-            yq[u] = f32(sQ[r * L::LDK + c0 + u]) * e;
+            yk[u] = f32(sK[r * L::LDK + c0 + u]) * nk(r) * e;
+            yq[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * e;
           }
           fk[ks] = sfrag_from<bf16>(yk);
           fq[ks] = sfrag_from<bf16>(yq);
@@ -624,7 +678,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
             float xr[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-              xr[u] = f32(sK[i * L::LDK + c0 + u]) * __expf(sG[ref * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
+              xr[u] = f32(sK[i * L::LDK + c0 + u]) * nk(i) * __expf(sG[ref * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
             const SFrag<bf16> fr = sfrag_from<bf16>(xr);
             akk = mma_ss(fk[ks], fr, akk);
             aqk = mma_ss(fq[ks], fr, aqk);
@@ -1040,9 +1094,24 @@ static hipError_t launch_prep(const Args& a, hipStream_t st, const char* name) {
   if constexpr (sizeof(E) == 2) {
     const long long items = (long long)a.max_chunks * a.H;
     const int grid = (int)std::min<long long>(items, device_cus());
-    KDA_TIMED(name, st, hipLaunchKernelGGL((kda_prep8<DK, DV, BWD>), dim3(grid), dim3(512), 0, st, a));
+#define KDA_PREP8(QKN, GATE) \
+  KDA_TIMED(name, st, hipLaunchKernelGGL((kda_prep8<DK, DV, BWD, QKN, GATE>), dim3(grid), dim3(512), 0, st, a))
+    if (a.qk_norm && a.gate_ls)
+      KDA_PREP8(true, true);
+    else if (a.qk_norm)
+      KDA_PREP8(true, false);
+    else if (a.gate_ls)
+      KDA_PREP8(false, true);
+    else
+      KDA_PREP8(false, false);
+#undef KDA_PREP8
   } else {
-    KDA_TIMED(name, st, hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
+    if (a.qk_norm)
+      KDA_TIMED(name, st,
+                hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD, true>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
+    else
+      KDA_TIMED(name, st,
+                hipLaunchKernelGGL((kda_prep<E, DK, DV, BWD, false>), dim3(a.max_chunks, a.H), dim3(256), 0, st, a));
   }
   return hipGetLastError();
 }

@@ -41,6 +41,11 @@ struct Args {
   float* wsdU;              // dU, fp32 [CH][DV]
   int dvs;                  // value-column slice width of the sequential passes
   int out_bf16;             // outputs and gradients stored as bf16 (else fp32)
+  // fused input preparation
+  int qk_norm;              // q, k rows L2-normalised inside (KDA_FLAG_QK_L2NORM)
+  int gate_ls;              // log_alpha holds a raw gate x; log alpha = logsigmoid(x)
+  float* wsDQK;             // backward with qk_norm: dq^, dk^ (normalised-input gradients),
+                            // fp32 [2][CH][DK] per chunk-head
 };
 
 // Decode / replay step (kda_decode).
@@ -52,6 +57,7 @@ struct DecodeArgs {
   void* out;                           // [B][T][H][DV] in the output dtype
   int B, T, H, pool_size;
   float scale;
+  int qk_norm, gate_ls;                // fused input preparation, as in Args
 };
 
 // Opt-in per-kernel timing (kda_timing_enable): a no-op unless enabled.

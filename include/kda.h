@@ -96,6 +96,21 @@ typedef struct {
  * are bit-identical to a kda_bwd call without the flag.  Violating the
  * precondition gives wrong gradients; it is not detected. */
 #define KDA_FLAG_USE_SAVED 2
+/* Fused input preparation (the step upstream of the recurrence in the page's
+ * KDA workloads), for kda_fwd, kda_bwd and kda_decode alike:
+ * KDA_FLAG_QK_L2NORM: q and k arrive raw; each (token, head) row is scaled to
+ *   x / sqrt(sum(x^2) + 1e-6) over the dk channels inside the kernels, and dq,
+ *   dk are gradients with respect to the raw rows.  With bf16 inputs the
+ *   normalised rows are rounded to bf16 once (as a separate bf16 normalisation
+ *   pass would round them).
+ * KDA_FLAG_GATE_LOGSIGMOID: log_alpha holds a raw gate x; the kernels use
+ *   log alpha = logsigmoid(x) (alpha = sigmoid(x)), and dlog_alpha is the
+ *   gradient with respect to x.
+ * A backward call must carry the same preparation flags as the forward it
+ * differentiates (and, with KDA_FLAG_USE_SAVED, as the saving forward);
+ * kda_workspace_bytes accounts for them. */
+#define KDA_FLAG_QK_L2NORM 4
+#define KDA_FLAG_GATE_LOGSIGMOID 8
 
 /* Bytes of device workspace kda_fwd (backward = 0) or kda_bwd (backward != 0)
  * needs for this problem; 0 if the descriptor is invalid. */
@@ -136,7 +151,7 @@ kda_status kda_bwd(const kda_desc *desc, const void *q, const void *k, const voi
  *                     untouched.  Outputs always follow all T tokens.
  * A verification pass over draft tokens commits 0; the replay of the accepted
  * prefix commits its length (or passes only the accepted tokens).
- * desc->num_seqs is ignored and desc->flags must be 0.  Non-padding slots must
+ * desc->num_seqs is ignored; desc->flags may hold only the preparation flags.  Non-padding slots must
  * be distinct within one call (two sequences on one slot race).  No
  * workspace: the call uses only the buffers passed in.  The 16-byte alignment
  * rule applies to q, k, v, log_alpha, out and state_pool; state_indices and

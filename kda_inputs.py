@@ -121,9 +121,13 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
     return (x / np.maximum(n, 1e-30)).astype(np.float32)
 
 
-def make_inputs(w: Workload, heads=None, with_grads=None) -> dict:
+def make_inputs(w: Workload, heads=None, with_grads=None, raw=False) -> dict:
     """Draw the inputs of workload w as float32 numpy arrays holding values
     exactly representable in the storage dtype.
+
+    raw=True: the values before input preparation, for kernels that prepare
+    them themselves: q, k as drawn (N(0,1), not normalised) and "log_alpha"
+    holding the raw gate x instead of logsigmoid(x).
 
     Token-major packed layout: q,k,log_alpha [N_tok,H,dk]; v [N_tok,H,dv];
     beta [N_tok,H]; init_state [num_seqs,H,dk,dv] float32 (or None);
@@ -145,11 +149,12 @@ def make_inputs(w: Workload, heads=None, with_grads=None) -> dict:
     def draw(name, shape, mu=0.0, sd=1.0):
         return _rng(s, name).standard_normal(size=shape, dtype=np.float32) * np.float32(sd) + np.float32(mu)
 
-    q = _unit_rows(draw("q", (n_tok, H, dk)))[:, hs]
-    k = _unit_rows(draw("k", (n_tok, H, dk)))[:, hs]
+    prep = (lambda a: a) if raw else _unit_rows
+    q = prep(draw("q", (n_tok, H, dk)))[:, hs]
+    k = prep(draw("k", (n_tok, H, dk)))[:, hs]
     v = draw("v", (n_tok, H, dv))[:, hs]
     x = draw("gate_x", (n_tok, H, dk), w.gate_mu, w.gate_sd)[:, hs].astype(np.float64)
-    log_alpha = -np.logaddexp(0.0, -x)          # logsigmoid(x)
+    log_alpha = x if raw else -np.logaddexp(0.0, -x)          # logsigmoid(x)
     bl = draw("beta_logit", (n_tok, H))[:, hs].astype(np.float64)
     beta = 1.0 / (1.0 + np.exp(-bl))
     out = dict(
@@ -179,7 +184,7 @@ def small(dtype="f32", lengths=(100,), H=2, dk=64, dv=64, gate_mu=3.0, gate_sd=1
 
 
 def decode_inputs(B, T, H, dk, dv, pool_size, dtype="bf16", gate_mu=3.0, gate_sd=1.0, state_sd=0.5,
-                  seed=4321) -> dict:
+                  seed=4321, raw=False) -> dict:
     """Inputs of a decode / replay step: B sequences of T tokens each, token-major
     [B,T,H,.] (same value recipe as the workloads above), and a float32 state
     pool [pool_size,H,dk,dv] ~ N(0, state_sd) standing in for states left by
@@ -188,11 +193,12 @@ def decode_inputs(B, T, H, dk, dv, pool_size, dtype="bf16", gate_mu=3.0, gate_sd
         return _rng(seed, "decode_" + name).standard_normal(size=shape, dtype=np.float32) * np.float32(sd) \
             + np.float32(mu)
 
-    q = _unit_rows(draw("q", (B, T, H, dk)))
-    k = _unit_rows(draw("k", (B, T, H, dk)))
+    prep = (lambda a: a) if raw else _unit_rows
+    q = prep(draw("q", (B, T, H, dk)))
+    k = prep(draw("k", (B, T, H, dk)))
     v = draw("v", (B, T, H, dv))
     x = draw("gate_x", (B, T, H, dk), gate_mu, gate_sd).astype(np.float64)
-    log_alpha = -np.logaddexp(0.0, -x)          # logsigmoid(x)
+    log_alpha = x if raw else -np.logaddexp(0.0, -x)          # logsigmoid(x), or the raw gate
     beta = 1.0 / (1.0 + np.exp(-draw("beta_logit", (B, T, H)).astype(np.float64)))
     out = {name: np.ascontiguousarray(_store(a, dtype)) for name, a in
            (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta))}

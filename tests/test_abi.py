@@ -150,9 +150,10 @@ def test_flag_validation(lib):
     """Unknown flag bits, a flag on the wrong call, and saving where no backward exists are rejected
     before any launch."""
     assert _fwd(lib, _desc(flags=kda.KDA_FLAG_USE_SAVED)) == S_INVALID
-    assert _fwd(lib, _desc(flags=4)) == S_INVALID
+    assert _fwd(lib, _desc(flags=16)) == S_INVALID
+    assert _fwd(lib, _desc(flags=kda.KDA_FLAG_QK_L2NORM | 32)) == S_INVALID
     assert _bwd(lib, _desc(flags=kda.KDA_FLAG_SAVE_FOR_BACKWARD)) == S_INVALID
-    assert _bwd(lib, _desc(flags=8)) == S_INVALID
+    assert _bwd(lib, _desc(flags=kda.KDA_FLAG_GATE_LOGSIGMOID | 16)) == S_INVALID
     assert _fwd(lib, _desc(dtype=0, dk=128, flags=kda.KDA_FLAG_SAVE_FOR_BACKWARD)) == S_UNSUP
 
 
@@ -178,6 +179,7 @@ def test_decode_validation(lib):
     assert _dec(lib, _desc(**dict(ok, T=-1))) == S_INVALID
     assert _dec(lib, _desc(**dict(ok, B=-1))) == S_INVALID
     assert _dec(lib, _desc(**dict(ok, flags=1))) == S_INVALID
+    assert _dec(lib, _desc(**dict(ok, flags=kda.KDA_FLAG_QK_L2NORM | kda.KDA_FLAG_USE_SAVED))) == S_INVALID
     assert _dec(lib, _desc(**dict(ok, dk=96))) == S_UNSUP
     assert _dec(lib, _desc(**dict(ok, dtype=0, out_dtype=1))) == S_UNSUP
     assert _dec(lib, _desc(**ok), pool_size=3) == S_INVALID           # slot b needs pool_size >= B
@@ -191,3 +193,13 @@ def test_decode_validation(lib):
     assert _dec(lib, _desc(**ok), beta=A + 1) == S_ALIGN
     assert _dec(lib, _desc(**dict(ok, B=0)), q=0, out=0, pool=0) == S_OK
     assert _dec(lib, _desc(**dict(ok, T=0)), q=0, out=0) == S_OK
+
+
+def test_fused_prep_workspace(lib):
+    """The backward's workspace grows by the normalised-row gradients only when q, k are normalised inside."""
+    base = lib.kda_workspace_bytes(ctypes.byref(_desc()), 1)
+    norm = lib.kda_workspace_bytes(ctypes.byref(_desc(flags=kda.KDA_FLAG_QK_L2NORM)), 1)
+    gate = lib.kda_workspace_bytes(ctypes.byref(_desc(flags=kda.KDA_FLAG_GATE_LOGSIGMOID)), 1)
+    fwd = lib.kda_workspace_bytes(ctypes.byref(_desc(flags=kda.KDA_FLAG_QK_L2NORM)), 0)
+    assert gate == base and norm > base
+    assert fwd == lib.kda_workspace_bytes(ctypes.byref(_desc()), 0)
