@@ -82,7 +82,7 @@ def _short_name(name, train=True):
     if "kda_decode_step" in name:
         return "kda_decode_step"
     if "kda_prep" in name:
-        bwd = (_bools(name) or [False])[-1]
+        bwd = (_bools(name) or [False])[0]   # <..., BWD, QKN[, GATE]>
         return ("kda_prep_save" if train else "kda_prep_bwd") if bwd else "kda_prep"
     if "kda_state" in name:
         b = _bools(name)
