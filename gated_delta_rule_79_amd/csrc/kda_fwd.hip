@@ -465,8 +465,19 @@ struct Prep8Lds {
   static constexpr size_t BETA = X + 3 * 256 * 4;             // float [CH]
   static constexpr size_t RED = BETA + CH * 4;                // float [512]
   static constexpr size_t NRM = RED + 512 * 4;                // float [2][CH]  1/|q_r|, 1/|k_r| (QKN)
-  static constexpr size_t BYTES = NRM + 2 * CH * 4;
+  // decayed Gram blocks, one pass of GC channels at a time:
+  static constexpr int GC = 32;
+  static constexpr int LDQ = GC + 8;                          // bf16 [CH][LDQ]  k~, q~ (hi, lo)
+  static constexpr int LDR = GC + 4;                          // float [CH][LDR] k e^{g_m - g}
+  static constexpr size_t GKH = NRM + 2 * CH * 4;
+  static constexpr size_t GKL = GKH + (size_t)CH * LDQ * 2;
+  static constexpr size_t GQH = GKL + (size_t)CH * LDQ * 2;
+  static constexpr size_t GQL = GQH + (size_t)CH * LDQ * 2;
+  static constexpr size_t GKR = GQL + (size_t)CH * LDQ * 2;
+  static constexpr size_t GF = GKR + (size_t)CH * LDR * 4;   // float [6][GC]  e^{g_m(a) - g_m(b)}, b < a
+  static constexpr size_t BYTES = GF + 6 * GC * 4;
   static_assert(BYTES <= 163840, "prep LDS");
+  static_assert(GKH % 16 == 0 && GKR % 16 == 0 && GF % 16 == 0, "16-byte rows");
 };
 
 // C(16x16) += A(16x16) B(16x16), fp32 operands in LDS (row-major), fp32 MFMA.
@@ -647,60 +658,102 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       if (tid < DK) wGam[tid] = __expf(sG[(CH - 1) * L::LDG + tid]);
     }
 
-    // ---- decayed Gram blocks (split bf16 operands; reference row m = 16a + 8)
+    // ---- decayed Gram blocks (split bf16 operands; reference row m(b) = 16b + 8).
+    // Block (a, b), b <= a, of K+ K-^T is sum_c k~_r[c] (k_i[c] e^{g_m(b) - g_i}) e^{g_m(a) - g_m(b)}
+    // with k~_r = k_r e^{g_r - g_m(a)}; every factor stays within an 8-token decay.  The
+    // channels go in passes of GC: each pass tabulates k~ and q~ (split), k e^{g_m - g} and
+    // the block-to-block factors once, and every wave reads its operands as 16-byte rows.
+    // The ten blocks are dealt to the waves so each SIMD (waves w and w + 4) gets two or three.
     {
-      const int ab = w & 3, pp = w >> 2;
-      const int nb = ab + 1, split = (nb + 1) >> 1;
-      const int b0 = pp ? split : 0, b1 = pp ? nb : split;
-      const int ref = 16 * ab + 8;
-      if (b0 < b1) {
-        const int r = 16 * ab + r16;
-        SFrag<bf16> fk[NKS], fq[NKS];
+      constexpr int GC = L::GC, NPASS = DK / GC;
+      bf16* tKh = reinterpret_cast<bf16*>(smem + L::GKH);
+      bf16* tKl = reinterpret_cast<bf16*>(smem + L::GKL);
+      bf16* tQh = reinterpret_cast<bf16*>(smem + L::GQH);
+      bf16* tQl = reinterpret_cast<bf16*>(smem + L::GQL);
+      float* tKR = reinterpret_cast<float*>(smem + L::GKR);
+      float* tF = reinterpret_cast<float*>(smem + L::GF);
+      // this wave's blocks: list index w and w + 8 of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+      constexpr int BA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+      constexpr int BB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+      const int nblk = w < 2 ? 2 : 1;
+      f32x4 akk[2] = {zero4(), zero4()}, aqk[2] = {zero4(), zero4()};
+      static_assert(NT == CH * (GC / 4), "table build: one thread per (token, 4 channels)");
+      for (int ps = 0; ps < NPASS; ++ps) {
+        if (ps > 0) __syncthreads();   // the previous pass's table reads are done
+        {
+          const int r = tid / (GC / 4), cl0 = 4 * (tid % (GC / 4)), c0 = GC * ps + cl0;
+          const int mref = 16 * (r >> 4) + 8;
+          float ek[4], eq[4], kr[4];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int c0 = 32 * ks + 8 * q4;
-          float yk[8], yq[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float e = __expf(sG[r * L::LDG + c0 + u] - sG[ref * L::LDG + c0 + u]);
-            yk[u] = f32(sK[r * L::LDK + c0 + u]) * nk(r) * e;
-            yq[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * e;
+          for (int u = 0; u < 4; ++u) {
+            const float g = sG[r * L::LDG + c0 + u], gm = sG[mref * L::LDG + c0 + u];
+            const float e = __expf(g - gm);
+            const float kv = f32(sK[r * L::LDK + c0 + u]) * nk(r);
+            ek[u] = kv * e;
+            eq[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * e;
+            kr[u] = kv * __expf(gm - g);
           }
-          fk[ks] = sfrag_from<bf16>(yk);
-          fq[ks] = sfrag_from<bf16>(yq);
+          store4_split<bf16>(tKh + r * L::LDQ + cl0, tKl + r * L::LDQ + cl0, ek[0], ek[1], ek[2], ek[3]);
+          store4_split<bf16>(tQh + r * L::LDQ + cl0, tQl + r * L::LDQ + cl0, eq[0], eq[1], eq[2], eq[3]);
+          *reinterpret_cast<f32x4*>(tKR + r * L::LDR + cl0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+          if (tid < 6 * GC) {   // pair (a, b), b < a, in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+            const int pi = tid / GC, c = GC * ps + tid % GC;
+            const int pa = pi < 1 ? 1 : (pi < 3 ? 2 : 3), pb = pi < 1 ? 0 : (pi < 3 ? pi - 1 : pi - 3);
+            tF[tid] = __expf(sG[(16 * pa + 8) * L::LDG + c] - sG[(16 * pb + 8) * L::LDG + c]);
+          }
         }
-        for (int b = b0; b < b1; ++b) {
-          f32x4 akk = zero4(), aqk = zero4();
-          const int i = 16 * b + r16;
+        __syncthreads();
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            const int c0 = 32 * ks + 8 * q4;
+        for (int j = 0; j < 2; ++j) {
+          if (j < nblk) {
+            const int li = w + 8 * j, ba = BA[li], bb = BB[li];
+            const SFrag<bf16> fk = sfrag_pair<bf16>(tKh, tKl, L::LDQ, 16 * ba + r16, 8 * q4);
+            const SFrag<bf16> fq = sfrag_pair<bf16>(tQh, tQl, L::LDQ, 16 * ba + r16, 8 * q4);
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4 + 4);
             float xr[8];
+            if (bb == ba) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              xr[u] = f32(sK[i * L::LDK + c0 + u]) * nk(i) * __expf(sG[ref * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
+              for (int u = 0; u < 4; ++u) {
+                xr[u] = v0[u];
+                xr[u + 4] = v1[u];
+              }
+            } else {
+              const float* f = tF + GC * (ba * (ba - 1) / 2 + bb) + 8 * q4;
+              const f32x4 f0 = *reinterpret_cast<const f32x4*>(f), f1 = *reinterpret_cast<const f32x4*>(f + 4);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                xr[u] = v0[u] * f0[u];
+                xr[u + 4] = v1[u] * f1[u];
+              }
+            }
             const SFrag<bf16> fr = sfrag_from<bf16>(xr);
-            akk = mma_ss(fk[ks], fr, akk);
-            aqk = mma_ss(fq[ks], fr, aqk);
-          }
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int rr = 16 * ab + 4 * q4 + ii, cc = 16 * b + r16;
-            sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[ii] : 0.f;
-            wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[ii] : 0.f);
-            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[ii] : 0.f;
+            akk[j] = mma_ss(fk, fr, akk[j]);
+            aqk[j] = mma_ss(fq, fr, aqk[j]);
           }
         }
       }
-      if (pp) {
-        for (int b = nb; b < 4; ++b) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (j < nblk) {
+          const int li = w + 8 * j, ba = BA[li], bb = BB[li];
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
-            const int rr = 16 * ab + 4 * q4 + ii, cc = 16 * b + r16;
-            sA[rr * L::LDA + cc] = 0.f;
-            wAqk[rr * CH + cc] = cvt<OP>(0.f);
-            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = 0.f;
+            const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
+            sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[j][ii] : 0.f;
+            wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[j][ii] : 0.f);
+            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[j][ii] : 0.f;
           }
+        }
+      }
+      if (w < 6) {   // blocks above the diagonal: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int ba = w < 3 ? 0 : (w < 5 ? 1 : 2), bb = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
+          sA[rr * L::LDA + cc] = 0.f;
+          wAqk[rr * CH + cc] = cvt<OP>(0.f);
+          if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = 0.f;
         }
       }
     }
