@@ -34,6 +34,8 @@ struct Plan {
   size_t esz = 0;
   size_t chunks = 0, sc0 = 0, so = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
   size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0, DQK = 0;
+  int segs = 1;
+  size_t vsc0 = 0, vord = 0, seg_in = 0, seg_loc = 0, seg_m = 0;
   size_t total = 0;
 };
 
@@ -87,6 +89,16 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
     p.dS = take(nb * dk * dv * 4);
     p.dU = take(nb * dv * CH * 4);
     if (d->flags & KDA_FLAG_QK_L2NORM) p.DQK = take(nb * 2 * CH * dk * 4);   // dq^, dk^ before the norm's chain rule
+  } else {
+    p.segs = kda::fwd_segments(N, d->H, d->dv, (long long)d->B * d->T, false);
+    if (p.segs > 1) {   // segment scan buffers
+      const size_t nv = (size_t)N * p.segs;
+      p.vsc0 = take((nv + 1) * sizeof(int32_t));
+      p.vord = take(nv * sizeof(int32_t));
+      p.seg_in = take(nv * d->H * dk * dv * 4);
+      p.seg_loc = take(nv * d->H * dk * dv * 4);
+      p.seg_m = take(nv * d->H * dk * dk * 4);
+    }
   }
   p.total = o;
   return p;
@@ -131,6 +143,12 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
   a.wsdS = fptr(p.dS);
   a.wsdU = fptr(p.dU);
   a.wsDQK = fptr(p.DQK);
+  a.segs = p.segs;
+  a.vsc0 = p.vsc0 ? reinterpret_cast<int32_t*>(b + p.vsc0) : nullptr;
+  a.vord = p.vord ? reinterpret_cast<int32_t*>(b + p.vord) : nullptr;
+  a.seg_in = fptr(p.seg_in);
+  a.seg_loc = fptr(p.seg_loc);
+  a.seg_m = fptr(p.seg_m);
 }
 
 hipError_t run_fwd(const kda_desc* d, const Args& a, hipStream_t st) {

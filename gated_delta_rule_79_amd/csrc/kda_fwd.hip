@@ -30,6 +30,7 @@
 // exp(g_r - g_i) = exp(g_r - g_m) * exp(g_m - g_i), so no factor exceeds the
 // decay of 8 consecutive tokens.
 #include <algorithm>
+#include <cstdlib>
 
 #include "kda_internal.hpp"
 
@@ -879,8 +880,17 @@ struct StateLds {
 // PF = 2: operands of chunk n+2 are in flight while chunk n+1 waits in
 // registers (one work-group per CU); PF = 1: one set of staging registers, so
 // the kernel fits 4 waves per SIMD and two work-groups share a CU.
-template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int PF>
+// MODE 1: the transfer of a stretch of chunks instead of a state.  The chunk
+// step S' = Gamma_C S + Kh^T (U~ - W S) is affine in S; run from S = I with
+// U~ = 0 it gives M = prod_n (Diag(Gamma_C) - Kh_n^T W_n) (dk x dk, DV = DK),
+// and S_end = M S_start + (the same run from S = 0 with U~).  MODE 2: one
+// launch of both, the first half of the grid the runs from S = 0 (end states
+// to final_state), the second half the transfers (to seg_m).
+template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int PF, int MODE = 0>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4 : 1, PF == 1 ? 4 : 2))) void kda_state(const Args a) {
+  static_assert(MODE == 0 || (!OUT && !SAVE && DV == DK), "transfer runs keep only the end state");
+  const bool xf = MODE == 1 || (MODE == 2 && blockIdx.x >= gridDim.x / 2);
+  const int bid = (MODE == 2 && xf) ? (int)(blockIdx.x - gridDim.x / 2) : (int)blockIdx.x;
   using L = StateLds<E, DK, DV, DVS, OUT, SAVE>;
   using OP = typename L::OP;
   using WB = WsBlock<E, DK, DV>;
@@ -891,7 +901,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
   int unit, sl;
-  if (!xcd_unit(blockIdx.x, NSL, a.N * a.H, unit, sl)) return;
+  if (!xcd_unit(bid, NSL, a.N * a.H, unit, sl)) return;
   const int seq = a.seq_order[unit / a.H], h = unit % a.H, H = a.H;   // longest sequences first
   const int n0 = sl * DVS;
   const int l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
@@ -928,7 +938,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   O* gOut = reinterpret_cast<O*>(a.out);
   const float scale = a.scale;
   const float* gInit = a.init;
-  float* gFinal = a.final_state;
+  float* gFinal = (MODE == 2 && xf) ? a.seg_m : a.final_state;
 
   f32x4 S[SPW];
   const size_t st_off = ((size_t)seq * H + h) * DK * DV;
@@ -938,7 +948,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int ch = 16 * mt + 4 * q4 + ii, col = n0 + 16 * nt + r16;
-      S[i][ii] = (gInit && t < NST) ? gInit[st_off + (size_t)ch * DV + col] : 0.f;
+      if (xf)
+        S[i][ii] = (t < NST && ch == col) ? 1.f : 0.f;
+      else
+        S[i][ii] = (gInit && t < NST) ? gInit[st_off + (size_t)ch * DV + col] : 0.f;
     }
   }
 
@@ -964,7 +977,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       p.aqk.load(gAqk + b * WB::AQK, CH);
     }
     p.kht.load(gKhT + b * WB::KHT, CH);
-    p.ut.load(gUt + b * WB::UT + (size_t)n0 * CH, CH);  // UT == UTF element count
+    if (!xf) p.ut.load(gUt + b * WB::UT + (size_t)n0 * CH, CH);  // UT == UTF element count
     p.gam.load(gGam + b * WB::GAM, DK);
   };
   auto stage_store = [&](const Stage& p) __attribute__((always_inline)) {
@@ -974,7 +987,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       p.aqk.store(sAqk, L::LDT);
     }
     p.kht.store(sKhT, L::LDT);
-    p.ut.store(sUt, CH);
+    if (!xf) p.ut.store(sUt, CH);
     p.gam.store(sGam, DK);
   };
 
@@ -1008,8 +1021,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
         const f32x4 x = tile_mm<DK>([&](int rr, int k) { return frag_row<OP>(sW, L::LDK, 16 * w + rr, k); },
                                     [&](int rr, int k) { return frag_row<OP>(sST, L::LDK, 16 * nt + rr, k); },
                                     zero4());
-        float ut[4];
-        load4<UTT>(sUt + (16 * nt + r16) * CH + 16 * w + 4 * q4, ut);
+        float ut[4] = {0.f, 0.f, 0.f, 0.f};
+        if (!xf) load4<UTT>(sUt + (16 * nt + r16) * CH + 16 * w + 4 * q4, ut);
         store4<OP>(sUL + (16 * nt + r16) * L::LDT + 16 * w + 4 * q4, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2],
                    ut[3] - x[3]);
         if constexpr (SAVE) {
@@ -1117,27 +1130,154 @@ int pick_dvs(int units, int dv) {
 #endif
 }
 
-template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE>
-static hipError_t launch_state(const Args& a, hipStream_t st) {
+template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int MODE = 0>
+static hipError_t launch_state(const Args& a, hipStream_t st, const char* name = nullptr) {
   constexpr int NSL = DV / DVS;
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
-  const int grid = groups * 8 * NSL;
+  const int grid = groups * 8 * NSL * (MODE == 2 ? 2 : 1);
   if (grid == 0) return hipSuccess;
   constexpr int PF = KDA_STATE_PF;
-  KDA_TIMED(OUT ? (SAVE ? "kda_state_fwd_save" : "kda_state_fwd") : "kda_state_bwd_fwdpass", st,
-            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT, SAVE, PF>), dim3(grid), dim3(512), 0, st, a));
+  if (!name) name = OUT ? (SAVE ? "kda_state_fwd_save" : "kda_state_fwd") : "kda_state_bwd_fwdpass";
+  KDA_TIMED(name, st,
+            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT, SAVE, PF, MODE>), dim3(grid), dim3(512), 0, st, a));
   return hipGetLastError();
 }
 
-template <typename E, typename O, int DK, int DV, bool OUT, bool SAVE>
-static hipError_t launch_state_auto(const Args& a, hipStream_t st) {
+template <typename E, typename O, int DK, int DV, bool OUT, bool SAVE, int MODE = 0>
+static hipError_t launch_state_auto(const Args& a, hipStream_t st, const char* name = nullptr) {
+  const int units = a.N * a.H * (MODE == 2 ? 2 : 1);
   if constexpr (sizeof(E) == 2) {
-    if (pick_dvs(a.N * a.H, DV) == 64) return launch_state<E, O, DK, DV, 64, OUT, SAVE>(a, st);
-    return launch_state<E, O, DK, DV, 16, OUT, SAVE>(a, st);
+    if (pick_dvs(units, DV) == 64) return launch_state<E, O, DK, DV, 64, OUT, SAVE, MODE>(a, st, name);
+    return launch_state<E, O, DK, DV, 16, OUT, SAVE, MODE>(a, st, name);
   } else {
-    return launch_state<E, O, DK, DV, 32, OUT, SAVE>(a, st);
+    return launch_state<E, O, DK, DV, 32, OUT, SAVE, MODE>(a, st, name);
   }
+}
+
+// ---------------------------------------------------------------------------
+// segment scan (the single-GPU half of splitting one long sequence over
+// ranks): each sequence is cut into `segs` stretches of whole chunks.  Every
+// stretch runs in parallel twice: from S = 0 with U~ (its end state S_loc)
+// and as a transfer M from S = I without U~.  A short sequential scan per
+// (sequence, head) then gives each stretch its entering state,
+// S_in(p + 1) = M(p) S_in(p) + S_loc(p), and the ordinary state pass runs all
+// stretches at once from those states, writing the outputs.
+// ---------------------------------------------------------------------------
+int fwd_segments(int N, int H, int dv, long long tokens, bool save) {
+  if (const char* env = std::getenv("KDA_SEGMENTS")) {   // explicit stretch count (tests, tuning)
+    const int p = std::atoi(env);
+    if (p >= 1) return save ? 1 : std::min(p, 64);
+  }
+  if (save || N <= 0) return 1;
+  // enough stretches that 64-column slices give every CU a chain (measured on
+  // one 128K-token sequence with 16 heads: 8 stretches 3.8 ms, 4 stretches
+  // 4.8 ms, none 5.4 ms; more than 8 lose to the longer scan)
+  const long long units = (long long)N * H * std::max(1, dv / 64);
+  const long long avg_chunks = tokens / CH / N;
+  if (units >= device_cus() || avg_chunks < 256) return 1;
+  long long p = (device_cus() + units - 1) / units;
+  p = std::min<long long>(p, std::min<long long>(8, avg_chunks / 64));
+  return (int)std::max<long long>(p, 1);
+}
+
+__global__ __launch_bounds__(256) void kda_segment_map(const int32_t* __restrict__ sc0, int N, int P,
+                                                      int32_t* __restrict__ vsc0, int32_t* __restrict__ vord) {
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v <= N * P; v += gridDim.x * blockDim.x) {
+    if (v == N * P) {
+      vsc0[v] = sc0[N];
+    } else {
+      const int n = v / P, p = v % P;
+      const int c0 = sc0[n], nch = sc0[n + 1] - c0;
+      vsc0[v] = c0 + (int)((long long)nch * p / P);
+      vord[v] = v;
+    }
+  }
+}
+
+// One work-group per (sequence, head): S (fp32, [DK][DV]) and the stretch's
+// transfer M ([DK][DK]) in LDS; each wave owns 16x16 tiles of the new state and
+// forms them with fp32 MFMA (16 channels of the contraction per step, in order:
+// bitwise reproducible).
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void kda_segment_scan(const Args a) {
+  constexpr int LS = DV + 4, LM = DK + 4;   // padded rows
+  __shared__ __attribute__((aligned(16))) float sS[DK * LS];
+  __shared__ __attribute__((aligned(16))) float sM[DK * LM];
+  constexpr int NT = 512, NTILE = (DK / 16) * (DV / 16), TPW = (NTILE + 7) / 8;
+  const int n = blockIdx.x / a.H, h = blockIdx.x % a.H, P = a.segs, tid = threadIdx.x;
+  const int w = wave_id(), l = lane_id(), r16 = l & 15, q4 = l >> 4;
+  constexpr size_t SZ = (size_t)DK * DV, MZ = (size_t)DK * DK;
+  const float* init = a.init ? a.init + ((size_t)n * a.H + h) * SZ : nullptr;
+  for (int o = tid; o < DK * DV; o += NT) sS[(o / DV) * LS + o % DV] = init ? init[o] : 0.f;
+  __syncthreads();
+  for (int p = 0; p < P; ++p) {
+    const size_t v = ((size_t)n * P + p) * a.H + h;
+    for (int o = tid; o < DK * DV; o += NT) a.seg_in[v * SZ + o] = sS[(o / DV) * LS + o % DV];
+    for (int o = tid; o < DK * DK; o += NT) sM[(o / DK) * LM + o % DK] = a.seg_m[v * MZ + o];
+    __syncthreads();
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + 8 * i, mt = t % (DK / 16), nt = t / (DK / 16);
+      acc[i] = zero4();
+      if (t < NTILE) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          acc[i][ii] = a.seg_loc[v * SZ + (size_t)(16 * mt + 4 * q4 + ii) * DV + 16 * nt + r16];
+        for (int kb = 0; kb < DK / 16; ++kb)
+          acc[i] = mm16_f32(sM + 16 * mt * LM + 16 * kb, LM, sS + 16 * kb * LS + 16 * nt, LS, acc[i]);
+      }
+    }
+    __syncthreads();   // every read of this stretch's S and M is done
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + 8 * i, mt = t % (DK / 16), nt = t / (DK / 16);
+      if (t < NTILE) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sS[(16 * mt + 4 * q4 + ii) * LS + 16 * nt + r16] = acc[i][ii];
+      }
+    }
+    __syncthreads();
+  }
+  if (a.final_state)
+    for (int o = tid; o < DK * DV; o += NT) a.final_state[((size_t)n * a.H + h) * SZ + o] = sS[(o / DV) * LS + o % DV];
+}
+
+template <typename E, typename O, int DK, int DV>
+static hipError_t launch_segmented_state(const Args& a, hipStream_t st) {
+  const int P = a.segs, NV = a.N * P;
+  KDA_TIMED("kda_seg_map", st,
+            hipLaunchKernelGGL(kda_segment_map, dim3((NV + 256) / 256), dim3(256), 0, st, a.seq_chunk0, a.N, P,
+                               a.vsc0, a.vord));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  Args av = a;   // the stretches as sequences of their own
+  av.N = NV;
+  av.seq_chunk0 = a.vsc0;
+  av.seq_order = a.vord;
+  av.out = nullptr;
+  Args al = av;   // end state of each stretch from zero, and (same launch when dk == dv) its transfer
+  al.init = nullptr;
+  al.final_state = a.seg_loc;
+  if constexpr (DK == DV) {
+    if ((e = launch_state_auto<E, O, DK, DV, false, false, 2>(al, st, "kda_seg_local_transfer")) != hipSuccess)
+      return e;
+  } else {
+    if ((e = launch_state_auto<E, O, DK, DV, false, false>(al, st, "kda_seg_local")) != hipSuccess) return e;
+    Args am = av;
+    am.init = nullptr;
+    am.final_state = a.seg_m;
+    if ((e = launch_state_auto<E, O, DK, DK, false, false, 1>(am, st, "kda_seg_transfer")) != hipSuccess) return e;
+  }
+  KDA_TIMED("kda_seg_scan", st,
+            hipLaunchKernelGGL((kda_segment_scan<DK, DV>), dim3(a.N * a.H), dim3(512), 0, st, a));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  Args ab = av;   // every stretch from its true entering state, with the outputs
+  ab.out = a.out;
+  ab.init = a.seg_in;
+  ab.final_state = nullptr;
+  return launch_state_auto<E, O, DK, DV, true, false>(ab, st);
 }
 
 // BWD: also keep what the backward pass needs (T, the un-beta Gram, fp32 Kh and U~).
@@ -1187,6 +1327,7 @@ hipError_t launch_fwd(const Args& a, hipStream_t st, bool save) {
   }
   e = launch_prep<E, DK, DV, false>(a, st, "kda_prep");
   if (e != hipSuccess) return e;
+  if (a.segs > 1) return launch_segmented_state<E, O, DK, DV>(a, st);
   return launch_state_auto<E, O, DK, DV, true, false>(a, st);
 }
 

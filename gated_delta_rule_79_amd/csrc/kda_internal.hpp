@@ -46,6 +46,14 @@ struct Args {
   int gate_ls;              // log_alpha holds a raw gate x; log alpha = logsigmoid(x)
   float* wsDQK;             // backward with qk_norm: dq^, dk^ (normalised-input gradients),
                             // fp32 [2][CH][DK] per chunk-head
+  // segment scan of long sequences (forward): each sequence split into `segs`
+  // stretches of whole chunks that run in parallel
+  int segs;                 // 1: no segmentation
+  int32_t* vsc0;            // [N*segs + 1] first chunk of each stretch
+  int32_t* vord;            // [N*segs] stretch order (identity)
+  float* seg_in;            // [N*segs][H][DK][DV] state entering each stretch
+  float* seg_loc;           // [N*segs][H][DK][DV] end state of each stretch run from zero
+  float* seg_m;             // [N*segs][H][DK][DK] transfer of each stretch
 };
 
 // Decode / replay step (kda_decode).
@@ -76,6 +84,7 @@ void note_launch(const char* name);   // keeps the first failing launch of this 
 
 hipError_t launch_chunk_map(const Args& a, hipStream_t st);
 int device_cus();                  // compute units of the current device
+int fwd_segments(int N, int H, int dv, long long tokens, bool save);   // stretches per sequence (segment scan)
 int pick_dvs(int units, int dv);   // value-slice width of the sequential passes (bf16 inputs)
 template <typename E, typename O, int DK, int DV> hipError_t launch_fwd(const Args& a, hipStream_t st, bool save);
 template <typename E, int DK, int DV> hipError_t launch_bwd_front(const Args& a, hipStream_t st);
