@@ -204,3 +204,43 @@ def decode_inputs(B, T, H, dk, dv, pool_size, dtype="bf16", gate_mu=3.0, gate_sd
            (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta))}
     out["state_pool"] = np.ascontiguousarray(draw("state", (pool_size, H, dk, dv), 0.0, state_sd))
     return out
+
+
+def conv_inputs(lengths, D, W, dtype="bf16", seed=777, state=True) -> dict:
+    """Inputs of the short convolution over packed sequences (channels D = the
+    concatenated q, k, v channels of all heads in the benchmark shapes):
+    x [T, D] ~ N(0, 1) and dy [T, D] ~ N(0, 1) in the storage dtype;
+    weight [D, W] ~ U(-1/sqrt(W), 1/sqrt(W)) and bias [D] ~ N(0, 0.1) in float32;
+    per-sequence state and final-state gradient [N, W-1, D] ~ N(0, 1) in float32
+    (the state None when state=False)."""
+    def draw(name, shape, sd=1.0):
+        return _rng(seed, "conv_" + name).standard_normal(size=shape, dtype=np.float32) * np.float32(sd)
+
+    lengths = [int(n) for n in lengths]
+    T, N = int(sum(lengths)), len(lengths)
+    lim = np.float32(1.0 / np.sqrt(W))
+    return dict(
+        x=np.ascontiguousarray(_store(draw("x", (T, D)), dtype)),
+        dy=np.ascontiguousarray(_store(draw("dy", (T, D)), dtype)),
+        weight=_rng(seed, "conv_weight").uniform(-lim, lim, size=(D, W)).astype(np.float32),
+        bias=draw("bias", (D,), 0.1),
+        init_state=draw("state", (N, W - 1, D)) if state else None,
+        d_final_state=draw("d_final", (N, W - 1, D)),
+        cu_seqlens=lengths_to_cu(lengths),
+    )
+
+
+def conv_decode_inputs(B, T, D, W, pool_size, dtype="bf16", seed=778) -> dict:
+    """Inputs of a short-convolution decode step: x [B, T, D] ~ N(0, 1) in the
+    storage dtype, weight and bias as in conv_inputs, and a float32 pool of
+    states [pool_size, W-1, D] ~ N(0, 1)."""
+    def draw(name, shape, sd=1.0):
+        return _rng(seed, "convdec_" + name).standard_normal(size=shape, dtype=np.float32) * np.float32(sd)
+
+    lim = np.float32(1.0 / np.sqrt(W))
+    return dict(
+        x=np.ascontiguousarray(_store(draw("x", (B, T, D)), dtype)),
+        weight=_rng(seed, "convdec_weight").uniform(-lim, lim, size=(D, W)).astype(np.float32),
+        bias=draw("bias", (D,), 0.1),
+        state_pool=draw("state", (pool_size, W - 1, D)),
+    )

@@ -13,6 +13,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
+from oracle import short_conv as sc
 
 RNG_SEED = 20261202
 
@@ -487,4 +488,133 @@ def pin_fused_prep_gate_limits(lib):
 
 FUSED_PREP_PINS = [pin_fused_prep_finite_differences, pin_fused_prep_row_scale_invariance,
                    pin_fused_prep_gate_limits]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS + FUSED_PREP_PINS
+
+
+# ---------------------------------------------------------------------------
+# short convolution (oracle/short_conv.py): a causal depthwise convolution along
+# time with a state of the last W - 1 inputs
+# ---------------------------------------------------------------------------
+def _conv_case(rng, lengths, D, W, state=True):
+    T = int(sum(lengths))
+    N = len(lengths)
+    return dict(x=rng.standard_normal((T, D)), weight=rng.standard_normal((D, W)), bias=rng.standard_normal(D),
+                init_state=rng.standard_normal((N, W - 1, D)) if state else None,
+                cu_seqlens=np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64))
+
+
+def pin_conv_textbook(lib):
+    """No state, no bias, identity: each sequence and channel is numpy's full convolution with the
+    reversed taps, cut to the sequence length (zero history before the first token)."""
+    rng = np.random.default_rng(RNG_SEED + 40)
+    for W in (2, 3, 4):
+        c = _conv_case(rng, [7, 1, 0, 12, 2], D=5, W=W, state=False)
+        y, fin = sc.short_conv_fwd(c["x"], c["weight"], c["cu_seqlens"])
+        for n in range(len(c["cu_seqlens"]) - 1):
+            a, e = c["cu_seqlens"][n], c["cu_seqlens"][n + 1]
+            for ch in range(5 if e > a else 0):   # np.convolve takes no empty input
+                ref = np.convolve(c["x"][a:e, ch], c["weight"][ch, ::-1])[: e - a]
+                _close(y[a:e, ch], ref, 1e-13, f"W={W} seq {n} ch {ch} vs np.convolve")
+            # the state after a sequence holds its last W - 1 inputs (zeros where it is shorter)
+            L = e - a
+            for r in range(W - 1):
+                t = L - (W - 1) + r
+                _close(fin[n, r], c["x"][a + t] if t >= 0 else np.zeros(5), 0.0, f"W={W} seq {n} final row {r}")
+
+
+def pin_conv_state_carries_across_a_split(lib):
+    """Running a sequence in two pieces, the first piece's final state as the second's initial state,
+    equals one run over the whole sequence (outputs and final state), for every split point."""
+    rng = np.random.default_rng(RNG_SEED + 41)
+    for W in (2, 4):
+        c = _conv_case(rng, [9], D=3, W=W)
+        y, fin = sc.short_conv_fwd(c["x"], c["weight"], c["cu_seqlens"], bias=c["bias"], init_state=c["init_state"],
+                                   silu=True)
+        for cut in range(0, 10):
+            y1, f1 = sc.short_conv_fwd(c["x"][:cut], c["weight"], [0, cut], bias=c["bias"],
+                                       init_state=c["init_state"], silu=True)
+            y2, f2 = sc.short_conv_fwd(c["x"][cut:], c["weight"], [0, 9 - cut], bias=c["bias"], init_state=f1,
+                                       silu=True)
+            _close(np.concatenate([y1, y2]), y, 1e-13, f"W={W} split at {cut}: outputs")
+            _close(f2, fin, 0.0, f"W={W} split at {cut}: final state")
+
+
+def pin_conv_bias_and_silu(lib):
+    """The bias shifts the pre-activation; SiLU is z * sigmoid(z) of it (scipy's expit), with
+    silu(0) = 0 and silu(z) -> z for large z."""
+    from scipy.special import expit
+    rng = np.random.default_rng(RNG_SEED + 42)
+    c = _conv_case(rng, [6, 4], D=4, W=3)
+    z0, _ = sc.short_conv_fwd(c["x"], c["weight"], c["cu_seqlens"], init_state=c["init_state"])
+    y, _ = sc.short_conv_fwd(c["x"], c["weight"], c["cu_seqlens"], bias=c["bias"], init_state=c["init_state"],
+                             silu=True)
+    z = z0 + c["bias"]
+    _close(y, z * expit(z), 1e-13, "bias + SiLU")
+    x = np.zeros((3, 1))
+    big = sc.short_conv_fwd(x, np.zeros((1, 2)), [0, 3], bias=np.array([40.0]), silu=True)[0]
+    zero = sc.short_conv_fwd(x, np.zeros((1, 2)), [0, 3], silu=True)[0]
+    _close(zero, np.zeros((3, 1)), 0.0, "silu(0)")
+    _close(big, np.full((3, 1), 40.0), 1e-12, "silu(40)")
+
+
+def _conv_loss(c, dy, dfin, silu):
+    y, fin = sc.short_conv_fwd(c["x"], c["weight"], c["cu_seqlens"], bias=c["bias"], init_state=c["init_state"],
+                               silu=silu)
+    return float(np.sum(y * dy) + np.sum(fin * dfin))
+
+
+def pin_conv_backward_finite_differences(lib):
+    """Every gradient (x, weight, bias, initial state) == central differences of
+    <dy, y> + <d_final, final_state>, over sequences longer and shorter than W - 1 and an empty one."""
+    rng = np.random.default_rng(RNG_SEED + 43)
+    for W, silu in ((4, True), (3, False), (2, True)):
+        c = _conv_case(rng, [6, 2, 0, 1, 5], D=2, W=W)
+        dy = rng.standard_normal(c["x"].shape)
+        dfin = rng.standard_normal(c["init_state"].shape)
+        g = sc.short_conv_bwd(c["x"], c["weight"], c["cu_seqlens"], dy, bias=c["bias"], init_state=c["init_state"],
+                              d_final_state=dfin, silu=silu)
+        h = 1e-6
+        for name, grad in (("x", g[0]), ("weight", g[1]), ("bias", g[2]), ("init_state", g[3])):
+            v = c[name]
+            num = np.zeros_like(v)
+            for idx in np.ndindex(v.shape):
+                old = v[idx]
+                v[idx] = old + h
+                lp = _conv_loss(c, dy, dfin, silu)
+                v[idx] = old - h
+                lm = _conv_loss(c, dy, dfin, silu)
+                v[idx] = old
+                num[idx] = (lp - lm) / (2 * h)
+            _close(grad, num, 1e-6, f"W={W} silu={silu}: d{name} vs central differences")
+
+
+def pin_conv_decode_is_forward_from_the_slot(lib):
+    """A decode step equals the forward over the same tokens started from the slot's state; the
+    committed slot holds the state after the committed prefix; padding entries leave everything alone."""
+    rng = np.random.default_rng(RNG_SEED + 44)
+    B, T, D, W, P = 4, 5, 3, 4, 6
+    x = rng.standard_normal((B, T, D))
+    w = rng.standard_normal((D, W))
+    bias = rng.standard_normal(D)
+    pool = rng.standard_normal((P, W - 1, D))
+    idx = np.array([3, -1, 0, 5])
+    nc = np.array([5, 2, 0, 2])
+    y, new = sc.short_conv_decode(x, w, pool, bias=bias, state_indices=idx, num_commit=nc, silu=True)
+    touched = set()
+    for b in range(B):
+        if idx[b] < 0:
+            _close(y[b], np.zeros((T, D)), 0.0, "padding outputs")
+            continue
+        yf, _ = sc.short_conv_fwd(x[b], w, [0, T], bias=bias, init_state=pool[idx[b]][None], silu=True)
+        _close(y[b], yf, 1e-13, f"decode seq {b} outputs")
+        if nc[b] > 0:
+            _, fp = sc.short_conv_fwd(x[b, : nc[b]], w, [0, nc[b]], bias=bias, init_state=pool[idx[b]][None])
+            _close(new[idx[b]], fp[0], 0.0, f"decode seq {b} committed state")
+            touched.add(int(idx[b]))
+    for s in range(P):
+        if s not in touched:
+            _close(new[s], pool[s], 0.0, f"slot {s} untouched")
+
+
+SHORT_CONV_PINS = [pin_conv_textbook, pin_conv_state_carries_across_a_split, pin_conv_bias_and_silu,
+                   pin_conv_backward_finite_differences, pin_conv_decode_is_forward_from_the_slot]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + DECODE_PINS + FUSED_PREP_PINS + SHORT_CONV_PINS

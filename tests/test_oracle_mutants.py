@@ -66,3 +66,37 @@ def test_mutant_is_caught(name, old, new, idx):
             except AssertionError as e:
                 failures.append(f"{pin.__name__}: {e}")
         assert failures, f"mutant {name} passed every pin"
+
+
+# Mutants of the short-convolution oracle (oracle/short_conv.py), run against its pins.
+CONV_SRC = os.path.join(os.path.dirname(oracle.__file__), "short_conv.py")
+CONV_MUTANTS = [
+    ("conv_taps_reversed", "z += weight[:, j] * xe[j:j + L]", "z += weight[:, W - 1 - j] * xe[j:j + L]", 0),
+    ("conv_state_rows_reversed", "np.concatenate([s0, xs], axis=0)", "np.concatenate([s0[::-1], xs], axis=0)", 0),
+    ("conv_final_state_not_advanced", "fin[n] = xe[L:]", "fin[n] = xe[:W - 1]", 0),
+    ("conv_bwd_drops_final_grad", "dxe[L:] += dfin[n]", "dxe[L:] += 0.0 * dfin[n]", 0),
+    ("conv_bwd_silu_grad_is_sigmoid", "return s * (1.0 + z * (1.0 - s))", "return s", 0),
+    ("conv_bwd_weight_taps_reversed", "dw[:, j] += np.sum", "dw[:, W - 1 - j] += np.sum", 0),
+    ("conv_decode_commit_off_by_one", "pool[slot] = xe[n:n + W - 1]", "pool[slot] = xe[n - 1:n + W - 2]", 0),
+]
+
+
+@pytest.mark.parametrize("name,old,new,idx", CONV_MUTANTS, ids=[m[0] for m in CONV_MUTANTS])
+def test_conv_mutant_is_caught(name, old, new, idx, monkeypatch):
+    import importlib.util
+    text = open(CONV_SRC).read()
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "short_conv_mutant.py")
+        with open(src, "w") as f:
+            f.write(_mutant_source(text, old, new, idx))
+        spec = importlib.util.spec_from_file_location("short_conv_mutant", src)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+    monkeypatch.setattr(oracle_pins, "sc", mod)
+    failures = []
+    for pin in oracle_pins.SHORT_CONV_PINS:
+        try:
+            pin(None)
+        except (AssertionError, ValueError) as e:
+            failures.append(f"{pin.__name__}: {e}")
+    assert failures, f"mutant {name} passed every pin"
