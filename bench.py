@@ -36,19 +36,28 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")   # training-s
 
 def traffic_file(workload):
     """Counter summary of a workload: the training step's file, or one named after the workload."""
-    if workload.startswith("decode_"):
+    if workload.startswith(("decode_", "conv_")):
         return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     return TRAFFIC_FILE
 
 
-def sources_digest():
-    """sha256 over the HIP sources: counters taken from other sources are stale."""
+CONV_SOURCES = ("kda_conv.hip", "kda_conv.hpp")
+
+
+def sources_digest(workload=""):
+    """sha256 over the sources a workload's kernels are built from: counters taken from other sources
+    are stale.  The convolution workload hashes its own kernel files; the KDA workloads every other file."""
     import hashlib
     h = hashlib.sha256()
+    conv = workload.startswith("conv_")
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+        if not name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            continue
+        if (name in CONV_SOURCES) != conv and not (conv and name in ("kda_common.hpp", "kda_internal.hpp",
+                                                                      "kda_api.cpp")):
+            continue
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -114,7 +123,7 @@ def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
         kernels[short] = {"fetch_kib": fk, "write_kib": wk,
                           "read_bytes": fk * 1024.0 * scale_f, "write_bytes": wk * 1024.0 * scale_w,
                           "bytes": fk * 1024.0 * scale_f + wk * 1024.0 * scale_w}
-    doc = {"workload": workload, "sources_sha256": sources_digest(),
+    doc = {"workload": workload, "sources_sha256": sources_digest(workload),
            "calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": f_kib, "copy_write_kib": w_kib,
                            "fetch_scale": scale_f, "write_scale": scale_w},
            "kernels": kernels}
@@ -131,7 +140,7 @@ def measured_traffic(kernel, workload):
         doc = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
-    if doc.get("workload") != workload or doc.get("sources_sha256") != sources_digest():
+    if doc.get("workload") != workload or doc.get("sources_sha256") != sources_digest(workload):
         return None
     k = doc.get("kernels", {}).get(kernel)
     return int(k["bytes"]) if k else None
@@ -308,6 +317,102 @@ def decode_bench(args, dev) -> int:
     return 0
 
 
+CONV_METRIC = "short causal convolution fwd+bwd tokens/s and % HBM roofline, D=6144 W=4 SiLU bf16"
+
+
+def conv_bench(args, dev) -> int:
+    """One step = kda_conv_fwd then kda_conv_bwd over the training step's eight packed sequences
+    (lengths of the varlen workload), D = 3 x 16 heads x 128 channels (the q, k, v channels a
+    short convolution precedes KDA with), W = 4, SiLU, bf16 inputs, fp32 states and weights."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_79_amd as kda
+    import kda_inputs as ki
+    D, W = 6144, 4
+    lengths = list(ki.config(4).lengths)
+    tokens, N = int(sum(lengths)), len(lengths)
+    eout = 2 if args.out_bf16 else 4
+    odt = torch.bfloat16 if args.out_bf16 else torch.float32
+    print(f"[bench] conv inputs: {N} sequences, {tokens} tokens, D={D}, W={W}", file=sys.stderr, flush=True)
+    c = ki.conv_inputs(lengths, D, W, dtype="bf16", seed=4)
+    g = {n: torch.from_numpy(c[n]).to(dev, torch.bfloat16).unsqueeze(0) for n in ("x", "dy")}
+    p = {n: torch.from_numpy(c[n]).to(dev) for n in ("weight", "bias", "init_state", "d_final_state")}
+    cu = torch.from_numpy(c["cu_seqlens"]).to(dev)
+    y = torch.empty((1, tokens, D), dtype=odt, device=dev)
+    fin = torch.empty((N, W - 1, D), dtype=torch.float32, device=dev)
+    dx = torch.empty((1, tokens, D), dtype=odt, device=dev)
+    dw = torch.empty((D, W), dtype=torch.float32, device=dev)
+    db = torch.empty((D,), dtype=torch.float32, device=dev)
+    dinit = torch.empty_like(fin)
+    ws = torch.empty(max(kda.conv_workspace_bytes(1, tokens, D, W, torch.bfloat16), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        kda.conv_fwd(g["x"], p["weight"], p["bias"], p["init_state"], cu_seqlens=cu, silu=True, out=y,
+                     final_state=fin, out_dtype=odt)
+        kda.conv_bwd(g["x"], p["weight"], g["dy"], p["bias"], p["init_state"], p["d_final_state"], cu_seqlens=cu,
+                     silu=True, out_dtype=odt, workspace=ws, dx=dx, dweight=dw, dbias=db, d_init=dinit)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} conv steps", file=sys.stderr, flush=True)
+    kda.timing_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    kt = kda.timing_read()
+    kda.timing_enable(False)
+    # algorithmic bytes per launch: the forward reads x and writes y; the backward reads x and dy and
+    # writes dx (states, weights and the per-channel sums are under 0.1% and left out)
+    alg = {"kda_conv_fwd": tokens * D * (2 + eout), "kda_conv_bwd": tokens * D * (2 + 2 + eout)}
+    step_bytes = sum(alg.values())
+    dom = max(alg, key=lambda k: kt[k][0])
+    tot_ms, n_launch = kt[dom]
+    avg_ms = tot_ms / max(n_launch, 1)
+    ach = alg[dom] / (avg_ms * 1e-3) / 1e9
+    wl = f"conv_varlen8_D{D}_W{W}"
+    roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, wl), "kernel": dom,
+            "avg_launch_ms": round(avg_ms, 5), "launches": n_launch, "alg_bytes_per_launch": int(alg[dom])}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import short_conv as sc
+        nch = 96
+        ch = np.arange(0, D, D // nch)[:nch]
+        sub = lambda a: np.ascontiguousarray(a[..., ch])  # noqa: E731
+        t0 = time.perf_counter()
+        sc.short_conv_fwd(sub(c["x"]), c["weight"][ch], c["cu_seqlens"], bias=c["bias"][ch],
+                          init_state=sub(c["init_state"]), silu=True)
+        sc.short_conv_bwd(sub(c["x"]), c["weight"][ch], c["cu_seqlens"], sub(c["dy"]), bias=c["bias"][ch],
+                          init_state=sub(c["init_state"]), d_final_state=sub(c["d_final_state"]), silu=True)
+        dt_cpu = time.perf_counter() - t0
+        cpu = {"value": round(tokens * nch / D / dt_cpu, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{nch} of the {D} channels (every {D // nch}th), all {tokens} tokens, fwd+bwd "
+                         f"(float64 numpy, one thread), {dt_cpu:.1f} s; value = tokens x {nch}/{D} / s"}
+    line = {
+        "metric": CONV_METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "tokens": tokens, "sequences": N, "D": D, "W": W, "activation": "silu",
+                   "out_dtype": "bf16" if args.out_bf16 else "f32", "pass": "fwd+bwd"},
+        "roofline": roof,
+        "step_roofline": {"alg_bytes": int(step_bytes), "roofline_ms": round(step_bytes / HBM_PEAK_GBS / 1e6, 4),
+                          "frac": round(step_bytes / HBM_PEAK_GBS / 1e6 / ms_step, 4), "bound": "hbm"},
+        "kernels_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in kt.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +430,9 @@ def main() -> int:
     ap.add_argument("--decode", default=None, metavar="B,T",
                     help="time the decode / replay step instead: B sequences x T tokens (e.g. 512,4), H=16, "
                          "d=128, bf16, states gathered from a pool through a permuted index list, all T committed")
+    ap.add_argument("--conv", action="store_true",
+                    help="time the short causal convolution (forward + backward) on the varlen workload's lengths, "
+                         "D=6144, W=4, SiLU, instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -333,7 +441,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.ingest_counters:
         import kda_inputs as ki
-        wl = ("decode_B{}_T{}".format(*args.decode.split(",")) if args.decode else ki.config(args.config).name)
+        wl = ("decode_B{}_T{}".format(*args.decode.split(",")) if args.decode else
+              "conv_varlen8_D6144_W4" if args.conv else ki.config(args.config).name)
         doc = ingest_counters(*args.ingest_counters, copy_bytes=1024 << 20, workload=wl)
         print(json.dumps(doc["calibration"]))
         for k, v in sorted(doc["kernels"].items()):
@@ -368,6 +477,8 @@ def main() -> int:
     kda.load_library()
     if args.decode:
         return decode_bench(args, dev)
+    if args.conv:
+        return conv_bench(args, dev)
 
     w = ki.config(args.config)
     fwd_only = args.fwd_only or not w.backward

@@ -7,6 +7,8 @@ module raises on use; there is no fallback implementation.
 
     o, S_T = fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None)
     dq, dk, dv, dlog_alpha, dbeta, d_init = bwd(q, k, v, log_alpha, beta, d_out, ...)
+    out = decode(q, k, v, log_alpha, beta, state_pool, state_indices, num_commit)
+    y, conv_state = conv_fwd(x, weight, bias, init_state, cu_seqlens, silu=True)   # short convolution
 
 Shapes: q, k, log_alpha [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H]; all of
 one dtype (torch.float32 or torch.bfloat16), contiguous, on the GPU.  States
@@ -18,8 +20,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "workspace_bytes", "KdaError", "lib_path", "load_library", "status_string", "timing_enable",
-           "timing_read"]
+__all__ = ["fwd", "bwd", "decode", "workspace_bytes", "conv_fwd", "conv_bwd", "conv_decode", "conv_workspace_bytes",
+           "KdaError", "lib_path", "load_library", "status_string", "timing_enable", "timing_read"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -39,6 +41,15 @@ class kda_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+class kda_conv_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("activation", ctypes.c_int32)]
+
+
+KDA_CONV_IDENTITY, KDA_CONV_SILU = 0, 1
 
 
 class KdaError(RuntimeError):
@@ -77,6 +88,15 @@ def load_library(path: str | None = None):
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_decode.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P]
     lib.kda_decode.restype = ctypes.c_int
+    CD = ctypes.POINTER(kda_conv_desc)
+    lib.kda_conv_workspace_bytes.argtypes = [CD]
+    lib.kda_conv_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_conv_fwd.argtypes = [CD, P, P, P, P, P, P, P, P]
+    lib.kda_conv_fwd.restype = ctypes.c_int
+    lib.kda_conv_bwd.argtypes = [CD, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_conv_bwd.restype = ctypes.c_int
+    lib.kda_conv_decode.argtypes = [CD, P, P, P, P, ctypes.c_int32, P, P, P, P]
+    lib.kda_conv_decode.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_timing_enable.argtypes = [ctypes.c_int]
@@ -313,4 +333,138 @@ def decode(q, k, v, log_alpha, beta, state_pool, state_indices=None, num_commit=
                         _ptr(out), _stream(dev))
     if rc:
         raise KdaError("kda_decode", rc)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# short causal convolution with a carried state (kda_conv_* in include/kda.h)
+# ---------------------------------------------------------------------------
+def _conv_desc(x, W, cu_seqlens, out_dtype, silu, decode=False):
+    import torch
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, D]")
+    B, T, D = x.shape
+    if x.device.type != "cuda":
+        raise ValueError("inputs must be on the GPU")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    N = B
+    if cu_seqlens is not None:
+        if decode or B != 1:
+            raise ValueError("cu_seqlens requires B == 1 (and is not used by the decode step)")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != x.device:
+            raise ValueError("cu_seqlens must be int32 [N+1] on the GPU")
+        N = cu_seqlens.shape[0] - 1
+    odt = torch.float32 if out_dtype is None else out_dtype
+    d = kda_conv_desc(int(B), int(T), int(D), int(W), int(N) if cu_seqlens is not None else 0, _dtype_code(x.dtype),
+                      _dtype_code(odt), KDA_CONV_SILU if silu else KDA_CONV_IDENTITY)
+    return d, (B, T, D, N), odt
+
+
+def _conv_params(weight, bias, D, dev):
+    import torch
+    if weight.dim() != 2 or weight.shape[0] != D:
+        raise ValueError("weight must be float32 [D, W]")
+    _check("weight", weight, torch.float32, (D, weight.shape[1]), dev)
+    if bias is not None:
+        _check("bias", bias, torch.float32, (D,), dev)
+    return int(weight.shape[1])
+
+
+def conv_workspace_bytes(B, T, D, W, dtype) -> int:
+    """Workspace bytes of conv_bwd (partial sums of dweight and dbias)."""
+    import torch
+    code = _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    d = kda_conv_desc(int(B), int(T), int(D), int(W), 0, code, KDA_F32, 0)
+    return int(load_library().kda_conv_workspace_bytes(ctypes.byref(d)))
+
+
+def conv_fwd(x, weight, bias=None, init_state=None, cu_seqlens=None, silu=False, out=None, final_state=None,
+             output_final_state=True, out_dtype=None):
+    """Short causal convolution: x [B, T, D] (or packed [1, T, D] with cu_seqlens), weight float32 [D, W],
+    bias float32 [D] or None, init_state float32 [N, W-1, D] or None.  Returns (y [B, T, D] in out_dtype
+    (default float32), final_state float32 [N, W-1, D] or None)."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    W = _conv_params(weight, bias, x.shape[-1], dev)
+    desc, (B, T, D, N), odt = _conv_desc(x, W, cu_seqlens, out_dtype, silu)
+    if init_state is not None:
+        _check("init_state", init_state, torch.float32, (N, W - 1, D), dev)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=odt, device=dev)
+    else:
+        _check("out", out, odt, (B, T, D), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, W - 1, D), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check("final_state", final_state, torch.float32, (N, W - 1, D), dev)
+    rc = lib.kda_conv_fwd(ctypes.byref(desc), _ptr(x), _ptr(weight), _ptr(bias), _ptr(init_state), _ptr(out),
+                          _ptr(final_state), _ptr(cu_seqlens), _stream(dev))
+    if rc:
+        raise KdaError("kda_conv_fwd", rc)
+    return out, final_state
+
+
+def conv_bwd(x, weight, dy, bias=None, init_state=None, d_final_state=None, cu_seqlens=None, silu=False,
+             out_dtype=None, need_d_bias=True, need_d_init=True, workspace=None, dx=None, dweight=None,
+             dbias=None, d_init=None):
+    """Gradients of <dy, y> + <d_final_state, final_state>: returns (dx in out_dtype (default float32),
+    dweight float32 [D, W], dbias float32 [D] or None, d_init_state float32 [N, W-1, D] or None)."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    W = _conv_params(weight, bias, x.shape[-1], dev)
+    desc, (B, T, D, N), odt = _conv_desc(x, W, cu_seqlens, out_dtype, silu)
+    _check("dy", dy, x.dtype, (B, T, D), dev)
+    for name, t in (("init_state", init_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check(name, t, torch.float32, (N, W - 1, D), dev)
+    dx = torch.empty((B, T, D), dtype=odt, device=dev) if dx is None else dx
+    _check("dx", dx, odt, (B, T, D), dev)
+    dweight = torch.empty((D, W), dtype=torch.float32, device=dev) if dweight is None else dweight
+    _check("dweight", dweight, torch.float32, (D, W), dev)
+    if dbias is None and need_d_bias:
+        dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    if dbias is not None:
+        _check("dbias", dbias, torch.float32, (D,), dev)
+    if d_init is None and need_d_init:
+        d_init = torch.empty((N, W - 1, D), dtype=torch.float32, device=dev)
+    if d_init is not None:
+        _check("d_init", d_init, torch.float32, (N, W - 1, D), dev)
+    need = lib.kda_conv_workspace_bytes(ctypes.byref(desc))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.kda_conv_bwd(ctypes.byref(desc), _ptr(x), _ptr(weight), _ptr(bias), _ptr(init_state),
+                          _ptr(cu_seqlens), _ptr(dy), _ptr(d_final_state), _ptr(dx), _ptr(dweight), _ptr(dbias),
+                          _ptr(d_init), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    if rc:
+        raise KdaError("kda_conv_bwd", rc)
+    return dx, dweight, dbias, d_init
+
+
+def conv_decode(x, weight, state_pool, bias=None, state_indices=None, num_commit=None, silu=False, out=None,
+                out_dtype=None):
+    """Decode / replay step of the convolution: x [B, T, D]; state_pool float32 [P, W-1, D] updated in place;
+    state_indices / num_commit int32 [B] as for decode().  Returns y [B, T, D] (out_dtype, default float32)."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    W = _conv_params(weight, bias, x.shape[-1], dev)
+    desc, (B, T, D, _), odt = _conv_desc(x, W, None, out_dtype, silu, decode=True)
+    if state_pool.dim() != 3:
+        raise ValueError("state_pool must be [P, W-1, D]")
+    _check("state_pool", state_pool, torch.float32, (state_pool.shape[0], W - 1, D), dev)
+    for name, t in (("state_indices", state_indices), ("num_commit", num_commit)):
+        if t is not None:
+            _check(name, t, torch.int32, (B,), dev)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=odt, device=dev)
+    else:
+        _check("out", out, odt, (B, T, D), dev)
+    rc = lib.kda_conv_decode(ctypes.byref(desc), _ptr(x), _ptr(weight), _ptr(bias), _ptr(state_pool),
+                             int(state_pool.shape[0]), _ptr(state_indices), _ptr(num_commit), _ptr(out),
+                             _stream(dev))
+    if rc:
+        raise KdaError("kda_conv_decode", rc)
     return out

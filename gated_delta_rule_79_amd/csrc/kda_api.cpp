@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "kda_internal.hpp"
+#include "kda_conv.hpp"
 
 namespace {
 
@@ -199,6 +200,64 @@ hipError_t run_decode(const kda_desc* d, const kda::DecodeArgs& a, hipStream_t s
   KDA_CASE(128, 64)
   KDA_CASE(128, 128)
 #undef KDA_CASE
+  return hipErrorInvalidValue;
+}
+
+// Short convolution: checks shared by the three entry points.
+bool conv_desc_ok(const kda_conv_desc* d) {
+  return d->W >= 2 && d->W <= 4 && d->D > 0 && d->D % 8 == 0 &&
+         (d->dtype == KDA_F32 || d->dtype == KDA_BF16) &&
+         (d->out_dtype == KDA_F32 || (d->out_dtype == KDA_BF16 && d->dtype == KDA_BF16)) &&
+         (d->activation == KDA_CONV_IDENTITY || d->activation == KDA_CONV_SILU);
+}
+
+// Sequences of a forward/backward call; false on a bad shape.
+bool conv_shape(const kda_conv_desc* d, bool varlen, int* N) {
+  if (d->B < 1 || d->T < 0) return false;
+  if ((long long)d->B * d->T * d->D >= (1LL << 40) || (long long)d->B * d->T >= (1LL << 31)) return false;
+  if (varlen) {
+    if (d->B != 1 || d->num_seqs < 1) return false;
+    *N = d->num_seqs;
+  } else {
+    *N = d->B;
+  }
+  return *N <= 65535;
+}
+
+size_t conv_ws_bytes(const kda_conv_desc* d) {
+  const long long tok = (long long)d->B * d->T;
+  const size_t tiles = (size_t)((tok + kda::CONV_BWD_TILE - 1) / kda::CONV_BWD_TILE);
+  return tiles * (size_t)(d->W + 1) * (size_t)d->D * sizeof(float);
+}
+
+void conv_args(kda::ConvArgs& c, const kda_conv_desc* d, int N) {
+  std::memset(&c, 0, sizeof c);
+  c.B = d->B;
+  c.T = d->T;
+  c.D = d->D;
+  c.N = N;
+  c.tokens = d->B * d->T;
+  c.silu = d->activation == KDA_CONV_SILU;
+}
+
+enum class ConvOp { Fwd, Bwd, Decode };
+hipError_t run_conv(const kda_conv_desc* d, const kda::ConvArgs& c, ConvOp op, hipStream_t st) {
+  const bool bf = d->dtype == KDA_BF16, obf = d->out_dtype == KDA_BF16;
+#define KDA_CONV_CALL(E, O, W)                                                   \
+  return op == ConvOp::Fwd   ? kda::launch_conv_fwd<E, O, W>(c, st)              \
+         : op == ConvOp::Bwd ? kda::launch_conv_bwd<E, O, W>(c, st)              \
+                             : kda::launch_conv_decode<E, O, W>(c, st);
+#define KDA_CONV_CASE(KW)                                \
+  if (d->W == KW) {                                      \
+    if (!bf) { KDA_CONV_CALL(float, float, KW) }         \
+    if (obf) { KDA_CONV_CALL(bf16, bf16, KW) }           \
+    KDA_CONV_CALL(bf16, float, KW)                       \
+  }
+  KDA_CONV_CASE(2)
+  KDA_CONV_CASE(3)
+  KDA_CONV_CASE(4)
+#undef KDA_CONV_CASE
+#undef KDA_CONV_CALL
   return hipErrorInvalidValue;
 }
 
@@ -459,6 +518,95 @@ kda_status kda_decode(const kda_desc* d, const void* q, const void* k, const voi
   (void)hipGetLastError();
   clear_error();
   return launch_status(run_decode(d, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kda_conv_workspace_bytes(const kda_conv_desc* d) {
+  if (!d || !conv_desc_ok(d) || d->B < 0 || d->T < 0) return 0;
+  return conv_ws_bytes(d);
+}
+
+kda_status kda_conv_fwd(const kda_conv_desc* d, const void* x, const float* weight, const float* bias,
+                        const float* init_state, void* y, float* final_state, const int32_t* cu_seqlens,
+                        void* stream) {
+  if (!d) return KDA_ERROR_INVALID_VALUE;
+  if (!conv_desc_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
+  int N;
+  if (!conv_shape(d, cu_seqlens != nullptr, &N)) return KDA_ERROR_INVALID_VALUE;
+  const bool any_tok = (long long)d->B * d->T > 0;
+  if (!weight || (any_tok && (!x || !y))) return KDA_ERROR_INVALID_VALUE;
+  const void* al16[] = {x, y, init_state, final_state};
+  for (const void* p : al16)
+    if (p && !aligned16(p)) return KDA_ERROR_MISALIGNED;
+  const void* al4[] = {weight, bias, cu_seqlens};
+  for (const void* p : al4)
+    if ((uintptr_t)p & 3u) return KDA_ERROR_MISALIGNED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cu_seqlens && env_int("KDA_DEBUG", 0) && !cu_ok(cu_seqlens, N, d->T, st)) return KDA_ERROR_INVALID_VALUE;
+  kda::ConvArgs c;
+  conv_args(c, d, N);
+  c.x = x; c.weight = weight; c.bias = bias; c.init = init_state; c.cu = cu_seqlens;
+  c.y = y; c.final_state = final_state;
+  (void)hipGetLastError();
+  clear_error();
+  return launch_status(run_conv(d, c, ConvOp::Fwd, st));
+}
+
+kda_status kda_conv_bwd(const kda_conv_desc* d, const void* x, const float* weight, const float* bias,
+                        const float* init_state, const int32_t* cu_seqlens, const void* dy,
+                        const float* d_final_state, void* dx, float* dweight, float* dbias,
+                        float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!d) return KDA_ERROR_INVALID_VALUE;
+  if (!conv_desc_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
+  int N;
+  if (!conv_shape(d, cu_seqlens != nullptr, &N)) return KDA_ERROR_INVALID_VALUE;
+  const bool any_tok = (long long)d->B * d->T > 0;
+  if (!weight || !dweight || (any_tok && (!x || !dy || !dx))) return KDA_ERROR_INVALID_VALUE;
+  const void* al16[] = {x, dy, dx, init_state, d_final_state, d_init_state, workspace};
+  for (const void* p : al16)
+    if (p && !aligned16(p)) return KDA_ERROR_MISALIGNED;
+  const void* al4[] = {weight, bias, dweight, dbias, cu_seqlens};
+  for (const void* p : al4)
+    if ((uintptr_t)p & 3u) return KDA_ERROR_MISALIGNED;
+  const size_t need = conv_ws_bytes(d);
+  if (need && (!workspace || workspace_bytes < need)) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cu_seqlens && env_int("KDA_DEBUG", 0) && !cu_ok(cu_seqlens, N, d->T, st)) return KDA_ERROR_INVALID_VALUE;
+  kda::ConvArgs c;
+  conv_args(c, d, N);
+  c.x = x; c.weight = weight; c.bias = bias; c.init = init_state; c.cu = cu_seqlens;
+  c.dy = dy; c.dfinal = d_final_state; c.dx = dx;
+  c.dweight = dweight; c.dbias = dbias; c.dinit = d_init_state;
+  c.part = static_cast<float*>(workspace);
+  (void)hipGetLastError();
+  clear_error();
+  return launch_status(run_conv(d, c, ConvOp::Bwd, st));
+}
+
+kda_status kda_conv_decode(const kda_conv_desc* d, const void* x, const float* weight, const float* bias,
+                           float* state_pool, int32_t pool_size, const int32_t* state_indices,
+                           const int32_t* num_commit, void* y, void* stream) {
+  if (!d) return KDA_ERROR_INVALID_VALUE;
+  if (!conv_desc_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
+  if (d->B < 0 || d->T < 0 || d->B > 65535 || pool_size < 0) return KDA_ERROR_INVALID_VALUE;
+  if ((long long)d->B * d->T * d->D >= (1LL << 40)) return KDA_ERROR_INVALID_VALUE;
+  if (d->B == 0) return KDA_SUCCESS;
+  if (!weight || !state_pool || (d->T > 0 && (!x || !y))) return KDA_ERROR_INVALID_VALUE;
+  if (!state_indices && pool_size < d->B) return KDA_ERROR_INVALID_VALUE;
+  const void* al16[] = {x, y, state_pool};
+  for (const void* p : al16)
+    if (p && !aligned16(p)) return KDA_ERROR_MISALIGNED;
+  const void* al4[] = {weight, bias, state_indices, num_commit};
+  for (const void* p : al4)
+    if ((uintptr_t)p & 3u) return KDA_ERROR_MISALIGNED;
+  kda::ConvArgs c;
+  std::memset(&c, 0, sizeof c);
+  c.B = d->B; c.T = d->T; c.D = d->D; c.tokens = d->B * d->T;
+  c.silu = d->activation == KDA_CONV_SILU;
+  c.x = x; c.weight = weight; c.bias = bias; c.y = y;
+  c.pool = state_pool; c.pool_size = pool_size; c.idx = state_indices; c.ncommit = num_commit;
+  (void)hipGetLastError();
+  clear_error();
+  return launch_status(run_conv(d, c, ConvOp::Decode, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

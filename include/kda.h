@@ -161,6 +161,78 @@ kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const 
                       const void *log_alpha, const void *beta, float *state_pool, int32_t pool_size,
                       const int32_t *state_indices, const int32_t *num_commit, void *out, void *stream);
 
+/* Short causal convolution with a carried state.  The same page's section on
+ * disaggregated prefill and decode lists, among what a KDA layer hands from one
+ * serving pool to another, a convolution state beside the recurrent state; the
+ * page defines neither.  Read here as a causal depthwise convolution of width
+ * W along time over each of D channels, whose state is the sequence's last
+ * W - 1 inputs:
+ *
+ *     z[t, c] = bias[c] + sum_{j<W} weight[c, j] * X[t - (W-1) + j, c]
+ *     y[t, c] = z[t, c]                      (KDA_CONV_IDENTITY)
+ *     y[t, c] = z[t, c] * sigmoid(z[t, c])   (KDA_CONV_SILU)
+ *
+ * X is the sequence's input preceded by its W - 1 state rows (state row i
+ * stands for time i - (W - 1); zero when init_state is NULL).  final_state is
+ * the last W - 1 rows of that extended input (for a sequence shorter than
+ * W - 1 it still holds some initial-state rows).
+ *
+ * Layouts (contiguous, token-major):
+ *   x, dy                    : [B, T, D] (or packed [1, T, D] with cu_seqlens), desc.dtype
+ *   y, dx                    : like x, desc.out_dtype
+ *   weight, dweight          : float32 [D, W];  bias, dbias : float32 [D]
+ *   init_state, final_state, d_final_state, d_init_state : float32 [N, W - 1, D]
+ *   cu_seqlens               : int32 [num_seqs + 1] in device memory (as for kda_fwd)
+ * Supported: W in {2, 3, 4}; D a positive multiple of 8.  All pointers are
+ * device memory owned by the caller; 16-byte alignment is required of x, y,
+ * dy, dx, the states and the pool; 4-byte alignment of weight, bias, dweight,
+ * dbias and the int32 arrays.  Validation happens before any launch; the
+ * calls enqueue on `stream`, allocate nothing and do not synchronise.
+ * final_state may alias init_state; nothing else may overlap. */
+typedef enum { KDA_CONV_IDENTITY = 0, KDA_CONV_SILU = 1 } kda_conv_activation;
+
+typedef struct {
+    int32_t B;            /* rows (decode: sequences); 1 when cu_seqlens is given   */
+    int32_t T;            /* tokens per row (total packed tokens with cu_seqlens)   */
+    int32_t D;            /* channels                                               */
+    int32_t W;            /* kernel width: 2, 3 or 4                                */
+    int32_t num_seqs;     /* packed sequences when cu_seqlens is given              */
+    kda_dtype dtype;      /* x, dy                                                  */
+    kda_dtype out_dtype;  /* y, dx (KDA_BF16 only with bf16 inputs)                 */
+    int32_t activation;   /* kda_conv_activation                                    */
+} kda_conv_desc;
+
+/* Bytes of device workspace kda_conv_bwd needs (partial sums of dweight and
+ * dbias over tiles of 256 tokens); kda_conv_fwd and kda_conv_decode need none.
+ * 0 if the descriptor is invalid or there is nothing to reduce. */
+size_t kda_conv_workspace_bytes(const kda_conv_desc *desc);
+
+/* Forward: y, and final_state unless NULL.  bias and init_state may be NULL. */
+kda_status kda_conv_fwd(const kda_conv_desc *desc, const void *x, const float *weight, const float *bias,
+                        const float *init_state, void *y, float *final_state, const int32_t *cu_seqlens,
+                        void *stream);
+
+/* Backward: gradients of <dy, y> + <d_final_state, final_state>.  dx and
+ * dweight are required; dbias and d_init_state may be NULL (not written);
+ * d_final_state may be NULL (zero).  d_init_state must not alias
+ * d_final_state.  dweight and dbias are sums over all tokens in a fixed order
+ * (bitwise reproducible). */
+kda_status kda_conv_bwd(const kda_conv_desc *desc, const void *x, const float *weight, const float *bias,
+                        const float *init_state, const int32_t *cu_seqlens, const void *dy,
+                        const float *d_final_state, void *dx, float *dweight, float *dbias,
+                        float *d_init_state, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Decode / replay step of the convolution, the companion of kda_decode: x
+ * [B, T, D] (T >= 0 tokens per sequence), y [B, T, D]; state_pool float32
+ * [pool_size, W - 1, D] updated in place; state_indices and num_commit as in
+ * kda_decode (NULL: slot b; NULL: commit all T; a slot outside
+ * [0, pool_size) is padding: zero outputs, no state touched; the slot
+ * receives the state after the first num_commit[b] tokens, clamped to
+ * [0, T]).  Non-padding slots must be distinct within one call. */
+kda_status kda_conv_decode(const kda_conv_desc *desc, const void *x, const float *weight, const float *bias,
+                           float *state_pool, int32_t pool_size, const int32_t *state_indices,
+                           const int32_t *num_commit, void *y, void *stream);
+
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);
 

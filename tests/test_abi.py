@@ -29,7 +29,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kda_bwd", "kda_decode", "kda_fwd", "kda_last_error", "kda_status_string",
-                                          "kda_timing_enable", "kda_timing_read", "kda_workspace_bytes"])
+                                          "kda_timing_enable", "kda_timing_read", "kda_workspace_bytes",
+                                          "kda_conv_workspace_bytes", "kda_conv_fwd", "kda_conv_bwd",
+                                          "kda_conv_decode"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -203,3 +205,63 @@ def test_fused_prep_workspace(lib):
     fwd = lib.kda_workspace_bytes(ctypes.byref(_desc(flags=kda.KDA_FLAG_QK_L2NORM)), 0)
     assert gate == base and norm > base
     assert fwd == lib.kda_workspace_bytes(ctypes.byref(_desc()), 0)
+
+
+# ---------------------------------------------------------------------------
+# short convolution entry points: host-side validation (nothing is launched)
+# ---------------------------------------------------------------------------
+def _cdesc(**kw):
+    d = dict(B=1, T=300, D=64, W=4, num_seqs=0, dtype=1, out_dtype=0, activation=1)
+    d.update(kw)
+    return kda.kda_conv_desc(**d)
+
+
+def _cfwd(lib, d, x=A, w=A, b=None, init=None, y=A, fin=None, cu=None):
+    return lib.kda_conv_fwd(ctypes.byref(d) if d is not None else None, P(x), P(w), P(b), P(init), P(y), P(fin),
+                            P(cu), None)
+
+
+def _cbwd(lib, d, ws=A, wsb=1 << 40, dx=A, dw=A, x=A):
+    return lib.kda_conv_bwd(ctypes.byref(d), P(x), P(A), None, None, None, P(A), None, P(dx), P(dw), None, None,
+                            P(ws), wsb, None)
+
+
+def test_conv_rejects_bad_descriptors(lib):
+    assert _cfwd(lib, None) == S_INVALID
+    for bad in (dict(W=1), dict(W=5), dict(D=12), dict(D=0), dict(dtype=7), dict(dtype=0, out_dtype=1),
+                dict(activation=2)):
+        assert _cfwd(lib, _cdesc(**bad)) == S_UNSUP, bad
+    assert _cfwd(lib, _cdesc(B=0)) == S_INVALID
+    assert _cfwd(lib, _cdesc(B=2), cu=A) == S_INVALID          # packed sequences need B == 1
+    assert _cfwd(lib, _cdesc(num_seqs=0), cu=A) == S_INVALID   # and num_seqs >= 1
+
+
+def test_conv_rejects_null_and_misaligned_pointers(lib):
+    assert _cfwd(lib, _cdesc(), x=None) == S_INVALID
+    assert _cfwd(lib, _cdesc(), w=None) == S_INVALID
+    assert _cfwd(lib, _cdesc(), y=None) == S_INVALID
+    assert _cfwd(lib, _cdesc(), x=A + 8) == S_ALIGN
+    assert _cfwd(lib, _cdesc(), w=A + 2) == S_ALIGN
+    assert _cfwd(lib, _cdesc(), fin=A + 4) == S_ALIGN
+    assert _cbwd(lib, _cdesc(), dw=None) == S_INVALID
+    assert _cbwd(lib, _cdesc(), dx=A + 4) == S_ALIGN
+
+
+def test_conv_workspace_size_and_check(lib):
+    d = _cdesc(T=1000, D=64, W=4)
+    need = lib.kda_conv_workspace_bytes(ctypes.byref(d))
+    assert need == 4 * 5 * 64 * 4          # ceil(1000 / 256) tiles x (W taps + bias) x D floats
+    assert _cbwd(lib, d, wsb=need - 1) == S_WS
+    assert _cbwd(lib, d, ws=None) == S_WS
+    assert lib.kda_conv_workspace_bytes(ctypes.byref(_cdesc(T=0))) == 0
+    assert lib.kda_conv_workspace_bytes(ctypes.byref(_cdesc(W=9))) == 0
+
+
+def test_conv_decode_validation(lib):
+    def dec(d, pool=A, n=4, idx=None, x=A):
+        return lib.kda_conv_decode(ctypes.byref(d), P(x), P(A), None, P(pool), n, P(idx), None, P(A), None)
+    assert dec(_cdesc(B=0)) == S_OK                     # nothing to do
+    assert dec(_cdesc(B=8, T=2), n=4) == S_INVALID      # slot b needs pool_size >= B
+    assert dec(_cdesc(B=2, T=2), pool=None) == S_INVALID
+    assert dec(_cdesc(B=2, T=2), pool=A + 4) == S_ALIGN
+    assert dec(_cdesc(B=2, T=2, W=6)) == S_UNSUP
