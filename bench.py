@@ -90,6 +90,9 @@ def _short_name(name, train=True):
         return "kda_chunk_map"
     if "kda_decode_step" in name:
         return "kda_decode_step"
+    for k in ("fwd", "bwd", "final", "dinit", "reduce", "decode"):
+        if f"kda_conv_{k}_k" in name:
+            return f"kda_conv_{k}"
     if "kda_prep" in name:
         bwd = (_bools(name) or [False])[0]   # <..., BWD, QKN[, GATE]>
         return ("kda_prep_save" if train else "kda_prep_bwd") if bwd else "kda_prep"
@@ -385,7 +388,7 @@ def conv_bench(args, dev) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import short_conv as sc
-        nch = 96
+        nch = 1536
         ch = np.arange(0, D, D // nch)[:nch]
         sub = lambda a: np.ascontiguousarray(a[..., ch])  # noqa: E731
         t0 = time.perf_counter()

@@ -18,9 +18,10 @@
 //
 // The work is elementwise along channels and a W-tap sliding window along
 // time, so it is bound by HBM traffic: each thread owns a group of adjacent
-// channels (one 16-byte load of a token row for bf16 in the forward), walks a
-// run of tokens and keeps the window in registers; a wave reads and writes
-// whole contiguous spans of a token row.  Per-tile partial sums of the weight
+// channels (four: one 16-byte fp32 store, or one 8-byte bf16 load, of a token
+// row), walks a run of tokens and keeps the window in registers; every load
+// and store instruction of a wave covers one contiguous span of a token row,
+// so no cache line is written in parts.  Per-tile partial sums of the weight
 // and bias gradients are reduced in a fixed order by a second kernel, so the
 // results are bitwise reproducible.
 #include "kda.h"
@@ -31,9 +32,19 @@ namespace kda {
 
 namespace {
 
+#ifndef KDA_CONV_TT
+#define KDA_CONV_TT 64       // forward: tokens per tile
+#endif
+#ifndef KDA_CONV_U
+#define KDA_CONV_U 8         // forward: token rows loaded ahead of their use
+#endif
+#ifndef KDA_CONV_BWD_U
+#define KDA_CONV_BWD_U 4     // backward: token rows (of x and dy) loaded ahead of their use
+#endif
 constexpr int CV_NT = 256;   // threads per work-group (4 waves)
-constexpr int CV_TT = 64;    // forward: tokens per tile
-constexpr int CV_U = 8;      // token rows loaded ahead of their use
+constexpr int CV_TT = KDA_CONV_TT;
+constexpr int CV_U = KDA_CONV_U;
+constexpr int CV_UB = KDA_CONV_BWD_U;
 
 // NC consecutive elements as floats.
 template <typename E, int NC> __device__ __forceinline__ void cload(const E* p, float (&x)[NC]) {
@@ -148,7 +159,7 @@ template <int R, int NC> __device__ __forceinline__ void push(float (&win)[R][NC
 // ---------------------------------------------------------------------------
 template <typename E, typename O, int W>
 __global__ __launch_bounds__(CV_NT) void kda_conv_fwd_k(const ConvArgs c) {
-  constexpr int NC = 8;
+  constexpr int NC = 4;
   const int ch = (blockIdx.y * CV_NT + threadIdx.x) * NC;
   if (ch >= c.D) return;
   // Work-group ids are dealt to the 8 XCDs round robin; give each XCD a
@@ -200,7 +211,7 @@ __global__ __launch_bounds__(CV_NT) void kda_conv_fwd_k(const ConvArgs c) {
 // final_state may alias init_state.
 template <typename E, int W>
 __global__ __launch_bounds__(CV_NT) void kda_conv_final_k(const ConvArgs c) {
-  constexpr int NC = 8;
+  constexpr int NC = 4;
   const int ch = (blockIdx.x * CV_NT + threadIdx.x) * NC;
   if (ch >= c.D) return;
   const int n = blockIdx.y;
@@ -252,10 +263,10 @@ __global__ __launch_bounds__(CV_NT) void kda_conv_bwd_k(const ConvArgs c) {
       ext_row<E, W, NC>(c, n, a, s0 - (W - 1) + j, ch, xwin[j]);
       czero(dzw[j]);   // dz before s0 only reaches dx rows before s0, which this pass does not emit
     }
-    for (int p0 = s0; p0 < send; p0 += CV_U) {
-      float xr[CV_U][NC], gr[CV_U][NC];
+    for (int p0 = s0; p0 < send; p0 += CV_UB) {
+      float xr[CV_UB][NC], gr[CV_UB][NC];
 #pragma unroll
-      for (int u = 0; u < CV_U; ++u) {
+      for (int u = 0; u < CV_UB; ++u) {
         const int p = p0 + u;
         if (p < send && p < e) {
           cload<E, NC>(x + (size_t)p * c.D + ch, xr[u]);
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(CV_NT) void kda_conv_bwd_k(const ConvArgs c) {
         }
       }
 #pragma unroll
-      for (int u = 0; u < CV_U; ++u) {
+      for (int u = 0; u < CV_UB; ++u) {
         const int p = p0 + u;
         if (p < send) {
           float dz[NC];
@@ -369,17 +380,42 @@ __global__ __launch_bounds__(CV_NT) void kda_conv_dinit_k(const ConvArgs c) {
   }
 }
 
-// dweight [D][W] and dbias [D]: the tiles' partial sums added in tile order.
-// One thread per (tap or bias, channel); grid over (W + 1) * D.
+// dweight [D][W] and dbias [D]: the tiles' partial sums added in a fixed
+// order.  A work-group takes 64 adjacent partial-sum columns (column = tap or
+// bias row j times D plus channel) and its four waves take every fourth tile
+// each; the four stripe sums are then added in stripe order.
+constexpr int CV_RED_COLS = 64;
 template <int W>
 __global__ __launch_bounds__(CV_NT) void kda_conv_reduce_k(const ConvArgs c, int tiles) {
-  const int id = blockIdx.x * CV_NT + threadIdx.x;
-  if (id >= (W + 1) * c.D) return;
-  const int j = id / c.D, ch = id % c.D;
+  __shared__ float part[CV_NT / CV_RED_COLS][CV_RED_COLS];
+  const int ncol = (W + 1) * c.D;
+  const int l = threadIdx.x % CV_RED_COLS, stripe = threadIdx.x / CV_RED_COLS;
+  const int col = blockIdx.x * CV_RED_COLS + l;
+  constexpr int NS = CV_NT / CV_RED_COLS;
   float s = 0.f;
-  for (int t = 0; t < tiles; ++t) s += c.part[((size_t)t * (W + 1) + j) * c.D + ch];
-  if (j < W) c.dweight[(size_t)ch * W + j] = s;
-  else if (c.dbias) c.dbias[ch] = s;
+  if (col < ncol) {
+    const float* p = c.part + col;
+    int t = stripe;
+    for (; t + 3 * NS < tiles; t += 4 * NS) {   // four tiles in flight, added in order
+      const float a = p[(size_t)t * ncol], b = p[(size_t)(t + NS) * ncol];
+      const float d = p[(size_t)(t + 2 * NS) * ncol], e = p[(size_t)(t + 3 * NS) * ncol];
+      s += a;
+      s += b;
+      s += d;
+      s += e;
+    }
+    for (; t < tiles; t += NS) s += p[(size_t)t * ncol];
+  }
+  part[stripe][l] = s;
+  __syncthreads();
+  if (stripe == 0 && col < ncol) {
+    float r = part[0][l];
+#pragma unroll
+    for (int k = 1; k < NS; ++k) r += part[k][l];
+    const int j = col / c.D, ch = col % c.D;
+    if (j < W) c.dweight[(size_t)ch * W + j] = r;
+    else if (c.dbias) c.dbias[ch] = r;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(CV_NT) void kda_conv_reduce_k(const ConvArgs c, int
 // ---------------------------------------------------------------------------
 template <typename E, typename O, int W>
 __global__ __launch_bounds__(CV_NT) void kda_conv_decode_k(const ConvArgs c) {
-  constexpr int NC = 8;
+  constexpr int NC = 4;
   const int ch = (blockIdx.x * CV_NT + threadIdx.x) * NC;
   if (ch >= c.D) return;
   const int b = blockIdx.y, T = c.T;
@@ -444,11 +480,11 @@ inline unsigned cgroups(int D, int nc) { return (unsigned)((D / nc + CV_NT - 1) 
 template <typename E, typename O, int W> hipError_t launch_conv_fwd(const ConvArgs& c, hipStream_t st) {
   if (c.tokens > 0)
     KDA_TIMED("kda_conv_fwd", st,
-              hipLaunchKernelGGL((kda_conv_fwd_k<E, O, W>), dim3(((c.tokens + CV_TT - 1) / CV_TT + 7) / 8 * 8, cgroups(c.D, 8)),
+              hipLaunchKernelGGL((kda_conv_fwd_k<E, O, W>), dim3(((c.tokens + CV_TT - 1) / CV_TT + 7) / 8 * 8, cgroups(c.D, 4)),
                                  dim3(CV_NT), 0, st, c));
   if (c.final_state)
     KDA_TIMED("kda_conv_final", st,
-              hipLaunchKernelGGL((kda_conv_final_k<E, W>), dim3(cgroups(c.D, 8), c.N), dim3(CV_NT), 0, st, c));
+              hipLaunchKernelGGL((kda_conv_final_k<E, W>), dim3(cgroups(c.D, 4), c.N), dim3(CV_NT), 0, st, c));
   return hipGetLastError();
 }
 
@@ -458,8 +494,8 @@ template <typename E, typename O, int W> hipError_t launch_conv_bwd(const ConvAr
     KDA_TIMED("kda_conv_bwd", st,
               hipLaunchKernelGGL((kda_conv_bwd_k<E, O, W>), dim3(tiles, cgroups(c.D, 4)), dim3(CV_NT), 0, st, c));
   KDA_TIMED("kda_conv_reduce", st,
-            hipLaunchKernelGGL((kda_conv_reduce_k<W>), dim3(((W + 1) * c.D + CV_NT - 1) / CV_NT), dim3(CV_NT), 0, st,
-                               c, tiles));
+            hipLaunchKernelGGL((kda_conv_reduce_k<W>), dim3(((W + 1) * c.D + CV_RED_COLS - 1) / CV_RED_COLS),
+                               dim3(CV_NT), 0, st, c, tiles));
   if (c.dinit)
     KDA_TIMED("kda_conv_dinit", st,
               hipLaunchKernelGGL((kda_conv_dinit_k<E, W>), dim3(cgroups(c.D, 4), c.N), dim3(CV_NT), 0, st, c));
@@ -468,7 +504,7 @@ template <typename E, typename O, int W> hipError_t launch_conv_bwd(const ConvAr
 
 template <typename E, typename O, int W> hipError_t launch_conv_decode(const ConvArgs& c, hipStream_t st) {
   KDA_TIMED("kda_conv_decode", st,
-            hipLaunchKernelGGL((kda_conv_decode_k<E, O, W>), dim3(cgroups(c.D, 8), c.B), dim3(CV_NT), 0, st, c));
+            hipLaunchKernelGGL((kda_conv_decode_k<E, O, W>), dim3(cgroups(c.D, 4), c.B), dim3(CV_NT), 0, st, c));
   return hipGetLastError();
 }
 
