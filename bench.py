@@ -423,6 +423,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload index (4 = varlen fwd+bwd)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training step (forward + backward) on a forward-only workload too "
+                         "(dO and dS_final drawn as for the varlen workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-bf16", action="store_true", help="bf16 outputs/gradients instead of fp32")
     ap.add_argument("--recompute", action="store_true",
@@ -484,7 +487,7 @@ def main() -> int:
         return conv_bench(args, dev)
 
     w = ki.config(args.config)
-    fwd_only = args.fwd_only or not w.backward
+    fwd_only = args.fwd_only or not (w.backward or args.train)
     print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
     inp = ki.make_inputs(w, with_grads=not fwd_only, raw=args.fused_prep)
     prep = dict(qk_l2norm=True, gate_logsigmoid=True) if args.fused_prep else {}

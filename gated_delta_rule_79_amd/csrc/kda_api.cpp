@@ -90,16 +90,17 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
     p.dS = take(nb * dk * dv * 4);
     p.dU = take(nb * dv * CH * 4);
     if (d->flags & KDA_FLAG_QK_L2NORM) p.DQK = take(nb * 2 * CH * dk * 4);   // dq^, dk^ before the norm's chain rule
-  } else {
-    p.segs = kda::fwd_segments(N, d->H, d->dv, (long long)d->B * d->T, false);
-    if (p.segs > 1) {   // segment scan buffers
-      const size_t nv = (size_t)N * p.segs;
-      p.vsc0 = take((nv + 1) * sizeof(int32_t));
-      p.vord = take(nv * sizeof(int32_t));
-      p.seg_in = take(nv * d->H * dk * dv * 4);
-      p.seg_loc = take(nv * d->H * dk * dv * 4);
-      p.seg_m = take(nv * d->H * dk * dk * 4);
-    }
+  }
+  // segment scan buffers (the same stretches for a training-mode forward and the
+  // backward, which reuses the forward's transfers)
+  p.segs = kda::fwd_segments(N, d->H, d->dv, (long long)d->B * d->T, bwd);
+  if (p.segs > 1) {
+    const size_t nv = (size_t)N * p.segs;
+    p.vsc0 = take((nv + 1) * sizeof(int32_t));
+    p.vord = take(nv * sizeof(int32_t));
+    p.seg_in = take(nv * d->H * dk * dv * 4);
+    p.seg_loc = take(nv * d->H * dk * dv * 4);
+    p.seg_m = take(nv * d->H * dk * dk * 4);
   }
   p.total = o;
   return p;

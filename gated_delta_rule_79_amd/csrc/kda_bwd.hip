@@ -54,7 +54,10 @@ struct RevLds {
   static_assert(BYTES <= 163840, "reverse pass LDS");
 };
 
-template <typename E, int DK, int DV, int DVS>
+// LOCAL: a stretch's run from dS' = 0 for the segment scan; only the gradient
+// entering the stretch is kept (written where d_init_state goes), no per-chunk
+// dS' or dU.
+template <typename E, int DK, int DV, int DVS, bool LOCAL = false>
 __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   using L = RevLds<E, DK, DV, DVS>;
   using OP = typename L::OP;
@@ -171,9 +174,11 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
       if (t < NST) {
         const int off = (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4;
         store4_split<OP>(sDSh + off, sDSl + off, dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
-        float* dst = gdS + blk_of(n) * WB::DS + (size_t)(16 * mt + 4 * q4) * DV + n0 + 16 * nt + r16;  // [DK][DV]
+        if constexpr (!LOCAL) {
+          float* dst = gdS + blk_of(n) * WB::DS + (size_t)(16 * mt + 4 * q4) * DV + n0 + 16 * nt + r16;  // [DK][DV]
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = dS[i][ii];
+          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = dS[i][ii];
+        }
       }
     }
     __syncthreads();
@@ -196,9 +201,11 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
         const f32x4 du = scale * x1 + x2;
         const int off = (16 * nt + r16) * L::LDT + 16 * tt + 4 * q4;
         store4_split<OP>(sDUh + off, sDUl + off, du[0], du[1], du[2], du[3]);
-        float* dst = gdU + blk_of(n) * WB::DU + (size_t)(16 * tt + 4 * q4) * DV + n0 + 16 * nt + r16;  // [CH][DV]
+        if constexpr (!LOCAL) {
+          float* dst = gdU + blk_of(n) * WB::DU + (size_t)(16 * tt + 4 * q4) * DV + n0 + 16 * nt + r16;  // [CH][DV]
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = du[ii];
+          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = du[ii];
+        }
       }
     }
     // scale Qt^T dO for this wave's state tiles (independent of dU)
@@ -954,13 +961,48 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV, int DVS>
+template <typename E, int DK, int DV, int DVS, bool LOCAL = false>
 static hipError_t launch_rev(const Args& a, hipStream_t st) {
   constexpr int NSL = DV / DVS;
   const int grid = (a.N * a.H + 7) / 8 * 8 * NSL;
-  KDA_TIMED("kda_state_bwd_revpass", st,
-            hipLaunchKernelGGL((kda_state_rev<E, DK, DV, DVS>), dim3(grid), dim3(512), 0, st, a));
+  KDA_TIMED(LOCAL ? "kda_seg_rev_local" : "kda_state_bwd_revpass", st,
+            hipLaunchKernelGGL((kda_state_rev<E, DK, DV, DVS, LOCAL>), dim3(grid), dim3(512), 0, st, a));
   return hipGetLastError();
+}
+
+template <typename E, int DK, int DV, bool LOCAL = false>
+static hipError_t launch_rev_auto(const Args& a, hipStream_t st) {
+  if (a.N * a.H == 0) return hipSuccess;
+  if constexpr (sizeof(E) == 2) {
+    if (pick_dvs(a.N * a.H, DV) == 64) return launch_rev<E, DK, DV, 64, LOCAL>(a, st);
+    return launch_rev<E, DK, DV, 16, LOCAL>(a, st);
+  } else {
+    return launch_rev<E, DK, DV, 32, LOCAL>(a, st);
+  }
+}
+
+// Segmented reverse pass (long sequences cut into the forward's stretches): each
+// stretch runs from dS' = 0 (in parallel), a reverse scan per (sequence, head)
+// with the transposed stretch transfers M^T the forward left in seg_m gives each
+// stretch the true gradient of the state leaving it, and the ordinary reverse
+// pass then runs every stretch from that gradient at once.
+template <typename E, int DK, int DV>
+static hipError_t launch_segmented_rev(const Args& a, hipStream_t st) {
+  hipError_t e = launch_segment_map(a, st);   // the same stretches as the forward (idempotent)
+  if (e != hipSuccess) return e;
+  Args av = a;   // the stretches as sequences of their own
+  av.N = a.N * a.segs;
+  av.seq_chunk0 = a.vsc0;
+  av.seq_order = a.vord;
+  Args al = av;
+  al.dfinal = nullptr;
+  al.dinit = a.seg_loc;   // gradient entering each stretch, from zero
+  if ((e = launch_rev_auto<E, DK, DV, true>(al, st)) != hipSuccess) return e;
+  if ((e = launch_segment_rscan<DK, DV>(a, st)) != hipSuccess) return e;   // seg_in, d_init_state
+  Args af = av;
+  af.dfinal = a.seg_in;
+  af.dinit = nullptr;
+  return launch_rev_auto<E, DK, DV>(af, st);
 }
 
 // `saved`: the workspace already holds the forward intermediates (kda_fwd with
@@ -972,18 +1014,8 @@ hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved) {
     e = launch_bwd_front<E, DK, DV>(a, st);
     if (e != hipSuccess) return e;
   }
-  const int units = a.N * a.H;
-  if (units > 0) {
-    if constexpr (sizeof(E) == 2) {
-      if (pick_dvs(units, DV) == 64)
-        e = launch_rev<E, DK, DV, 64>(a, st);
-      else
-        e = launch_rev<E, DK, DV, 16>(a, st);
-    } else {
-      e = launch_rev<E, DK, DV, 32>(a, st);
-    }
-    if (e != hipSuccess) return e;
-  }
+  e = a.segs > 1 ? launch_segmented_rev<E, DK, DV>(a, st) : launch_rev_auto<E, DK, DV>(a, st);
+  if (e != hipSuccess) return e;
   if (a.max_chunks > 0) {
     if (a.qk_norm)
       KDA_TIMED("kda_bwd_chunk", st,

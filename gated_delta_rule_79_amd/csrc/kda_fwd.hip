@@ -858,7 +858,9 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
 // updates its 16x16 tiles of S.  S stays in fp32 registers; each chunk it is
 // copied to LDS in the operand type for the products that read it.  The next
 // chunk's matrices are loaded into registers while the current one computes.
-template <typename E, int DK, int DV, int DVS, bool OUT, bool SAVE>
+// UF: U~ is read in fp32 (the copy a training-mode prep writes) rather than in
+// the operand type.
+template <typename E, int DK, int DV, int DVS, bool OUT, bool SAVE, bool UF = SAVE>
 struct StateLds {
   using OP = typename OpOf<E>::T;
   static constexpr int P = PADE<OP>;
@@ -868,7 +870,7 @@ struct StateLds {
   static constexpr size_t QT = W + (size_t)CH * LDK * sizeof(OP);                 // OP [CH][LDK]  (OUT)
   static constexpr size_t KHT = QT + (OUT ? (size_t)CH * LDK * sizeof(OP) : 0);   // OP [DK][LDT]
   static constexpr size_t AQK = KHT + (size_t)DK * LDT * sizeof(OP);              // OP [CH][LDT]  (OUT)
-  using UTT = typename std::conditional<SAVE, float, OP>::type;                  // U~ element type
+  using UTT = typename std::conditional<UF, float, OP>::type;                    // U~ element type
   static constexpr size_t UT = AQK + (OUT ? (size_t)CH * LDT * sizeof(OP) : 0);   // UTT [DVS][CH]
   static constexpr size_t GAM = UT + (size_t)DVS * CH * sizeof(UTT);              // float [DK]
   static constexpr size_t ST = GAM + (size_t)DK * 4;                              // OP [DVS][LDK]  S^T
@@ -886,12 +888,12 @@ struct StateLds {
 // and S_end = M S_start + (the same run from S = 0 with U~).  MODE 2: one
 // launch of both, the first half of the grid the runs from S = 0 (end states
 // to final_state), the second half the transfers (to seg_m).
-template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int PF, int MODE = 0>
+template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int PF, int MODE = 0, bool UF = SAVE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4 : 1, PF == 1 ? 4 : 2))) void kda_state(const Args a) {
   static_assert(MODE == 0 || (!OUT && !SAVE && DV == DK), "transfer runs keep only the end state");
   const bool xf = MODE == 1 || (MODE == 2 && blockIdx.x >= gridDim.x / 2);
   const int bid = (MODE == 2 && xf) ? (int)(blockIdx.x - gridDim.x / 2) : (int)blockIdx.x;
-  using L = StateLds<E, DK, DV, DVS, OUT, SAVE>;
+  using L = StateLds<E, DK, DV, DVS, OUT, SAVE, UF>;
   using OP = typename L::OP;
   using WB = WsBlock<E, DK, DV>;
   constexpr int NT = 512, NSL = DV / DVS;
@@ -931,7 +933,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   const OP* gQt = reinterpret_cast<const OP*>(a.wsQt);
   const OP* gAqk = reinterpret_cast<const OP*>(a.wsAqk);
   const OP* gKhT = reinterpret_cast<const OP*>(a.wsKhT);
-  const UTT* gUt = SAVE ? reinterpret_cast<const UTT*>(a.wsUtF) : reinterpret_cast<const UTT*>(a.wsUt);
+  const UTT* gUt = UF ? reinterpret_cast<const UTT*>(a.wsUtF) : reinterpret_cast<const UTT*>(a.wsUt);
   const float* gGam = a.wsGam;
   OP* gS = reinterpret_cast<OP*>(a.wsS);
   float* gU = a.wsU;
@@ -1130,7 +1132,7 @@ int pick_dvs(int units, int dv) {
 #endif
 }
 
-template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int MODE = 0>
+template <typename E, typename O, int DK, int DV, int DVS, bool OUT, bool SAVE, int MODE = 0, bool UF = SAVE>
 static hipError_t launch_state(const Args& a, hipStream_t st, const char* name = nullptr) {
   constexpr int NSL = DV / DVS;
   const int units = a.N * a.H;
@@ -1140,18 +1142,18 @@ static hipError_t launch_state(const Args& a, hipStream_t st, const char* name =
   constexpr int PF = KDA_STATE_PF;
   if (!name) name = OUT ? (SAVE ? "kda_state_fwd_save" : "kda_state_fwd") : "kda_state_bwd_fwdpass";
   KDA_TIMED(name, st,
-            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT, SAVE, PF, MODE>), dim3(grid), dim3(512), 0, st, a));
+            hipLaunchKernelGGL((kda_state<E, O, DK, DV, DVS, OUT, SAVE, PF, MODE, UF>), dim3(grid), dim3(512), 0, st, a));
   return hipGetLastError();
 }
 
-template <typename E, typename O, int DK, int DV, bool OUT, bool SAVE, int MODE = 0>
+template <typename E, typename O, int DK, int DV, bool OUT, bool SAVE, int MODE = 0, bool UF = SAVE>
 static hipError_t launch_state_auto(const Args& a, hipStream_t st, const char* name = nullptr) {
   const int units = a.N * a.H * (MODE == 2 ? 2 : 1);
   if constexpr (sizeof(E) == 2) {
-    if (pick_dvs(units, DV) == 64) return launch_state<E, O, DK, DV, 64, OUT, SAVE, MODE>(a, st, name);
-    return launch_state<E, O, DK, DV, 16, OUT, SAVE, MODE>(a, st, name);
+    if (pick_dvs(units, DV) == 64) return launch_state<E, O, DK, DV, 64, OUT, SAVE, MODE, UF>(a, st, name);
+    return launch_state<E, O, DK, DV, 16, OUT, SAVE, MODE, UF>(a, st, name);
   } else {
-    return launch_state<E, O, DK, DV, 32, OUT, SAVE, MODE>(a, st, name);
+    return launch_state<E, O, DK, DV, 32, OUT, SAVE, MODE, UF>(a, st, name);
   }
 }
 
@@ -1167,9 +1169,10 @@ static hipError_t launch_state_auto(const Args& a, hipStream_t st, const char* n
 int fwd_segments(int N, int H, int dv, long long tokens, bool save) {
   if (const char* env = std::getenv("KDA_SEGMENTS")) {   // explicit stretch count (tests, tuning)
     const int p = std::atoi(env);
-    if (p >= 1) return save ? 1 : std::min(p, 64);
+    if (p >= 1) return std::min(p, 64);
   }
-  if (save || N <= 0) return 1;
+  (void)save;   // training mode segments the same way (the backward reuses the transfers)
+  if (N <= 0) return 1;
   // enough stretches that 64-column slices give every CU a chain (measured on
   // one 128K-token sequence with 16 heads: 8 stretches 3.8 ms, 4 stretches
   // 4.8 ms, none 5.4 ms; more than 8 lose to the longer scan)
@@ -1244,13 +1247,83 @@ __global__ __launch_bounds__(512) void kda_segment_scan(const Args a) {
     for (int o = tid; o < DK * DV; o += NT) a.final_state[((size_t)n * a.H + h) * SZ + o] = sS[(o / DV) * LS + o % DV];
 }
 
-template <typename E, typename O, int DK, int DV>
+// Reverse scan for the backward (the transposed maps): the gradient of the
+// state entering stretch p is dS_in(p) = M(p)^T dS_out(p) + dS_loc(p), where
+// dS_loc(p) is stretch p's reverse pass run from zero and dS_out(p) =
+// dS_in(p + 1) (dS_final for the last stretch).  Writes dS_out(p) of every
+// stretch to seg_in and d_init_state = dS_in(0).  One work-group per
+// (sequence, head); M^T is staged in LDS and the products are fp32 MFMA in a
+// fixed order.
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void kda_segment_rscan(const Args a) {
+  constexpr int LS = DV + 4, LM = DK + 4;   // padded rows
+  __shared__ __attribute__((aligned(16))) float sS[DK * LS];
+  __shared__ __attribute__((aligned(16))) float sM[DK * LM];   // M^T
+  constexpr int NT = 512, NTILE = (DK / 16) * (DV / 16), TPW = (NTILE + 7) / 8;
+  const int n = blockIdx.x / a.H, h = blockIdx.x % a.H, P = a.segs, tid = threadIdx.x;
+  const int w = wave_id(), l = lane_id(), r16 = l & 15, q4 = l >> 4;
+  constexpr size_t SZ = (size_t)DK * DV, MZ = (size_t)DK * DK;
+  const float* dfin = a.dfinal ? a.dfinal + ((size_t)n * a.H + h) * SZ : nullptr;
+  for (int o = tid; o < DK * DV; o += NT) sS[(o / DV) * LS + o % DV] = dfin ? dfin[o] : 0.f;
+  __syncthreads();
+  for (int p = P - 1; p >= 0; --p) {
+    const size_t v = ((size_t)n * P + p) * a.H + h;
+    for (int o = tid; o < DK * DV; o += NT) a.seg_in[v * SZ + o] = sS[(o / DV) * LS + o % DV];
+    for (int o = tid; o < DK * DK; o += NT) sM[(o % DK) * LM + o / DK] = a.seg_m[v * MZ + o];
+    __syncthreads();
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + 8 * i, mt = t % (DK / 16), nt = t / (DK / 16);
+      acc[i] = zero4();
+      if (t < NTILE) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          acc[i][ii] = a.seg_loc[v * SZ + (size_t)(16 * mt + 4 * q4 + ii) * DV + 16 * nt + r16];
+        for (int kb = 0; kb < DK / 16; ++kb)
+          acc[i] = mm16_f32(sM + 16 * mt * LM + 16 * kb, LM, sS + 16 * kb * LS + 16 * nt, LS, acc[i]);
+      }
+    }
+    __syncthreads();   // every read of this stretch's dS and M^T is done
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = w + 8 * i, mt = t % (DK / 16), nt = t / (DK / 16);
+      if (t < NTILE) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) sS[(16 * mt + 4 * q4 + ii) * LS + 16 * nt + r16] = acc[i][ii];
+      }
+    }
+    __syncthreads();
+  }
+  if (a.dinit)
+    for (int o = tid; o < DK * DV; o += NT) a.dinit[((size_t)n * a.H + h) * SZ + o] = sS[(o / DV) * LS + o % DV];
+}
+
+hipError_t launch_segment_map(const Args& a, hipStream_t st) {
+  const int NV = a.N * a.segs;
+  KDA_TIMED("kda_seg_map", st,
+            hipLaunchKernelGGL(kda_segment_map, dim3((NV + 256) / 256), dim3(256), 0, st, a.seq_chunk0, a.N, a.segs,
+                               a.vsc0, a.vord));
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_segment_rscan(const Args& a, hipStream_t st) {
+  KDA_TIMED("kda_seg_rscan", st,
+            hipLaunchKernelGGL((kda_segment_rscan<DK, DV>), dim3(a.N * a.H), dim3(512), 0, st, a));
+  return hipGetLastError();
+}
+template hipError_t launch_segment_rscan<64, 64>(const Args&, hipStream_t);
+template hipError_t launch_segment_rscan<64, 128>(const Args&, hipStream_t);
+template hipError_t launch_segment_rscan<128, 64>(const Args&, hipStream_t);
+template hipError_t launch_segment_rscan<128, 128>(const Args&, hipStream_t);
+
+// TRAIN: the prep ran in training mode (fp32 U~) and the final pass keeps the
+// backward's intermediates; OUT: the final pass writes the outputs.
+template <typename E, typename O, int DK, int DV, bool TRAIN, bool OUT>
 static hipError_t launch_segmented_state(const Args& a, hipStream_t st) {
   const int P = a.segs, NV = a.N * P;
-  KDA_TIMED("kda_seg_map", st,
-            hipLaunchKernelGGL(kda_segment_map, dim3((NV + 256) / 256), dim3(256), 0, st, a.seq_chunk0, a.N, P,
-                               a.vsc0, a.vord));
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_segment_map(a, st);
   if (e != hipSuccess) return e;
   Args av = a;   // the stretches as sequences of their own
   av.N = NV;
@@ -1261,23 +1334,24 @@ static hipError_t launch_segmented_state(const Args& a, hipStream_t st) {
   al.init = nullptr;
   al.final_state = a.seg_loc;
   if constexpr (DK == DV) {
-    if ((e = launch_state_auto<E, O, DK, DV, false, false, 2>(al, st, "kda_seg_local_transfer")) != hipSuccess)
+    if ((e = launch_state_auto<E, O, DK, DV, false, false, 2, TRAIN>(al, st, "kda_seg_local_transfer")) != hipSuccess)
       return e;
   } else {
-    if ((e = launch_state_auto<E, O, DK, DV, false, false>(al, st, "kda_seg_local")) != hipSuccess) return e;
+    if ((e = launch_state_auto<E, O, DK, DV, false, false, 0, TRAIN>(al, st, "kda_seg_local")) != hipSuccess) return e;
     Args am = av;
     am.init = nullptr;
     am.final_state = a.seg_m;
-    if ((e = launch_state_auto<E, O, DK, DK, false, false, 1>(am, st, "kda_seg_transfer")) != hipSuccess) return e;
+    if ((e = launch_state_auto<E, O, DK, DK, false, false, 1, TRAIN>(am, st, "kda_seg_transfer")) != hipSuccess)
+      return e;
   }
   KDA_TIMED("kda_seg_scan", st,
             hipLaunchKernelGGL((kda_segment_scan<DK, DV>), dim3(a.N * a.H), dim3(512), 0, st, a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  Args ab = av;   // every stretch from its true entering state, with the outputs
+  Args ab = av;   // every stretch from its true entering state, with the outputs (and what the backward keeps)
   ab.out = a.out;
   ab.init = a.seg_in;
   ab.final_state = nullptr;
-  return launch_state_auto<E, O, DK, DV, true, false>(ab, st);
+  return launch_state_auto<E, O, DK, DV, OUT, TRAIN>(ab, st);
 }
 
 // BWD: also keep what the backward pass needs (T, the un-beta Gram, fp32 Kh and U~).
@@ -1322,12 +1396,13 @@ hipError_t launch_fwd(const Args& a, hipStream_t st, bool save) {
     } else {
       e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_save");
       if (e != hipSuccess) return e;
+      if (a.segs > 1) return launch_segmented_state<E, O, DK, DV, true, true>(a, st);
       return launch_state_auto<E, O, DK, DV, true, true>(a, st);
     }
   }
   e = launch_prep<E, DK, DV, false>(a, st, "kda_prep");
   if (e != hipSuccess) return e;
-  if (a.segs > 1) return launch_segmented_state<E, O, DK, DV>(a, st);
+  if (a.segs > 1) return launch_segmented_state<E, O, DK, DV, false, true>(a, st);
   return launch_state_auto<E, O, DK, DV, true, false>(a, st);
 }
 
@@ -1339,6 +1414,7 @@ hipError_t launch_bwd_front(const Args& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   e = launch_prep<E, DK, DV, true>(a, st, "kda_prep_bwd");
   if (e != hipSuccess) return e;
+  if (a.segs > 1) return launch_segmented_state<E, float, DK, DV, true, false>(a, st);
   return launch_state_auto<E, float, DK, DV, false, true>(a, st);
 }
 

@@ -86,6 +86,8 @@ hipError_t launch_chunk_map(const Args& a, hipStream_t st);
 int device_cus();                  // compute units of the current device
 int fwd_segments(int N, int H, int dv, long long tokens, bool save);   // stretches per sequence (segment scan)
 int pick_dvs(int units, int dv);   // value-slice width of the sequential passes (bf16 inputs)
+hipError_t launch_segment_map(const Args& a, hipStream_t st);   // stretches of each sequence (vsc0, vord)
+template <int DK, int DV> hipError_t launch_segment_rscan(const Args& a, hipStream_t st);   // backward scan
 template <typename E, typename O, int DK, int DV> hipError_t launch_fwd(const Args& a, hipStream_t st, bool save);
 template <typename E, int DK, int DV> hipError_t launch_bwd_front(const Args& a, hipStream_t st);
 template <typename E, typename O, int DK, int DV> hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved);

@@ -1,5 +1,7 @@
-"""Segment scan of the forward state pass (long sequences cut into stretches that run in parallel,
-joined by a short scan of their transfers) against the float64 oracle.
+"""Segment scan of the sequential passes (long sequences cut into stretches that run in parallel,
+joined by a short scan of their transfers) against the float64 oracle: the forward, and the
+training step, whose forward keeps the backward's intermediates from every stretch's true entering
+state and whose reverse pass is joined by a reverse scan with the transposed transfers.
 
 KDA_SEGMENTS forces the stretch count per sequence; without it the library segments only long
 sequences that leave CUs idle (configs 2 and 3 in test_gpu_fwd.py take that path).
@@ -10,7 +12,7 @@ import numpy as np
 import pytest
 
 import kda_inputs as ki
-from kda_testutil import TOL, gpu_fwd, np_of, oracle_fwd, rel_err, to_gpu
+from kda_testutil import TOL, gpu_bwd, gpu_fwd, np_of, oracle_bwd, oracle_fwd, rel_err, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -79,3 +81,82 @@ def test_auto_segmentation_choice(segments):
     os.environ.pop("KDA_SEGMENTS", None)
     assert kda.workspace_bytes(8, 4096, 16, 128, 128, torch.bfloat16) == kda.workspace_bytes(
         8, 4096, 16, 128, 128, torch.bfloat16, backward=False)
+
+
+GRADS = ["dq", "dk", "dv", "dlog_alpha", "dbeta", "d_init"]
+TRAIN_CASES = [
+    ("bf16", (1000, 700, 323), 2, 128, 128, 3),
+    ("bf16", (2000,), 2, 128, 128, 5),
+    ("f32", (900, 64, 7, 500), 2, 64, 64, 2),
+    ("bf16", (640, 130), 3, 64, 128, 4),
+    ("bf16", (200, 1, 65), 2, 128, 64, 7),   # more stretches than some sequences have chunks
+]
+
+
+@pytest.mark.parametrize("dtype,lengths,H,dk,dv,P", TRAIN_CASES, ids=lambda x: str(x))
+def test_segmented_training_step_matches_oracle(segments, dtype, lengths, H, dk, dv, P):
+    """fwd(save_for_backward) + bwd(use_saved) with P stretches per sequence: outputs and every
+    gradient within the parity bound, and bit-identical to the self-contained backward (which
+    recomputes the forward with the same stretches)."""
+    import torch
+    import gated_delta_rule_79_amd as kda
+    w = ki.small(dtype=dtype, lengths=lengths, H=H, dk=dk, dv=dv)
+    inp = ki.make_inputs(w, with_grads=True)
+    g = to_gpu(inp, dtype)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    segments(P)
+    ws = torch.empty(kda.workspace_bytes(1, g["q"].shape[1], H, dk, dv, dt, num_seqs=len(lengths), backward=True),
+                     dtype=torch.uint8, device="cuda")
+    o, fin = kda.fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], init_state=g["init_state"],
+                     cu_seqlens=g["cu_seqlens"], workspace=ws, save_for_backward=True)
+    got = kda.bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["d_out"], init_state=g["init_state"],
+                  d_final_state=g["d_final_state"], cu_seqlens=g["cu_seqlens"], workspace=ws, use_saved=True)
+    rec = gpu_bwd(g)
+    torch.cuda.synchronize()
+    ro, rf = oracle_fwd(inp)
+    ref = oracle_bwd(inp)
+    errs = {"o": rel_err(np_of(o)[0], ro), "final_state": rel_err(np_of(fin), rf)}
+    for name, a, b in zip(GRADS, got, ref):
+        ga = np_of(a)
+        errs[name] = rel_err(ga if name == "d_init" else ga[0], b)
+    print(f"P={P}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, f"errors above {TOL[dtype]}: {bad}"
+    for name, a, b in zip(GRADS, got, rec):
+        assert torch.equal(a, b), name
+
+
+def test_segmented_backward_without_state_grads(segments):
+    """No d_final_state (zero) and no d_init_state output on the segmented reverse pass."""
+    import torch
+    import gated_delta_rule_79_amd as kda
+    w = ki.small(dtype="bf16", lengths=(900, 260), H=2, dk=128, dv=128)
+    inp = ki.make_inputs(w, with_grads=True)
+    inp["d_final_state"] = None
+    g = to_gpu(inp, "bf16")
+    segments(4)
+    got = kda.bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["d_out"], init_state=g["init_state"],
+                  cu_seqlens=g["cu_seqlens"], need_d_init=False)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(inp)
+    assert got[5] is None
+    for name, a, b in zip(GRADS[:5], got[:5], ref[:5]):
+        assert rel_err(np_of(a)[0], b) <= TOL["bf16"], name
+
+
+def test_auto_segmentation_of_the_training_step(segments):
+    """A long single sequence with few heads is segmented in training mode too (stretch buffers in the
+    backward's workspace plan); the packed 8-sequence training batch is not."""
+    import torch
+    import gated_delta_rule_79_amd as kda
+    os.environ.pop("KDA_SEGMENTS", None)
+    long_one = kda.workspace_bytes(1, 131072, 16, 128, 128, torch.bfloat16, backward=True)
+    segments(1)
+    plain = kda.workspace_bytes(1, 131072, 16, 128, 128, torch.bfloat16, backward=True)
+    assert long_one > plain
+    os.environ.pop("KDA_SEGMENTS", None)
+    w = ki.config(4)
+    n = sum(w.lengths)
+    with_auto = kda.workspace_bytes(1, n, 16, 128, 128, torch.bfloat16, num_seqs=8, backward=True)
+    segments(1)
+    assert with_auto == kda.workspace_bytes(1, n, 16, 128, 128, torch.bfloat16, num_seqs=8, backward=True)
