@@ -194,3 +194,19 @@ def test_conv_full_size_sampled_channels():
     assert rel_err(np_of(dw[tch]), r[1]) <= TOL_SUM
     assert rel_err(np_of(db[tch]), r[2]) <= TOL_SUM
     assert rel_err(np_of(dinit[:, :, tch]), r[3]) <= TOL_Y
+
+
+def test_conv_no_tokens():
+    """Packed sequences that are all empty: y is empty, final_state = init_state, d_init_state =
+    d_final_state, dweight and dbias are zero."""
+    import gated_delta_rule_79_amd as kda
+    import torch
+    c, g = _inputs([0, 0, 0], 24, 3, "bf16")
+    y, fin = kda.conv_fwd(g["x"], g["weight"], g["bias"], g["init_state"], cu_seqlens=g["cu"], silu=True)
+    dx, dw, db, dinit = kda.conv_bwd(g["x"], g["weight"], g["dy"], g["bias"], g["init_state"], g["d_final_state"],
+                                     cu_seqlens=g["cu"], silu=True)
+    torch.cuda.synchronize()
+    assert y.shape == (1, 0, 24) and dx.shape == (1, 0, 24)
+    assert torch.equal(fin, g["init_state"])
+    assert torch.equal(dinit, g["d_final_state"])
+    assert not dw.any() and not db.any()
