@@ -79,11 +79,26 @@ def _bools(name):
     return [x == "true" for x in re.findall(r"\b(true|false)\b", name)]
 
 
+def _ints(name):
+    """Integer template arguments of a kernel name (mangled 'Li64E' or demangled ', 64')."""
+    import re
+    m = re.findall(r"Li(\d+)E", name)
+    if m:
+        return [int(x) for x in m]
+    inner = name[name.find("<") + 1:name.rfind(">")] if "<" in name else ""
+    return [int(x) for x in re.findall(r"(?:^|,)\s*(\d+)\s*(?=,|$)", inner)]
+
+
 def _short_name(name, train=True):
     """rocprofv3 kernel name -> the timing name the library uses (train: the forward saves for
     the backward, so the prep that keeps T etc. is the forward's)."""
     if "kda_state_rev" in name:
-        return "kda_state_bwd_revpass"
+        b = _bools(name)   # kda_state_rev<E, DK, DV, DVS, LOCAL>
+        return "kda_seg_rev_local" if b and b[-1] else "kda_state_bwd_revpass"
+    if "kda_segment_rscan" in name:
+        return "kda_seg_rscan"
+    if "kda_segment_scan" in name:
+        return "kda_seg_scan"
     if "kda_bwd_chunk" in name:
         return "kda_bwd_chunk"
     if "kda_chunk_map" in name:
@@ -97,8 +112,13 @@ def _short_name(name, train=True):
         bwd = (_bools(name) or [False])[0]   # <..., BWD, QKN[, GATE]>
         return ("kda_prep_save" if train else "kda_prep_bwd") if bwd else "kda_prep"
     if "kda_state" in name:
+        # kda_state<E, O, DK, DV, DVS, OUT, SAVE, PF, MODE, UF>: the bools are OUT, SAVE, UF and the
+        # last integer argument is MODE (2: a stretch's run from zero with its transfer)
         b = _bools(name)
-        out, save = (b[-2], b[-1]) if len(b) >= 2 else (True, False)
+        out, save = (b[0], b[1]) if len(b) >= 2 else (True, False)
+        ints = _ints(name)
+        if ints and ints[-1] == 2:
+            return "kda_seg_local_transfer"
         if out:
             return "kda_state_fwd_save" if save else "kda_state_fwd"
         return "kda_state_bwd_fwdpass"
