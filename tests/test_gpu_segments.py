@@ -160,3 +160,39 @@ def test_auto_segmentation_of_the_training_step(segments):
     with_auto = kda.workspace_bytes(1, n, 16, 128, 128, torch.bfloat16, num_seqs=8, backward=True)
     segments(1)
     assert with_auto == kda.workspace_bytes(1, n, 16, 128, 128, torch.bfloat16, num_seqs=8, backward=True)
+
+
+def test_segmented_training_full_size_sampled_heads(segments):
+    """The long-sequence workload (one 131,072-token sequence, H = 16) as a training step, with the
+    stretches the library chooses for it (8), in the launch configuration `bench.py --config 3 --train`
+    times; the oracle checks heads 3 and 12 over the whole sequence."""
+    import torch
+    import gated_delta_rule_79_amd as kda
+    os.environ.pop("KDA_SEGMENTS", None)
+    w = ki.config(3)
+    inp = ki.make_inputs(w, with_grads=True)
+    g = to_gpu(inp, "bf16")
+    T, H = g["q"].shape[1], w.H
+    auto = kda.workspace_bytes(1, T, H, 128, 128, torch.bfloat16, num_seqs=1, backward=True)
+    segments(1)
+    assert auto > kda.workspace_bytes(1, T, H, 128, 128, torch.bfloat16, num_seqs=1, backward=True)   # segmented
+    os.environ.pop("KDA_SEGMENTS", None)
+    ws = torch.empty(kda.workspace_bytes(1, T, H, 128, 128, torch.bfloat16, num_seqs=1, backward=True),
+                     dtype=torch.uint8, device="cuda")
+    o, fin = kda.fwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], init_state=g["init_state"],
+                     cu_seqlens=g["cu_seqlens"], workspace=ws, save_for_backward=True)
+    got = kda.bwd(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["d_out"], init_state=g["init_state"],
+                  d_final_state=g["d_final_state"], cu_seqlens=g["cu_seqlens"], workspace=ws, use_saved=True)
+    torch.cuda.synchronize()
+    heads = [3, 12]
+    units = [(0, h) for h in heads]
+    ro, rf = oracle_fwd(inp, units=units)
+    ref = oracle_bwd(inp, units=units)
+    errs = {"o": rel_err(np_of(o)[0][:, heads], ro[:, heads]), "final_state": rel_err(np_of(fin)[:, heads], rf[:, heads])}
+    for name, a, b in zip(GRADS, got, ref):
+        ga = np_of(a)
+        ga = ga if name == "d_init" else ga[0]
+        errs[name] = rel_err(ga[:, heads], b[:, heads])
+    print("full size, heads 3 and 12: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL["bf16"]}
+    assert not bad, f"errors above {TOL['bf16']}: {bad}"
