@@ -164,8 +164,8 @@ def test_auto_segmentation_of_the_training_step(segments):
 
 def test_segmented_training_full_size_sampled_heads(segments):
     """The long-sequence workload (one 131,072-token sequence, H = 16) as a training step, with the
-    stretches the library chooses for it (8), in the launch configuration `bench.py --config 3 --train`
-    times; the oracle checks heads 3 and 12 over the whole sequence."""
+    stretches the library chooses for it (8), in the launch configuration the benchmark's long-sequence
+    training step times; the oracle checks heads 3 and 12 over the whole sequence."""
     import torch
     import gated_delta_rule_79_amd as kda
     os.environ.pop("KDA_SEGMENTS", None)
