@@ -210,3 +210,40 @@ def test_conv_no_tokens():
     assert torch.equal(fin, g["init_state"])
     assert torch.equal(dinit, g["d_final_state"])
     assert not dw.any() and not db.any()
+
+
+@pytest.mark.parametrize("silu", [False, True])
+def test_conv_backward_rows_without_cu_seqlens(silu):
+    """B rows of T tokens (no cu_seqlens): gradients against the oracle over the same packed rows."""
+    import gated_delta_rule_79_amd as kda
+    import torch
+    c = ki.conv_inputs([300, 300, 300], 48, 4, dtype="bf16", seed=21)
+    x = _t(c["x"], "bf16").reshape(3, 300, 48)
+    dy = _t(c["dy"], "bf16").reshape(3, 300, 48)
+    dx, dw, db, dinit = kda.conv_bwd(x, _t(c["weight"]), dy, _t(c["bias"]), _t(c["init_state"]),
+                                     _t(c["d_final_state"]), silu=silu)
+    torch.cuda.synchronize()
+    r = sc.short_conv_bwd(c["x"], c["weight"], c["cu_seqlens"], c["dy"], bias=c["bias"], init_state=c["init_state"],
+                          d_final_state=c["d_final_state"], silu=silu)
+    assert rel_err(np_of(dx).reshape(r[0].shape), r[0]) <= TOL_Y
+    assert rel_err(np_of(dw), r[1]) <= TOL_SUM and rel_err(np_of(db), r[2]) <= TOL_SUM
+    assert rel_err(np_of(dinit), r[3]) <= TOL_Y
+
+
+def test_conv_bf16_outputs_round_once():
+    """bf16 y (forward and decode) is the fp32 result rounded once to bf16."""
+    import gated_delta_rule_79_amd as kda
+    import torch
+    c, g = _inputs([300, 0, 1, 2, 777], 72, 4, "bf16")
+    y32, f32 = kda.conv_fwd(g["x"], g["weight"], g["bias"], g["init_state"], cu_seqlens=g["cu"], silu=True)
+    y16, f16 = kda.conv_fwd(g["x"], g["weight"], g["bias"], g["init_state"], cu_seqlens=g["cu"], silu=True,
+                            out_dtype=torch.bfloat16)
+    d = ki.conv_decode_inputs(5, 3, 64, 4, 5, dtype="bf16", seed=8)
+    pa, pb = _t(d["state_pool"]), _t(d["state_pool"])
+    yd32 = kda.conv_decode(_t(d["x"], "bf16"), _t(d["weight"]), pa, bias=_t(d["bias"]), silu=True)
+    yd16 = kda.conv_decode(_t(d["x"], "bf16"), _t(d["weight"]), pb, bias=_t(d["bias"]), silu=True,
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16 and torch.equal(y16, y32.to(torch.bfloat16))
+    assert torch.equal(f16, f32)
+    assert torch.equal(yd16, yd32.to(torch.bfloat16)) and torch.equal(pa, pb)
