@@ -8,10 +8,15 @@ H=16, dk=dv=128, bf16 inputs, fp32 states, fp32 outputs and gradients.
 
 Prints one JSON line: tokens/s for the whole step, the roofline of the
 dominant kernel (HIP-event durations recorded live around every launch of the
-timed steps), the whole-step roofline, and the float64 CPU oracle timed on a
-bounded sample of the same workload on this host's cores.
+timed steps), the whole-step HBM and bf16-MFMA rooflines with achieved TFLOP/s,
+the float64 CPU oracle timed on a bounded sample of the same workload on this
+host's cores, and (configs_fwd) the forward pass of the three single-sequence
+workloads (T = 4K, 32K with the sharp gate, 128K; H=16, d=128, bf16) timed in
+the same run.  Algorithmic bytes count outputs and gradients at the inputs'
+storage size (the primal dtype): 1,282 B forward and 2,308 B backward per
+token-head at d = 128, plus the states.
 
-    python bench.py [--steps K] [--warmup W] [--config 4] [--fwd-only]
+    python bench.py [--steps K] [--warmup W] [--config 4] [--fwd-only] [--no-extra-configs]
 """
 from __future__ import annotations
 
@@ -31,14 +36,12 @@ FP32_PEAK_TFLOPS = 157.3
 METRIC = "KDA fwd(+bwd) tokens/s and % MFMA/HBM roofline, H=16 d=128 bf16, T=4K\u2013128K"
 
 CSRC = os.path.join(ROOT, "gated_delta_rule_79_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")   # training-step workload
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def traffic_file(workload):
-    """Counter summary of a workload: the training step's file, or one named after the workload."""
-    if workload.startswith(("decode_", "conv_")):
-        return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
-    return TRAFFIC_FILE
+    """Counter summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled) of one workload."""
+    return os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
 
 
 CONV_SOURCES = ("kda_conv.hip", "kda_conv.hpp")
@@ -150,7 +153,7 @@ def ingest_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_b
            "calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": f_kib, "copy_write_kib": w_kib,
                            "fetch_scale": scale_f, "write_scale": scale_w},
            "kernels": kernels}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_file(workload), "w") as f:
         json.dump(doc, f, indent=1, sort_keys=True)
         f.write("\n")
@@ -169,50 +172,56 @@ def measured_traffic(kernel, workload):
     return int(k["bytes"]) if k else None
 
 
-def algorithmic_bytes(w, tokens, n_seqs, fwd_only, eout=4):
-    """Compulsory HBM bytes of the path (inputs read once, outputs written once)."""
+def algorithmic_bytes(w, tokens, n_seqs, fwd_only):
+    """Compulsory HBM bytes of the path: inputs read once, outputs written once.  Outputs and
+    gradients are counted at the inputs' storage size (the primal dtype, 1,282 B forward and
+    2,308 B backward per token-head at d = 128 in bf16) whatever dtype a run stores them in, so
+    fp32 outputs cost time without earning bytes."""
     H, dk, dv = w.H, w.dk, w.dv
-    ein = 2 if w.dtype == "bf16" else 4
+    e = 2 if w.dtype == "bf16" else 4
     th = tokens * H
     state = n_seqs * H * dk * dv * 4
-    fwd = th * (ein * (2 * dk + dk + dv) + ein) + th * eout * dv + 2 * state      # q,k,la,v,beta -> o; S0 in, S_T out
+    fwd = th * (e * (2 * dk + dk + dv) + e) + th * e * dv + 2 * state      # q,k,la,v,beta -> o; S0 in, S_T out
     if fwd_only:
         return fwd, {"fwd": fwd}
-    bwd = (th * (ein * (2 * dk + dk + dv) + ein + ein * dv)                       # q,k,la,v,beta,dO
-           + th * eout * (2 * dk + dk + dv + 1)                                   # dq,dk,dla,dv,dbeta
-           + 3 * state)                                                           # S0, dS_T in; dS0 out
+    bwd = (th * (e * (2 * dk + dk + dv) + e + e * dv)                       # q,k,la,v,beta,dO
+           + th * e * (2 * dk + dk + dv + 1)                                # dq,dk,dla,dv,dbeta
+           + 3 * state)                                                     # S0, dS_T in; dS0 out
     return fwd + bwd, {"fwd": fwd, "bwd": bwd}
 
 
+def flops_per_token_head(d, C=64):
+    """Algorithmic flops per token-head of the chunked form (triangular products counted once):
+    forward = Gram blocks A_kk, A_qk + W, U~ (4 x C/2 x d x 2) + W S, Qt S, Kh^T U (3 x 2 d^2)
+    + Aqk U (C/2 x d x 2) + the triangular inverse (C^2 / 3); 141 kFLOP at d = 128.  The
+    backward is 2.75 times the forward (387 kFLOP at d = 128): dU, dS over the chain, the
+    value-side contractions, the T products and the gated products."""
+    fwd = 4 * (C // 2) * d * 2 + 3 * 2 * d * d + (C // 2) * d * 2 + C * C / 3
+    return fwd, 2.75 * fwd
+
+
 def algorithmic_flops(w, tokens, fwd_only):
-    """Chunked-form flops per token-head (C=64, triangles counted once), as derived for the roofline."""
-    d = w.dk
-    C = 64
-    # forward per token-head: Gram blocks (2 * C/2 * d * 2), W, U~ (2 * C/2 * d * 2), W S, Qt S, Kh^T U (3 * 2 d^2),
-    # Aqk U (C/2 * d * 2)
-    fwd = 2 * (C // 2) * d * 2 + 2 * (C // 2) * d * 2 + 3 * 2 * d * d + (C // 2) * d * 2
-    bwd = 2.75 * fwd
-    per = fwd if fwd_only else fwd + bwd
-    return per * tokens * w.H
+    f, b = flops_per_token_head(w.dk)
+    return (f if fwd_only else f + b) * tokens * w.H
 
 
-def kernel_alg_bytes(name, w, tokens, n_seqs, eout=4):
-    """Compulsory bytes one launch of a kernel must move: its share of the path's
-    own inputs and outputs (intermediates in the workspace are not counted)."""
+def kernel_alg_bytes(name, w, tokens, n_seqs):
+    """Compulsory bytes one launch of a kernel must move: its share of the path's own inputs
+    and outputs (intermediates in the workspace are not counted; outputs at the primal size)."""
     H, dk, dv = w.H, w.dk, w.dv
-    ein = 2 if w.dtype == "bf16" else 4
+    e = 2 if w.dtype == "bf16" else 4
     th = tokens * H
     state = n_seqs * H * dk * dv * 4
     table = {
-        "kda_prep": th * (ein * (3 * dk + dv) + ein),                     # reads q, k, log_alpha, v, beta
-        "kda_prep_bwd": th * (ein * (3 * dk + dv) + ein),                 # same reads, backward recompute
-        "kda_prep_save": th * (ein * (3 * dk + dv) + ein),                # forward prep keeping the backward's data
-        "kda_state_fwd_save": th * eout * dv + 2 * state,                 # as kda_state_fwd
-        "kda_state_fwd": th * eout * dv + 2 * state,                      # writes o; reads S0, writes S_T
+        "kda_prep": th * (e * (3 * dk + dv) + e),                         # reads q, k, log_alpha, v, beta
+        "kda_prep_bwd": th * (e * (3 * dk + dv) + e),                     # same reads, backward recompute
+        "kda_prep_save": th * (e * (3 * dk + dv) + e),                    # forward prep keeping the backward's data
+        "kda_state_fwd_save": th * e * dv + 2 * state,                    # as kda_state_fwd
+        "kda_state_fwd": th * e * dv + 2 * state,                         # writes o; reads S0, writes S_T
         "kda_state_bwd_fwdpass": state,                                   # reads S0
-        "kda_state_bwd_revpass": th * ein * dv + 2 * state,               # reads dO, dS_T; writes dS0
+        "kda_state_bwd_revpass": th * e * dv + 2 * state,                 # reads dO, dS_T; writes dS0
         # reads q, k, log_alpha, v, dO, beta; writes dq, dk, dlog_alpha, dv, dbeta
-        "kda_bwd_chunk": th * (ein * (3 * dk + 2 * dv) + ein + eout * (3 * dk + dv + 1)),
+        "kda_bwd_chunk": th * (e * (3 * dk + 2 * dv) + e + e * (3 * dk + dv + 1)),
         "kda_chunk_map": 0,
     }
     return table.get(name, 0)
@@ -277,7 +286,6 @@ def decode_bench(args, dev) -> int:
     B, T = (int(x) for x in args.decode.split(","))
     H, dk, dv = 16, 128, 128
     P = B
-    eout = 2 if args.out_bf16 else 4
     odt = torch.bfloat16 if args.out_bf16 else torch.float32
     print(f"[bench] decode inputs B={B} T={T}", file=sys.stderr, flush=True)
     inp = ki.decode_inputs(B, T, H, dk, dv, P, dtype="bf16", seed=99)
@@ -311,7 +319,8 @@ def decode_bench(args, dev) -> int:
     avg_ms = tot_ms / max(n_launch, 1)
     # algorithmic bytes: each (sequence, head) state read and written once (fp32), the tokens' q, k,
     # log_alpha, v, beta read (bf16) and outputs written, plus the index list
-    ab = B * H * (2 * dk * dv * 4 + T * (2 * (3 * dk + dv) + 2 + eout * dv)) + 4 * B
+    # (outputs counted at the inputs' bf16 size, whatever out_dtype stores them in)
+    ab = B * H * (2 * dk * dv * 4 + T * (2 * (3 * dk + dv) + 2 + 2 * dv)) + 4 * B
     ach = ab / (avg_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic("kda_decode_step", f"decode_B{B}_T{T}"),
@@ -356,7 +365,6 @@ def conv_bench(args, dev) -> int:
     D, W = 6144, 4
     lengths = list(ki.config(4).lengths)
     tokens, N = int(sum(lengths)), len(lengths)
-    eout = 2 if args.out_bf16 else 4
     odt = torch.bfloat16 if args.out_bf16 else torch.float32
     print(f"[bench] conv inputs: {N} sequences, {tokens} tokens, D={D}, W={W}", file=sys.stderr, flush=True)
     c = ki.conv_inputs(lengths, D, W, dtype="bf16", seed=4)
@@ -395,8 +403,9 @@ def conv_bench(args, dev) -> int:
     kt = kda.timing_read()
     kda.timing_enable(False)
     # algorithmic bytes per launch: the forward reads x and writes y; the backward reads x and dy and
-    # writes dx (states, weights and the per-channel sums are under 0.1% and left out)
-    alg = {"kda_conv_fwd": tokens * D * (2 + eout), "kda_conv_bwd": tokens * D * (2 + 2 + eout)}
+    # writes dx, outputs counted at the inputs' bf16 size (states, weights and the per-channel sums are
+    # under 0.1% and left out)
+    alg = {"kda_conv_fwd": tokens * D * (2 + 2), "kda_conv_bwd": tokens * D * (2 + 2 + 2)}
     step_bytes = sum(alg.values())
     dom = max(alg, key=lambda k: kt[k][0])
     tot_ms, n_launch = kt[dom]
@@ -448,6 +457,9 @@ def main() -> int:
                     help="time the training step (forward + backward) on a forward-only workload too "
                          "(dO and dS_final drawn as for the varlen workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the forward timings of the T = 4K, 32K and 128K single-sequence workloads that "
+                         "the default training-step run adds under configs_fwd")
     ap.add_argument("--out-bf16", action="store_true", help="bf16 outputs/gradients instead of fp32")
     ap.add_argument("--recompute", action="store_true",
                     help="self-contained backward (recomputes the forward) instead of the training step in which "
@@ -481,7 +493,6 @@ def main() -> int:
               f"part of this build", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import gated_delta_rule_79_amd as kda
@@ -508,7 +519,31 @@ def main() -> int:
         return conv_bench(args, dev)
 
     w = ki.config(args.config)
-    fwd_only = args.fwd_only or not (w.backward or args.train)
+    res = run_workload(args, dev, w, with_cpu=not args.no_cpu_baseline, steps=args.steps, warmup=args.warmup)
+    line = res["line"]
+    if args.config == 4 and not args.fwd_only and not args.no_extra_configs:
+        # the forward of the three single-sequence workloads (T = 4K, 32K with the sharp gate, 128K),
+        # timed in the same run; not the headline value, which is the training step above
+        extra = {}
+        for c in (1, 2, 3):
+            r = run_workload(args, dev, ki.config(c), with_cpu=False, steps=max(1, min(args.steps, 10)),
+                             warmup=max(1, min(args.warmup, 2)), force_fwd=True)
+            extra[str(c)] = r["summary"]
+            del r
+            torch.cuda.empty_cache()
+        line["configs_fwd"] = extra
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_workload(args, dev, w, with_cpu, steps, warmup, force_fwd=False):
+    """Time `steps` steps of workload w (forward, or forward + backward) with inputs resident in HBM."""
+    import torch
+
+    import gated_delta_rule_79_amd as kda
+    import kda_inputs as ki
+
+    fwd_only = force_fwd or args.fwd_only or not (w.backward or args.train)
     print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
     inp = ki.make_inputs(w, with_grads=not fwd_only, raw=args.fused_prep)
     prep = dict(qk_l2norm=True, gate_logsigmoid=True) if args.fused_prep else {}
@@ -518,12 +553,11 @@ def main() -> int:
     init = torch.from_numpy(inp["init_state"]).to(dev) if inp["init_state"] is not None else None
     varlen = w.lengths is not None
     cu = torch.from_numpy(inp["cu_seqlens"]).to(dev) if varlen else None
-    if varlen:
-        pass
-    else:
+    if not varlen:
         t = {k: v.reshape(w.B, w.T, *v.shape[2:]) for k, v in t.items()}
     tokens = int(sum(inp["lengths"]))
     n_seqs = len(inp["lengths"])
+    d_out = d_fin = None
     if not fwd_only:
         d_out = torch.from_numpy(inp["d_out"]).to(dev, dt).unsqueeze(0)
         if not varlen:
@@ -534,7 +568,7 @@ def main() -> int:
                                          backward=not fwd_only, **prep), dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, w.H, w.dv), dtype=odt, device=dev)
     fin = torch.empty((n_seqs, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
-    grads = None
+    grads = dinit = None
     if not fwd_only:
         grads = tuple(torch.empty(x.shape, dtype=odt, device=dev) for x in (t["q"], t["k"], t["v"], t["log_alpha"],
                                                                             t["beta"]))
@@ -549,19 +583,19 @@ def main() -> int:
             kda.bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], d_out, init_state=init, d_final_state=d_fin,
                     cu_seqlens=cu, workspace=ws, out_dtype=odt, grads=grads, d_init=dinit, use_saved=train, **prep)
 
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print(f"[bench] {w.name}: warmup {warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: timing {steps} steps", file=sys.stderr, flush=True)
     kda.timing_enable(True)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
@@ -569,46 +603,56 @@ def main() -> int:
     ms_total = e0.elapsed_time(e1)
     kt = kda.timing_read()
     kda.timing_enable(False)
-    ms_step = ms_total / args.steps
+    ms_step = ms_total / steps
     value = tokens / (ms_step * 1e-3)
 
-    # dominant kernel roofline
+    # dominant kernel roofline: algorithmic bytes (and flops) of one launch over its average duration,
+    # the duration from HIP events recorded around every launch on the launch stream
     dom = max(kt.items(), key=lambda kv: kv[1][0]) if kt else None
     roof = None
     if dom:
         name, (tot_ms, n_launch) = dom
         avg_ms = tot_ms / max(n_launch, 1)
-        ab = kernel_alg_bytes(name, w, tokens, n_seqs, 2 if args.out_bf16 else 4)
+        ab = kernel_alg_bytes(name, w, tokens, n_seqs)
         af = kernel_alg_flops(name, w, tokens)
+        gbs = ab / (avg_ms * 1e-3) / 1e9
+        tfs = af / (avg_ms * 1e-3) / 1e12
         if ab / (HBM_PEAK_GBS * 1e9) >= af / (BF16_PEAK_TFLOPS * 1e12):
-            ach = ab / (avg_ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4)}
+            roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)}
         else:
-            ach = af / (avg_ms * 1e-3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+            roof = {"bound": "mfma", "achieved": round(tfs, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tfs / BF16_PEAK_TFLOPS, 4)}
         roof.update({"traffic": measured_traffic(name, w.name), "kernel": name, "avg_launch_ms": round(avg_ms, 4),
-                     "launches": n_launch, "alg_bytes_per_launch": int(ab), "alg_flops_per_launch": int(af)})
-    total_bytes, parts = algorithmic_bytes(w, tokens, n_seqs, fwd_only, 2 if args.out_bf16 else 4)
+                     "launches": n_launch, "alg_bytes_per_launch": int(ab), "alg_flops_per_launch": int(af),
+                     "mfma": {"achieved_tflops": round(tfs, 3), "peak_tflops": BF16_PEAK_TFLOPS,
+                              "frac": round(tfs / BF16_PEAK_TFLOPS, 5)}})
+    total_bytes, parts = algorithmic_bytes(w, tokens, n_seqs, fwd_only)
     flops = algorithmic_flops(w, tokens, fwd_only)
     t_hbm = total_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
-    step_roof = {"alg_bytes": int(total_bytes), "alg_flops": int(flops), "roofline_ms": round(max(t_hbm, t_mfma) * 1e3, 4),
-                 "frac": round(max(t_hbm, t_mfma) / (ms_step * 1e-3), 4), "bound": "hbm" if t_hbm >= t_mfma else "mfma"}
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    step_roof = {"alg_bytes": int(total_bytes), "alg_flops": int(flops),
+                 "roofline_ms": round(max(t_hbm, t_mfma) * 1e3, 4),
+                 "frac": round(max(t_hbm, t_mfma) / (ms_step * 1e-3), 4), "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                 "hbm": {"achieved_gbs": round(total_bytes / (ms_step * 1e-3) / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+                         "frac": round(t_hbm / (ms_step * 1e-3), 4)},
+                 "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                          "frac": round(tflops / BF16_PEAK_TFLOPS, 5)}}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp, w, not fwd_only, prepped=args.fused_prep)
 
+    kernels = {k: round(v[0] / steps, 4) for k, v in kt.items()}
     line = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -622,12 +666,17 @@ def main() -> int:
                    "input_prep": "fused (raw q, k, gate)" if args.fused_prep else "inputs already prepared"},
         "roofline": roof,
         "step_roofline": step_roof,
-        "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in kt.items()},
+        "tflops": round(tflops, 2),
+        "kernels_ms_per_step": kernels,
         "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 3),
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    summary = {"workload": w.name, "tokens": tokens, "steps": steps, "ms_per_step": round(ms_step, 4),
+               "tokens_per_s": round(value, 1), "tflops": round(tflops, 2),
+               "hbm_frac": step_roof["hbm"]["frac"], "mfma_frac": step_roof["mfma"]["frac"],
+               "roofline_ms": step_roof["roofline_ms"], "kernels_ms_per_step": kernels,
+               "dominant": roof}
+    return {"line": line, "summary": summary}
 
 
 if __name__ == "__main__":

@@ -46,19 +46,26 @@ bool dims_ok(const kda_desc* d) {
          (d->out_dtype == KDA_F32 || (d->out_dtype == KDA_BF16 && d->dtype == KDA_BF16));
 }
 
-// Number of sequences and chunk slots; varlen when `varlen`.
+// Number of sequences and chunk slots; varlen when `varlen`.  Sizes are taken in
+// 64 bits and bounded so that every work-item count and launch grid derived from
+// them (chunk slots x heads; sequences x heads x value slices x stretches, at most
+// 64 stretches and 8 slices) fits an int.
 bool shape_of(const kda_desc* d, bool varlen, int* N, int* max_chunks) {
   if (d->B < 1 || d->T < 0 || d->H < 1 || d->H > 65535) return false;
   const long long tok = (long long)d->B * d->T;
   if (tok >= (1LL << 31)) return false;
+  long long n, mc;
   if (varlen) {
     if (d->B != 1 || d->num_seqs < 1) return false;
-    *N = d->num_seqs;
-    *max_chunks = d->T / CH + d->num_seqs;
+    n = d->num_seqs;
+    mc = (long long)d->T / CH + n;
   } else {
-    *N = d->B;
-    *max_chunks = d->B * ((d->T + CH - 1) / CH);
+    n = d->B;
+    mc = (long long)d->B * (((long long)d->T + CH - 1) / CH);
   }
+  if (mc * d->H >= (1LL << 31) || n * d->H >= (1LL << 22)) return false;
+  *N = (int)n;
+  *max_chunks = (int)mc;
   return true;
 }
 
@@ -85,7 +92,7 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
     p.UtF = take(nb * dv * CH * 4);
     p.G = take(nb * CH * CH * 4);
     p.KhF = take(nb * CH * dk * 4);
-    p.S = take(nb * dk * dv * e);
+    p.S = take(nb * dk * dv * 4);
     p.U = take(nb * dv * CH * 4);
     p.dS = take(nb * dk * dv * 4);
     p.dU = take(nb * dv * CH * 4);
@@ -140,7 +147,7 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
   a.wsUtF = fptr(p.UtF);
   a.wsG = fptr(p.G);
   a.wsKhF = fptr(p.KhF);
-  a.wsS = p.S ? b + p.S : nullptr;
+  a.wsS = fptr(p.S);
   a.wsU = fptr(p.U);
   a.wsdS = fptr(p.dS);
   a.wsdU = fptr(p.dU);

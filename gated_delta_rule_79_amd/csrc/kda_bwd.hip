@@ -336,8 +336,7 @@ struct BwdLds {
   static constexpr size_t KP = DW + (size_t)CH * LDO * OPB;           // OP    [CH][LDO]  K+
   static constexpr size_t BETA = KP + (size_t)CH * LDO * OPB;         // float [CH]
   static constexpr size_t RED = BETA + CH * 4;                        // float [512]  scan / column-sum partials
-  static constexpr size_t GAMP = RED + 512 * 4;                       // float [512]  dGamma_C partials
-  static constexpr size_t DGAM = GAMP + 512 * 4;                      // float [DK]
+  static constexpr size_t DGAM = RED + 512 * 4;                       // float [DK]  dGamma_C
   static constexpr size_t BV = DGAM + DK * 4;                         // float [2][CH] rowsum(V * T^T dU) halves
   static constexpr size_t DBP = BV + 2 * CH * 4;                      // float [2][CH] dbeta halves
   static constexpr size_t NRM = DBP + 2 * CH * 4;                     // float [2][CH] 1/|q_r|, 1/|k_r| (qk_norm)
@@ -345,21 +344,19 @@ struct BwdLds {
   static constexpr size_t END0 = NDOT + 4 * CH * 4;
   static constexpr size_t Y = DW;                                     // OP [CH][LDT]
   static_assert(LDT <= LDO, "Y fits in the dW region");
-  // gated products, per pass of 32 channels: decayed q and k tables (split SE,
-  // [channel][token]) and the decayed-k table for the row side (float,
-  // [channel][token]).  They reuse the dW and K+ regions (dead by then) where
-  // those are large enough (dk = 128), else they follow the rest.
+  // gated products, per pass of 32 channels: fp32 tables [channel][token] of
+  // q_r e^{g_r - g_m(R)}, k_r e^{g_r - g_m(R)} (row side) and k_i e^{g_m(C) - g_i}
+  // (column side), R, C the tokens' 8-token groups.  They reuse the dW and K+ regions
+  // (dead by then) where those are large enough (dk = 128), else they follow the rest.
   static constexpr int TC = 32;
-  static constexpr size_t TQSZ = (size_t)TC * LDQ * sizeof(SE);
-  static constexpr size_t TAB_SZ = 2 * (SSPLIT ? 2 : 1) * TQSZ + (size_t)TC * LDR * 4;
+  static constexpr size_t TAB1 = (size_t)TC * LDR * 4;
+  static constexpr size_t TAB_SZ = 3 * TAB1;
   static constexpr bool TAB_REUSE = TAB_SZ <= 2 * (size_t)CH * LDO * OPB;
-  static constexpr size_t QCH = TAB_REUSE ? DW : END0;
-  static constexpr size_t QCL = QCH + TQSZ;                             // lo halves: split types only
-  static constexpr size_t KCH = QCH + (SSPLIT ? 2 : 1) * TQSZ;
-  static constexpr size_t KCL = KCH + TQSZ;
-  static constexpr size_t KR = KCH + (SSPLIT ? 2 : 1) * TQSZ;
+  static constexpr size_t TQ = TAB_REUSE ? DW : END0;
+  static constexpr size_t TK = TQ + TAB1;
+  static constexpr size_t KR = TK + TAB1;
   static constexpr size_t BYTES = TAB_REUSE ? END0 : END0 + TAB_SZ;
-  static_assert(KR % 16 == 0 && KCH % 16 == 0 && QCH % 16 == 0, "table rows stay 16-byte aligned");
+  static_assert(KR % 16 == 0 && TK % 16 == 0 && TQ % 16 == 0, "table rows stay 16-byte aligned");
   static_assert(BYTES <= 163840, "backward chunk kernel LDS");
   static_assert(A_END % 16 == 0 && B_END % 16 == 0, "LDS regions stay 16-byte aligned");
 };
@@ -408,10 +405,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   float* sA2 = reinterpret_cast<float*>(smem + L::A2);   // dT
   SE* sA2h = reinterpret_cast<SE*>(smem + L::A2);   // dG, split (after dT is dead)
   SE* sA2l = sA2h + CH * L::LDQ;
-  SE* tQh = reinterpret_cast<SE*>(smem + L::QCH);
-  SE* tQl = reinterpret_cast<SE*>(smem + L::QCL);
-  SE* tKh = reinterpret_cast<SE*>(smem + L::KCH);
-  SE* tKl = reinterpret_cast<SE*>(smem + L::KCL);
+  float* tQ = reinterpret_cast<float*>(smem + L::TQ);
+  float* tK = reinterpret_cast<float*>(smem + L::TK);
   float* tKR = reinterpret_cast<float*>(smem + L::KR);
   // x as a split pair hi + lo (hi only on the fp32 path)
   auto put_split = [&](SE* hi, SE* lo, int idx, float x) __attribute__((always_inline)) {
@@ -428,7 +423,6 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   OP* sKp = reinterpret_cast<OP*>(smem + L::KP);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sRed = reinterpret_cast<float*>(smem + L::RED);
-  float* sGamP = reinterpret_cast<float*>(smem + L::GAMP);
   float* sDGam = reinterpret_cast<float*>(smem + L::DGAM);
   float* sBv = reinterpret_cast<float*>(smem + L::BV);
   float* sDbp = reinterpret_cast<float*>(smem + L::DBP);
@@ -451,7 +445,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const E* vh = reinterpret_cast<const E*>(a.v) + (size_t)ci.t0 * rv + (size_t)h * DV;
   const E* doh = reinterpret_cast<const E*>(a.dout) + (size_t)ci.t0 * rv + (size_t)h * DV;
   const E* bh = reinterpret_cast<const E*>(a.beta) + (size_t)ci.t0 * H + h;
-  const OP* gS = reinterpret_cast<const OP*>(a.wsS) + blk * WB::S;
+  const float* gS = a.wsS + blk * WB::S;
   const float* gdS = a.wsdS + blk * WB::DS;
   const float* gU = a.wsU + blk * WB::U;
   const float* gdU = a.wsdU + blk * WB::DU;
@@ -467,8 +461,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 
   // ---- phase A staging: contractions over the value dimension, a quarter of the columns at a time
   struct QStage {
-    TileCopy<OP, DK, QC, NT> s;
-    TileCopy<float, DK, QC, NT> ds;
+    TileCopy<float, DK, QC, NT> s, ds;   // the same shape and type: a thread holds the same elements of both
     TileCopy<float, CH, QC, NT> u, du;
     TileCopy<E, CH, QC, NT> dov, vv;
   };
@@ -508,12 +501,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
   for (int i = 0; i < NKH; ++i) accQ[i] = accK[i] = accW[i] = zero4();
   float bv[4] = {0.f, 0.f, 0.f, 0.f};
-  float gp = 0.f;
+  constexpr int GPER = TileCopy<float, DK, QC, NT>::PER;
+  float gp[GPER];   // partial dGamma_C of the rows this thread holds in the quarter tiles
+#pragma unroll
+  for (int i = 0; i < GPER; ++i) gp[i] = 0.f;
 
   for (int qq = 0; qq < NQ; ++qq) {
     const int cq = qq * QC;
     __syncthreads();  // the previous quarter's LDS reads are done
-    qs.s.store(sS, L::LSV);
+    qs.s.template store_cvt<OP>(sS, L::LSV, DK);
     qs.ds.template store_split<OP>(sDSh, sDSl, L::LSV);
     qs.u.template store_split<OP>(sUh, sUl, L::LSV);
     qs.du.template store_split<OP>(sDUh, sDUl, L::LSV);
@@ -533,36 +529,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     });
     qs.dov.template store_cvt<OP>(sDO, L::LSV, len);
     qs.vv.template store_cvt<OP>(sV, L::LSV, len);
+    // dGamma_C = value sums of dS' * S, in fp32 from the registers the quarter was loaded
+    // into (before the next quarter's loads reuse them): a thread holds the same 4-column pieces of S and dS'
+    static_for<0, decltype(qs.s)::PER>([&](auto I) __attribute__((always_inline)) {
+      const float* x = reinterpret_cast<const float*>(&qs.s.r[I]);
+      const float* y = reinterpret_cast<const float*>(&qs.ds.r[I]);
+      gp[I] += (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
+    });
     if (qq + 1 < NQ) qload(qq + 1);
     __syncthreads();
-    // value sums of dS' * S for channel c (NT / DK parts of the quarter's columns; 16-byte
-    // rows where a part spans whole fragments)
-    {
-      constexpr int NPART = NT / DK, CPP = QC / NPART;
-      const int c = tid % DK, p = tid / DK;
-      if constexpr (CPP % 8 == 0) {
-#pragma unroll
-        for (int col = p * CPP; col < (p + 1) * CPP; col += 8) {
-          const Frag<OP> s8 = frag_row<OP>(sS, L::LSV, c, col);
-          const Frag<OP> h8 = frag_row<OP>(sDSh, L::LSV, c, col);
-          if constexpr (L::SPLIT) {
-            const Frag<OP> l8 = frag_row<OP>(sDSl, L::LSV, c, col);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) gp += (f32(h8.v[u]) + f32(l8.v[u])) * f32(s8.v[u]);
-          } else {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) gp += f32(h8.v[u]) * f32(s8.v[u]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int col = p * CPP; col < (p + 1) * CPP; ++col) {
-          const int o = c * L::LSV + col;
-          const float ds = L::SPLIT ? f32(sDSh[o]) + f32(sDSl[o]) : f32(sDSh[o]);
-          gp += ds * f32(sS[o]);
-        }
-      }
-    }
     const Frag<OP> fdo = frag_row<OP>(sDO, L::LSV, 16 * tw + r16, kq);
     const SFrag<OP> fdu = sfrag_pair<OP>(sDUh, sDUl, L::LSV, 16 * tw + r16, kq);
     const SFrag<OP> fu = sfrag_pair<OP>(sUh, sUl, L::LSV, 16 * tw + r16, kq);
@@ -619,7 +594,17 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     for (int jj = 0; jj < NKH; ++jj) sDW[rr * L::LDO + 16 * (hf * NKH + jj) + r16] = cvt<OP>(-accW[jj][ii]);
     if (r16 == 0) sBv[hf * CH + rr] = bv[ii];
   }
-  sGamP[tid] = gp;
+  {
+    // a row's QC / 4 column pieces sit in consecutive lanes
+    constexpr int VPR = QC / 4;
+    static_for<0, GPER>([&](auto I) __attribute__((always_inline)) {
+      float p = gp[I];
+#pragma unroll
+      for (int m = 1; m < VPR; m <<= 1) p += __shfl_xor(p, m);
+      const int v = tid + I * NT;
+      if (v % VPR == 0 && v < DK * VPR) sDGam[v / VPR] = p;
+    });
+  }
   float gGram[2][4];   // this wave's tiles of the un-beta strict Gram (for dbeta)
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj)
@@ -641,16 +626,10 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   pk.template store_cvt<E>(sK, L::LDK, len);
   pq.template store_cvt<E>(sQ, L::LDK, len);
   if (a.gate_ls)   // raw gate x -> log alpha = logsigmoid(x)
-    pl.template store_map<float>(sG, L::LDG, len, [](float x) { return logsigmoid(x); });
+    pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(logsigmoid(x)); });
   else
-    pl.template store_cvt<float>(sG, L::LDG, len);
+    pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(x); });
   __syncthreads();
-  if (tid < DK) {
-    float s = 0.f;
-#pragma unroll
-    for (int p = 0; p < NT / DK; ++p) s += sGamP[p * DK + tid];
-    sDGam[tid] = s;
-  }
   // cumulative sum of log_alpha over the chunk (per channel, NT / DK row parts)
   constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
   {
@@ -746,14 +725,21 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   __syncthreads();
 
   // ---- per channel tile of half hf: gated products, then the assembly of dq, dk, dg.
-  // Decayed products use per-block reference rows m(b) = 16b + 8 (split bf16 operands):
-  // row side, block a = tw: dq_g = e^{g_r - g_m(a)} (dAqk . R_a), dkp_g = e^{g_r - g_m(a)} (dG . R_a),
-  // R_a[i] = k_i e^{g_m(a) - g_i}; column side, block b = tw:
-  // dkm = e^{g_m(b) - g_i} sum_{a >= b} e^{g_m(a) - g_m(b)} (dAqk_a^T q~_a + dG_a^T k~_a),
-  // q~_r = q_r e^{g_r - g_m(blk r)}, k~ likewise.  One pass per channel tile: the pass's
-  // 32 channels (tile jj of both halves) get tables of q~, k~ (split, [channel][token]) and
-  // k_i e^{g_m(blk i) - g_i} (fp32), so every operand is a 16-byte LDS row read and the
-  // exponentials are taken once per element and pass.
+  // Every decayed product e^{g_r - g_i} (i <= r) goes through reference rows in the
+  // middle of 8-token groups (group_ref), split bf16 operands, with ch(R, C) =
+  // e^{g_m(R) - g_m(C)} <= 1 the chain factor of groups C < R (1 for C = R, 0 above):
+  // row side, tile a = tw:
+  //   dq_g[r] = e^{g_r - g_m(R)} sum_i dAqk[r][i] k_i e^{g_m(C) - g_i} ch(R, C),  dkp_g likewise with dG;
+  // column side, tile b = tw:
+  //   dkm[i] = e^{g_m(C) - g_i} sum_r (dAqk[r][i] q_r + dG[r][i] k_r) e^{g_r - g_m(R)} ch(R, C).
+  // The chain factor depends on the channel, so it goes into the channel-side operand:
+  // each tile is two products, one per 8-token group of its output rows, accumulated
+  // into one tile with the other group's rows of the token-side operand zeroed.  A
+  // chain factor below CHAIN_MIN makes the wave form those channel-side values as one
+  // exponential each instead.  One pass per channel tile: the pass's 32 channels (tile
+  // jj of both halves) get tables [channel][token] of the outer factors times q or k,
+  // so the usual operand is a 16-byte LDS row read and each exponential is taken once
+  // per element.
   O* dqo = reinterpret_cast<O*>(a.dq) + (size_t)ci.t0 * rk + (size_t)h * DK;
   O* dko = reinterpret_cast<O*>(a.dk_) + (size_t)ci.t0 * rk + (size_t)h * DK;
   O* dlo = reinterpret_cast<O*>(a.dla) + (size_t)ci.t0 * rk + (size_t)h * DK;
@@ -764,6 +750,21 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   float* wDK = qk_norm ? wDQ + CH * DK : nullptr;
   constexpr int TC = L::TC;
   static_assert(TC == 2 * 16 && NT == TC * (CH / 4), "table build: one thread per (channel, 4 tokens)");
+  // chain factor of groups (R, C) for channel c: at most 1, zero above the diagonal
+  auto chain = [&](int R, int C, int c) __attribute__((always_inline)) {
+    const float e = __expf(sG[group_ref(R) * L::LDG + c] - sG[group_ref(C) * L::LDG + c]);
+    return C < R ? e : (C == R ? 1.f : 0.f);
+  };
+  // 8 table values [channel cl][token t0 ..] times f
+  auto scaled = [&](const float* tab, int cl, int t0, float f, float (&x)[8]) __attribute__((always_inline)) {
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(tab + cl * L::LDR + t0);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(tab + cl * L::LDR + t0 + 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = v0[u] * f;
+      x[u + 4] = v1[u] * f;
+    }
+  };
   // (dk = 128 keeps the pass loop rolled: unrolled, it no longer fits the registers)
 #pragma unroll(DK == 128 ? 1 : NKH)
   for (int jj = 0; jj < NKH; ++jj) {
@@ -771,75 +772,84 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     {
       const int cl = tid % TC, r0 = 4 * (tid / TC);
       const int c = 16 * ((cl >> 4) * NKH + jj) + (cl & 15);   // channel tile jj of half cl >> 4
-      const float gm = sG[(16 * (r0 >> 4) + 8) * L::LDG + c];
-      float kr[4];
+      const float gm = sG[group_ref(r0 >> 3) * L::LDG + c];
+      float eq[4], ek[4], kr[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = r0 + u;
         const float g = sG[r * L::LDG + c];
         const float e = __expf(g - gm);
         const float kv = kn(r, c);
-        put_split(tQh, tQl, cl * L::LDQ + r, qn(r, c) * e);
-        put_split(tKh, tKl, cl * L::LDQ + r, kv * e);
+        eq[u] = qn(r, c) * e;
+        ek[u] = kv * e;
         kr[u] = kv * __expf(gm - g);
       }
+      *reinterpret_cast<f32x4*>(tQ + cl * L::LDR + r0) = f32x4{eq[0], eq[1], eq[2], eq[3]};
+      *reinterpret_cast<f32x4*>(tK + cl * L::LDR + r0) = f32x4{ek[0], ek[1], ek[2], ek[3]};
       *reinterpret_cast<f32x4*>(tKR + cl * L::LDR + r0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
     }
     __syncthreads();
     const int cl = 16 * hf + r16, cc = 16 * (hf * NKH + jj) + r16;
+    const int hh = q4 >> 1;   // group 2 tw + hh holds this lane's output rows 16 tw + 4 q4 + ii
     f32x4 dqg = zero4(), dkpg = zero4(), dkm = zero4();
     {
       const int ab = tw, kmax = 16 * (ab + 1);   // columns i < kmax can be nonzero
-      const float gma = sG[(16 * ab + 8) * L::LDG + cc];
       for (int k = 0; k < kmax; k += 32) {
-        const SFrag<SE> fa1 = sfrag_pair<SE>(sA1h, sA1l, L::LDQ, 16 * ab + r16, k + kq);
-        const SFrag<SE> fa2 = sfrag_pair<SE>(sA2h, sA2l, L::LDQ, 16 * ab + r16, k + kq);
-        const int i0 = k + kq, bb = i0 >> 4;
-        float xr[8];
-        if (i0 < kmax) {
-          const float f = bb == ab ? 1.f : __expf(gma - sG[(16 * bb + 8) * L::LDG + cc]);
-          const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + cl * L::LDR + i0);
-          const f32x4 v1 = *reinterpret_cast<const f32x4*>(tKR + cl * L::LDR + i0 + 4);
+        const int i0 = k + kq, C = i0 >> 3;   // this lane's 8 columns form group C
+#pragma unroll 1
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int R = 2 * ab + g2;
+          const float f = chain(R, C, cc);   // zero past the diagonal block
+          float xr[8];
+          scaled(tKR, cl, i0, f, xr);
+          if (__any(C < R && f < CHAIN_MIN) && C < R) {   // k_i e^{g_m(R) - g_i}, one exponential each
+            const float gmr = sG[group_ref(R) * L::LDG + cc];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            xr[u] = v0[u] * f;
-            xr[u + 4] = v1[u] * f;
+            for (int u = 0; u < 8; ++u) xr[u] = kn(i0 + u, cc) * __expf(gmr - sG[(i0 + u) * L::LDG + cc]);
           }
-        } else {
-#pragma unroll
-          for (int u = 0; u < 8; ++u) xr[u] = 0.f;
+          const SFrag<SE> fr = sfrag_from<SE>(xr);
+          const bool mine = (r16 >> 3) == g2;   // this lane supplies row r16 of the tile
+          dqg = mma_ss(sfrag_keep(sfrag_pair<SE>(sA1h, sA1l, L::LDQ, 16 * ab + r16, k + kq), mine), fr, dqg);
+          dkpg = mma_ss(sfrag_keep(sfrag_pair<SE>(sA2h, sA2l, L::LDQ, 16 * ab + r16, k + kq), mine), fr, dkpg);
         }
-        const SFrag<SE> fr = sfrag_from<SE>(xr);
-        dqg = mma_ss(fa1, fr, dqg);
-        dkpg = mma_ss(fa2, fr, dkpg);
       }
+      const float gmr = sG[group_ref(2 * ab + hh) * L::LDG + cc];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gma);
+        const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gmr);
         dqg[ii] *= e;
         dkpg[ii] *= e;
       }
     }
     {
       const int b = tw;
-      const float gmb = sG[(16 * b + 8) * L::LDG + cc];
       // A[m = i][k = r'] : r' < 16 -> dAqk[16a + r'][i], r' >= 16 -> dG[16a + r' - 16][i];
-      // B[k = r'][n] : q~ rows of block a for r' < 16, k~ rows for r' >= 16
-      const SE* aH = q4 < 2 ? sA1h : sA2h;
-      const SE* aL = q4 < 2 ? sA1l : sA2l;
-      const SE* bH = q4 < 2 ? tQh : tKh;
-      const SE* bL = q4 < 2 ? tQl : tKl;
+      // B[k = r'][n] : decayed q rows of block a for r' < 16, decayed k rows for r' >= 16
+      const bool useq = q4 < 2;
+      const SE* aH = useq ? sA1h : sA2h;
+      const SE* aL = useq ? sA1l : sA2l;
+      const float* bT = useq ? tQ : tK;
       for (int ab = b; ab < 4; ++ab) {
-        const int rbase = 16 * ab + 8 * (q4 & 1);
-        const SFrag<SE> fa = sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase);
-        const SFrag<SE> fb = sfrag_pair<SE>(bH, bL, L::LDQ, cl, rbase);
-        const f32x4 y = mma_ss(fa, fb, zero4());
-        const float f = ab == b ? 1.f : __expf(sG[(16 * ab + 8) * L::LDG + cc] - gmb);
+        const int rbase = 16 * ab + 8 * (q4 & 1), R = rbase >> 3;   // this lane's 8 rows form group R
+#pragma unroll 1
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int C = 2 * b + g2;
+          const float f = chain(R, C, cc);   // zero for rows above the output group
+          float xb[8];
+          scaled(bT, cl, rbase, f, xb);
+          if (__any(C < R && f < CHAIN_MIN) && C < R) {   // w_r e^{g_r - g_m(C)}, one exponential each
+            const float gmc = sG[group_ref(C) * L::LDG + cc];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) dkm[ii] += f * y[ii];
+            for (int u = 0; u < 8; ++u)
+              xb[u] = (useq ? qn(rbase + u, cc) : kn(rbase + u, cc)) * __expf(sG[(rbase + u) * L::LDG + cc] - gmc);
+          }
+          dkm = mma_ss(sfrag_keep(sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase), (r16 >> 3) == g2),
+                       sfrag_from<SE>(xb), dkm);
+        }
       }
+      const float gmc = sG[group_ref(2 * b + hh) * L::LDG + cc];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) dkm[ii] *= __expf(gmb - sG[(16 * b + 4 * q4 + ii) * L::LDG + cc]);
+      for (int ii = 0; ii < 4; ++ii) dkm[ii] *= __expf(gmc - sG[(16 * b + 4 * q4 + ii) * L::LDG + cc]);
     }
     // assembly (rows 16tw + 4q4 + ii)
     {
@@ -935,7 +945,12 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
     for (int rr = (s + 1) * RPS - 1; rr >= s * RPS; --rr) {
       acc += sG[rr * L::LDG + c];
-      if (rr < len) dlo[(size_t)rr * rk + c] = cvt<O>(a.gate_ls ? acc * sigmoid_neg(f32(lh[(size_t)rr * rk + c])) : acc);
+      if (rr < len) {
+        // through the gate's map and the floor of log alpha (flat below it)
+        const float x = f32(lh[(size_t)rr * rk + c]);
+        const float d = a.gate_ls ? acc * sigmoid_neg(x) : acc;
+        dlo[(size_t)rr * rk + c] = cvt<O>(above_floor(a.gate_ls ? logsigmoid(x) : x) ? d : 0.f);
+      }
     }
   }
   if constexpr (qk_norm) {

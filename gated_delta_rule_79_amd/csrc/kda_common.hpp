@@ -167,6 +167,16 @@ template <typename E> __device__ __forceinline__ SFrag<E> sfrag_col_f32(const fl
   for (int j = 0; j < 8; ++j) x[j] = p[(k0 + j) * ld + col];
   return sfrag_from<E>(x);
 }
+// The fragment, or zeros when !keep (per lane: masks the operand rows a lane supplies).
+template <typename E> __device__ __forceinline__ SFrag<E> sfrag_keep(const SFrag<E>& s, bool keep) {
+  SFrag<E> z;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    z.hi.v[j] = keep ? s.hi.v[j] : (E)0.f;
+    if constexpr (sizeof(E) == 2) z.lo.v[j] = keep ? s.lo.v[j] : (E)0.f;
+  }
+  return z;
+}
 template <typename E> __device__ __forceinline__ f32x4 mma_ss(const SFrag<E>& a, const SFrag<E>& b, f32x4 c) {
   if constexpr (sizeof(E) == 2) {
     c = mma(a.lo, b.hi, c);
@@ -353,6 +363,42 @@ __device__ __forceinline__ void copy_out(E* __restrict__ dst, size_t dst_ld, con
 }
 
 // ---------------------------------------------------------------------------
+// channel-wise decay inside a chunk
+// ---------------------------------------------------------------------------
+// log alpha is read as max(log alpha, -LOG_ALPHA_FLOOR): a token that would keep
+// less than e^-16 (about 1.1e-7, fp32 resolution) of a state row keeps e^-16 of
+// it.  The comparison is written so that a NaN passes through.  The floor bounds
+// every decay factor the chunked kernels form (see group_ref), so none of them
+// can overflow whatever the gates; its derivative is 0 below the floor.
+constexpr float LOG_ALPHA_FLOOR = 16.f;
+constexpr float ALPHA_FLOOR = 1.12535175e-7f;   // e^-16
+__device__ __forceinline__ float floor_log_alpha(float x) { return x < -LOG_ALPHA_FLOOR ? -LOG_ALPHA_FLOOR : x; }
+__device__ __forceinline__ bool above_floor(float x) { return !(x < -LOG_ALPHA_FLOOR); }
+
+// Decayed products e^{g_r - g_i} (g = in-chunk cumulative log decay, i <= r) are
+// factored through reference rows in the middle of 8-token groups, m(R) = 8R + 4:
+//   e^{g_r - g_i} = e^{g_r - g_m(R)} * e^{g_m(R) - g_m(C)} * e^{g_m(C) - g_i}
+// with R, C the groups of r and i.  The outer factors span at most 4 and 3 tokens
+// (at most e^{4 LOG_ALPHA_FLOOR}), the chain factor is at most 1 for C <= R.
+constexpr int NGROUP = CH / 8;
+constexpr int NGROUP_PAIRS = NGROUP * (NGROUP - 1) / 2;   // pairs C < R
+__host__ __device__ constexpr int group_ref(int R) { return 8 * R + 4; }
+__host__ __device__ constexpr int pair_index(int R, int C) { return R * (R - 1) / 2 + C; }   // C < R
+__device__ __forceinline__ int pair_r(int pi) {
+  int R = 1;
+  while ((R + 1) * R / 2 <= pi) ++R;
+  return R;
+}
+__device__ __forceinline__ int pair_c(int pi) { const int R = pair_r(pi); return pi - R * (R - 1) / 2; }
+// The outer factors can exceed 1 (the row factor up to e^{4 LOG_ALPHA_FLOOR}, the column
+// factor up to e^{3 LOG_ALPHA_FLOOR}), so a chain factor below fp32's normal range can
+// belong to a product that is not small.  Column operands whose chain factor falls
+// below CHAIN_MIN are therefore formed as one exponential of the summed exponent,
+// k_i e^{g_m(R) - g_i} <= 1, which leaves at most one factor above 1 in any product:
+// whatever then falls out of fp32 range was below e^-23 of the result.
+constexpr float CHAIN_MIN = 1.8e-35f;   // e^-80
+
+// ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
 // Fused input preparation (kda.h: KDA_FLAG_QK_L2NORM, KDA_FLAG_GATE_LOGSIGMOID).
@@ -424,7 +470,7 @@ struct WsBlock {
   static constexpr size_t G = (size_t)CH * CH;     // un-beta strict Gram [CH][CH]   float
   static constexpr size_t KHF = (size_t)CH * DK;   // Kh  [CH][DK]   float-sized slot: fp32 Kh, or (split
                                                    // types) fp16 hi [CH][DK] followed by fp16 lo [CH][DK]
-  static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk [DK][DV]   OP
+  static constexpr size_t S = (size_t)DK * DV;     // state entering a chunk [DK][DV]   float
   static constexpr size_t U = (size_t)DV * CH;     // U [CH][DV]   float
   static constexpr size_t DS = (size_t)DK * DV;    // dS' [DK][DV]   float
   static constexpr size_t DU = (size_t)DV * CH;    // dU [CH][DV]  float

@@ -101,7 +101,8 @@ __global__ __launch_bounds__(DEC_NT) void kda_decode_step(const DecodeArgs a) {
     sQ[t][c] = f32(q[g]);
     sK[t][c] = f32(k[g]);
     const float x = f32(la[g]);
-    sA[t][c] = a.gate_ls ? 1.f / (1.f + __expf(-x)) : __expf(x);   // alpha = sigmoid(x) for a raw gate
+    const float al = a.gate_ls ? 1.f / (1.f + __expf(-x)) : __expf(x);   // alpha = sigmoid(x) for a raw gate
+    sA[t][c] = al < ALPHA_FLOOR ? ALPHA_FLOOR : al;   // the floor of log alpha the chunked kernels apply
   }
   for (int o = tid; o < T * DV; o += DEC_NT) {
     const int t = o / DV, j = o % DV;

@@ -221,11 +221,11 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
         xk[ks][u] *= nk;
       }
   }
-  if (a.gate_ls && rv_ok) {   // rows past the chunk stay 0 (no decay)
+  if (rv_ok) {   // rows past the chunk stay 0 (no decay)
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) xl[ks][u] = logsigmoid(xl[ks][u]);
+      for (int u = 0; u < 8; ++u) xl[ks][u] = floor_log_alpha(a.gate_ls ? logsigmoid(xl[ks][u]) : xl[ks][u]);
   }
   const float bet = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
   if (tid < CH) sBeta[tid] = bet;
@@ -302,11 +302,15 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
     }
   }
 
-  // ---- 3. decayed Gram blocks: wave w owns row block a = w.  The gated
-  // factors can exceed fp16 range, so they are split bf16 (fp32 inputs: fp32).
+  // ---- 3. decayed Gram blocks: wave w owns row block a = w.  Reference rows in the
+  // middle of 8-token groups (group_ref): the lane's row r in group R carries
+  // e^{g_r - g_m(R)}; the column operand of row group R (h = 0, 1 of the block)
+  // carries e^{g_m(R) - g_i} for columns in groups up to R and zero beyond, so each
+  // block is two products, one per row group.  The gated factors can exceed fp16
+  // range, so they are split bf16 (fp32 inputs: fp32).
   {
     const int ab = w;
-    const int ref = 16 * ab + 8;
+    const int ref = group_ref(r >> 3);
     using SE = typename std::conditional<sizeof(E) == 4, float, bf16>::type;
     SFrag<SE> fk[NKS], fq[NKS];
 #pragma unroll
@@ -323,25 +327,32 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
       fq[ks] = sfrag_from<SE>(yq);
     }
     for (int b = 0; b <= ab; ++b) {
-      f32x4 akk = zero4(), aqk = zero4();
-      const int i = 16 * b + r16;
+      f32x4 akk[2] = {zero4(), zero4()}, aqk[2] = {zero4(), zero4()};
+      const int i = 16 * b + r16, C = i >> 3;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int c0 = 32 * ks + 8 * q4;
-        float xr[8];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int R = 2 * ab + hh, mr = group_ref(R);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          xr[u] = f32(sK[i * L::LDK + c0 + u]) * __expf(sG[ref * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
-        const SFrag<SE> fr = sfrag_from<SE>(xr);
-        akk = mma_ss(fk[ks], fr, akk);
-        aqk = mma_ss(fq[ks], fr, aqk);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int c0 = 32 * ks + 8 * q4;
+          float xr[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float x = f32(sK[i * L::LDK + c0 + u]) * __expf(sG[mr * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
+            xr[u] = C <= R ? x : 0.f;
+          }
+          const SFrag<SE> fr = sfrag_from<SE>(xr);
+          akk[hh] = mma_ss(fk[ks], fr, akk[hh]);
+          aqk[hh] = mma_ss(fq[ks], fr, aqk[hh]);
+        }
       }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int rr = 16 * ab + 4 * q4 + ii, cc = 16 * b + r16;
-        sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[ii] : 0.f;
-        wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[ii] : 0.f);
-        if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[ii] : 0.f;
+        const float vk = (q4 >> 1) ? akk[1][ii] : akk[0][ii], vq = (q4 >> 1) ? aqk[1][ii] : aqk[0][ii];
+        sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * vk : 0.f;
+        wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? vq : 0.f);
+        if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? vk : 0.f;
       }
     }
     for (int b = ab + 1; b < 4; ++b) {
@@ -475,8 +486,8 @@ struct Prep8Lds {
   static constexpr size_t GQH = GKL + (size_t)CH * LDQ * 2;
   static constexpr size_t GQL = GQH + (size_t)CH * LDQ * 2;
   static constexpr size_t GKR = GQL + (size_t)CH * LDQ * 2;
-  static constexpr size_t GF = GKR + (size_t)CH * LDR * 4;   // float [6][GC]  e^{g_m(a) - g_m(b)}, b < a
-  static constexpr size_t BYTES = GF + 6 * GC * 4;
+  static constexpr size_t GF = GKR + (size_t)CH * LDR * 4;   // float [28][GC] e^{g_m(R) - g_m(C)}, C < R
+  static constexpr size_t BYTES = GF + NGROUP_PAIRS * GC * 4;
   static_assert(BYTES <= 163840, "prep LDS");
   static_assert(GKH % 16 == 0 && GKR % 16 == 0 && GF % 16 == 0, "16-byte rows");
 };
@@ -572,9 +583,9 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
     pk.template store_cvt<E>(sK, L::LDK, len);
     pq.template store_cvt<E>(sQ, L::LDK, len);
     if constexpr (GATE)   // raw gate x -> log alpha = logsigmoid(x)
-      pl.template store_map<float>(sG, L::LDG, len, [](float x) { return logsigmoid(x); });
+      pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(logsigmoid(x)); });
     else
-      pl.template store_cvt<float>(sG, L::LDG, len);
+      pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(x); });
     {
       // V^T: each 16-byte piece is 8 value columns of one token
       constexpr int VPR = DV / 8;
@@ -659,12 +670,16 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       if (tid < DK) wGam[tid] = __expf(sG[(CH - 1) * L::LDG + tid]);
     }
 
-    // ---- decayed Gram blocks (split bf16 operands; reference row m(b) = 16b + 8).
-    // Block (a, b), b <= a, of K+ K-^T is sum_c k~_r[c] (k_i[c] e^{g_m(b) - g_i}) e^{g_m(a) - g_m(b)}
-    // with k~_r = k_r e^{g_r - g_m(a)}; every factor stays within an 8-token decay.  The
-    // channels go in passes of GC: each pass tabulates k~ and q~ (split), k e^{g_m - g} and
-    // the block-to-block factors once, and every wave reads its operands as 16-byte rows.
-    // The ten blocks are dealt to the waves so each SIMD (waves w and w + 4) gets two or three.
+    // ---- decayed Gram blocks (split bf16 operands; reference rows in the middle of
+    // 8-token groups, m(R) = 8R + 4).  For row r in group R and column i in group C <= R,
+    //   e^{g_r - g_i} = e^{g_r - g_m(R)} e^{g_m(R) - g_m(C)} e^{g_m(C) - g_i},
+    // the outer two factors tabulated per (token, channel), the middle one per (R, C) pair.
+    // With log alpha >= -LOG_ALPHA_FLOOR no factor exceeds e^{4 LOG_ALPHA_FLOOR}: the row
+    // and column factors span at most 4 and 3 tokens and the chain factor is at most 1.
+    // A 16x16 tile (a, b) is computed once per row group R in {2a, 2a+1} with the chain
+    // folded into the column operand (zero for C > R, where the pairs lie above the
+    // diagonal); each lane keeps the rows of its own group.  The channels go in passes of
+    // GC; the 20 tile halves are dealt to the waves so each SIMD gets five.
     {
       constexpr int GC = L::GC, NPASS = DK / GC;
       bf16* tKh = reinterpret_cast<bf16*>(smem + L::GKH);
@@ -673,23 +688,24 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       bf16* tQl = reinterpret_cast<bf16*>(smem + L::GQL);
       float* tKR = reinterpret_cast<float*>(smem + L::GKR);
       float* tF = reinterpret_cast<float*>(smem + L::GF);
-      // this wave's blocks: list index w and w + 8 of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-      constexpr int BA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-      constexpr int BB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-      const int nblk = w < 2 ? 2 : 1;
-      f32x4 akk[2] = {zero4(), zero4()}, aqk[2] = {zero4(), zero4()};
+      // tile halves (a, b, h): list index w, w + 8, w + 16 for wave w
+      constexpr int HA[20] = {0, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3, 3, 3, 3, 3, 0, 1, 2, 3};
+      constexpr int HB[20] = {0, 0, 1, 0, 0, 1, 2, 0, 1, 0, 1, 2, 3, 0, 1, 2, 0, 1, 2, 3};
+      constexpr int HH[20] = {1, 0, 1, 1, 0, 0, 1, 1, 1, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0};
+      const int nitem = w < 4 ? 3 : 2;
+      f32x4 akk[3] = {zero4(), zero4(), zero4()}, aqk[3] = {zero4(), zero4(), zero4()};
       static_assert(NT == CH * (GC / 4), "table build: one thread per (token, 4 channels)");
       for (int ps = 0; ps < NPASS; ++ps) {
         if (ps > 0) __syncthreads();   // the previous pass's table reads are done
         {
           const int r = tid / (GC / 4), cl0 = 4 * (tid % (GC / 4)), c0 = GC * ps + cl0;
-          const int mref = 16 * (r >> 4) + 8;
+          const int mref = group_ref(r >> 3);
           float ek[4], eq[4], kr[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const float g = sG[r * L::LDG + c0 + u], gm = sG[mref * L::LDG + c0 + u];
-            const float e = __expf(g - gm);
             const float kv = f32(sK[r * L::LDK + c0 + u]) * nk(r);
+            const float e = __expf(g - gm);
             ek[u] = kv * e;
             eq[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * e;
             kr[u] = kv * __expf(gm - g);
@@ -697,36 +713,45 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
           store4_split<bf16>(tKh + r * L::LDQ + cl0, tKl + r * L::LDQ + cl0, ek[0], ek[1], ek[2], ek[3]);
           store4_split<bf16>(tQh + r * L::LDQ + cl0, tQl + r * L::LDQ + cl0, eq[0], eq[1], eq[2], eq[3]);
           *reinterpret_cast<f32x4*>(tKR + r * L::LDR + cl0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
-          if (tid < 6 * GC) {   // pair (a, b), b < a, in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-            const int pi = tid / GC, c = GC * ps + tid % GC;
-            const int pa = pi < 1 ? 1 : (pi < 3 ? 2 : 3), pb = pi < 1 ? 0 : (pi < 3 ? pi - 1 : pi - 3);
-            tF[tid] = __expf(sG[(16 * pa + 8) * L::LDG + c] - sG[(16 * pb + 8) * L::LDG + c]);
+          for (int e = tid; e < NGROUP_PAIRS * GC; e += NT) {   // chain factors of the group pairs C < R
+            const int pi = e / GC, c = GC * ps + e % GC;
+            tF[e] = __expf(sG[group_ref(pair_r(pi)) * L::LDG + c] - sG[group_ref(pair_c(pi)) * L::LDG + c]);
           }
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (j < nblk) {
-            const int li = w + 8 * j, ba = BA[li], bb = BB[li];
+        for (int j = 0; j < 3; ++j) {
+          if (j < nitem) {
+            const int li = w + 8 * j, ba = HA[li], bb = HB[li], R = 2 * ba + HH[li];
+            const int C = 2 * bb + (r16 >> 3);   // group of this lane's column
             const SFrag<bf16> fk = sfrag_pair<bf16>(tKh, tKl, L::LDQ, 16 * ba + r16, 8 * q4);
             const SFrag<bf16> fq = sfrag_pair<bf16>(tQh, tQl, L::LDQ, 16 * ba + r16, 8 * q4);
             const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4);
             const f32x4 v1 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4 + 4);
             float xr[8];
-            if (bb == ba) {
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                xr[u] = v0[u];
-                xr[u + 4] = v1[u];
-              }
-            } else {
-              const float* f = tF + GC * (ba * (ba - 1) / 2 + bb) + 8 * q4;
+            bool tiny = false;
+            if (C < R) {
+              const float* f = tF + GC * pair_index(R, C) + 8 * q4;
               const f32x4 f0 = *reinterpret_cast<const f32x4*>(f), f1 = *reinterpret_cast<const f32x4*>(f + 4);
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
                 xr[u] = v0[u] * f0[u];
                 xr[u + 4] = v1[u] * f1[u];
+                tiny |= f0[u] < CHAIN_MIN || f1[u] < CHAIN_MIN;
               }
+            } else {
+              const bool on = C == R;   // C > R: pairs above the diagonal (zero, and kept finite)
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                xr[u] = on ? v0[u] : 0.f;
+                xr[u + 4] = on ? v1[u] : 0.f;
+              }
+            }
+            if (__any(tiny) && C < R) {   // one exponential per element (see CHAIN_MIN)
+              const int i = 16 * bb + r16, c0 = GC * ps + 8 * q4, mr = group_ref(R);
+#pragma unroll
+              for (int u = 0; u < 8; ++u)
+                xr[u] = f32(sK[i * L::LDK + c0 + u]) * nk(i) * __expf(sG[mr * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
             }
             const SFrag<bf16> fr = sfrag_from<bf16>(xr);
             akk[j] = mma_ss(fk, fr, akk[j]);
@@ -735,15 +760,17 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (j < nblk) {
-          const int li = w + 8 * j, ba = BA[li], bb = BB[li];
+      for (int j = 0; j < 3; ++j) {
+        if (j < nitem) {
+          const int li = w + 8 * j, ba = HA[li], bb = HB[li], hh = HH[li];
+          if ((q4 >> 1) == hh) {   // this lane's rows 4q4 .. 4q4 + 3 of the tile are in row group 2a + hh
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
-            sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[j][ii] : 0.f;
-            wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[j][ii] : 0.f);
-            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[j][ii] : 0.f;
+            for (int ii = 0; ii < 4; ++ii) {
+              const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
+              sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[j][ii] : 0.f;
+              wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[j][ii] : 0.f);
+              if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[j][ii] : 0.f;
+            }
           }
         }
       }
@@ -935,7 +962,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   const OP* gKhT = reinterpret_cast<const OP*>(a.wsKhT);
   const UTT* gUt = UF ? reinterpret_cast<const UTT*>(a.wsUtF) : reinterpret_cast<const UTT*>(a.wsUt);
   const float* gGam = a.wsGam;
-  OP* gS = reinterpret_cast<OP*>(a.wsS);
+  float* gS = reinterpret_cast<float*>(a.wsS);
   float* gU = a.wsU;
   O* gOut = reinterpret_cast<O*>(a.out);
   const float scale = a.scale;
@@ -1006,10 +1033,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       if (t < NST) {
         store4<OP>(sST + (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4, S[i][0], S[i][1], S[i][2], S[i][3]);
         if constexpr (SAVE) {
-          // backward needs the state entering every chunk: OP [DK][DV] per chunk-head
-          OP* dst = gS + blk_of(n) * WB::S + (size_t)(16 * mt + 4 * q4) * DV + n0 + 16 * nt + r16;
+          // backward needs the state entering every chunk: fp32 [DK][DV] per chunk-head
+          float* dst = gS + blk_of(n) * WB::S + (size_t)(16 * mt + 4 * q4) * DV + n0 + 16 * nt + r16;
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = cvt<OP>(S[i][ii]);
+          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = S[i][ii];
         }
       }
     }

@@ -35,7 +35,7 @@ struct Args {
   float* wsUtF;             // U~^T in fp32 [DV][CH] (the backward's state pass reads it)
   float* wsG;               // un-beta strict Gram K+ K-^T
   float* wsKhF;             // Kh token-major: fp32, or a split pair of fp16 arrays (bf16 inputs)
-  void* wsS;                // state entering each chunk, OP [DK][DV]
+  float* wsS;               // state entering each chunk, fp32 [DK][DV]
   float* wsU;               // U, fp32 [CH][DV]
   float* wsdS;              // gradient of the state leaving each chunk, fp32 [DK][DV]
   float* wsdU;              // dU, fp32 [CH][DV]

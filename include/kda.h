@@ -45,10 +45,19 @@
  *
  * Errors: arguments are validated on the host before anything is enqueued; on
  * an error nothing is launched.  Launch failures return KDA_ERROR_LAUNCH.
+ * Sizes: B*T < 2^31 tokens, H <= 65535, (T/64 + N)*H < 2^31 chunk slots (B*ceil(T/64)*H
+ * without cu_seqlens) and N*H < 2^22, with N the number of sequences; larger
+ * problems return KDA_ERROR_INVALID_VALUE (kda_workspace_bytes returns 0).
  * The contents of cu_seqlens are a precondition (checked with a synchronous
- * copy only when the environment variable KDA_DEBUG=1).  log_alpha must be
- * finite and <= 0; full accuracy is kept while the total log-decay of any
- * channel over 8 consecutive tokens stays above -80.
+ * copy only when the environment variable KDA_DEBUG=1).
+ *
+ * Decay: log_alpha must be <= 0 (-inf allowed: alpha = 0).  Every kernel reads
+ * it as max(log_alpha, -16): a token that would keep less than e^-16 (about
+ * 1.1e-7, fp32 resolution) of a state row keeps e^-16 of it, and dlog_alpha is
+ * 0 for such tokens (the derivative of that floor).  The floor bounds every
+ * decay factor the chunked kernels form, so no gate can make them overflow or
+ * produce NaN; results move by far less than the error bounds.  A NaN in any
+ * input of one (sequence, head) reaches no other (sequence, head).
  */
 #ifndef KDA_H_
 #define KDA_H_

@@ -28,7 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kda_bwd", "kda_decode", "kda_fwd", "kda_last_error", "kda_status_string",
+    assert declared_functions() == sorted(["kda_bwd", "kda_decode", "kda_fwd", "kda_last_error",
+                                          "kda_status_string",
                                           "kda_timing_enable", "kda_timing_read", "kda_workspace_bytes",
                                           "kda_conv_workspace_bytes", "kda_conv_fwd", "kda_conv_bwd",
                                           "kda_conv_decode"])
@@ -92,6 +93,18 @@ def test_rejects_unsupported(lib, kw):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(T=-1), dict(H=0), dict(B=70000, T=40000)])
 def test_rejects_bad_shapes(lib, kw):
     assert _fwd(lib, _desc(**kw)) == S_INVALID
+
+
+def test_rejects_sizes_whose_grids_overflow(lib):
+    """Chunk slots x heads and sequences x heads are bounded on the host (they size int launch grids)."""
+    big = _desc(T=1 << 20, H=64, num_seqs=(1 << 31) - 1)
+    assert _fwd(lib, big, cu=A) == S_INVALID
+    assert _bwd(lib, big, cu=A) == S_INVALID
+    # the varlen reading of the descriptor is rejected; the size is the one without cu_seqlens
+    assert lib.kda_workspace_bytes(ctypes.byref(big), 1) == lib.kda_workspace_bytes(
+        ctypes.byref(_desc(T=1 << 20, H=64, num_seqs=0)), 1)
+    assert _fwd(lib, _desc(T=1 << 21, H=65535, num_seqs=1), cu=A) == S_INVALID   # (T/64 + 1) x H >= 2^31
+    assert _fwd(lib, _desc(T=1 << 16, H=1024, num_seqs=1 << 12), cu=A) == S_INVALID   # N x H >= 2^22
 
 
 def test_rejects_varlen_misuse(lib):
