@@ -33,8 +33,8 @@ struct Plan {
   int N = 0;
   int max_chunks = 0;
   size_t esz = 0;
-  size_t chunks = 0, sc0 = 0, so = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0;
-  size_t T = 0, UtF = 0, G = 0, KhF = 0, S = 0, U = 0, dS = 0, dU = 0, DQK = 0;
+  size_t chunks = 0, sc0 = 0, so = 0, W = 0, KhT = 0, Qt = 0, Ut = 0, Aqk = 0, Gam = 0, steep = 0;
+  size_t T = 0, UtF = 0, G = 0, KhF = 0, KhTL = 0, S = 0, U = 0, dS = 0, dU = 0, DQK = 0, GS = 0;
   int segs = 1;
   size_t vsc0 = 0, vord = 0, seg_in = 0, seg_loc = 0, seg_m = 0;
   size_t total = 0;
@@ -87,16 +87,19 @@ Plan make_plan(const kda_desc* d, bool bwd, int N, int max_chunks) {
   p.Ut = take(nb * dv * CH * e);
   p.Aqk = take(nb * CH * CH * e);
   p.Gam = take(nb * dk * 4);
+  p.steep = take(nb * 4);
   if (bwd) {
     p.T = take(nb * CH * CH * e);   // operand type
     p.UtF = take(nb * dv * CH * 4);
     p.G = take(nb * CH * CH * 4);
     p.KhF = take(nb * CH * dk * 4);
+    if (e == 2) p.KhTL = take(nb * dk * CH * e);   // Kh^T lo half (split training-mode state update)
     p.S = take(nb * dk * dv * 4);
     p.U = take(nb * dv * CH * 4);
     p.dS = take(nb * dk * dv * 4);
     p.dU = take(nb * dv * CH * 4);
     if (d->flags & KDA_FLAG_QK_L2NORM) p.DQK = take(nb * 2 * CH * dk * 4);   // dq^, dk^ before the norm's chain rule
+    p.GS = take((2 + kda::GS_PARTS) * 4);   // gradient scale (s, 1/s) and the pre-pass's partial maxima
   }
   // segment scan buffers (the same stretches for a training-mode forward and the
   // backward, which reuses the forward's transfers)
@@ -142,16 +145,22 @@ void fill_ws(Args& a, const Plan& p, void* ws) {
   a.wsUt = b + p.Ut;
   a.wsAqk = b + p.Aqk;
   a.wsGam = reinterpret_cast<float*>(b + p.Gam);
+  a.steep = reinterpret_cast<int32_t*>(b + p.steep);
   auto fptr = [&](size_t off) { return off ? reinterpret_cast<float*>(b + off) : nullptr; };
   a.wsT = p.T ? b + p.T : nullptr;
   a.wsUtF = fptr(p.UtF);
   a.wsG = fptr(p.G);
   a.wsKhF = fptr(p.KhF);
+  a.wsKhTL = p.KhTL ? b + p.KhTL : nullptr;
   a.wsS = fptr(p.S);
   a.wsU = fptr(p.U);
   a.wsdS = fptr(p.dS);
   a.wsdU = fptr(p.dU);
   a.wsDQK = fptr(p.DQK);
+  if (p.GS && p.esz == 2) {   // the fp32 backward narrows nothing: no scale
+    a.gscale = fptr(p.GS);
+    a.gs_part = a.gscale + 2;
+  }
   a.segs = p.segs;
   a.vsc0 = p.vsc0 ? reinterpret_cast<int32_t*>(b + p.vsc0) : nullptr;
   a.vord = p.vord ? reinterpret_cast<int32_t*>(b + p.vord) : nullptr;

@@ -30,6 +30,72 @@ template <typename E, int DK, int DV>
 hipError_t launch_bwd_front(const Args& a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// scale of the upstream gradients (bf16 inputs)
+// ---------------------------------------------------------------------------
+// The bf16 backward narrows dO, dS' and dU to fp16 (hi, lo) pairs, whose range
+// (normal from 6.1e-5 up to 65504) is far narrower than bf16's.  The backward is
+// linear in (dO, dS_final), so the kernels run on s dO and s dS_final, with s the
+// power of two that puts the largest magnitude of both in [0.5, 1), and multiply
+// every gradient they store by 1/s; both scalings are exact.  s = 1 when the
+// maximum is 0, inf or NaN (the non-finite values then reach the gradients as
+// they would without the scale).
+__global__ __launch_bounds__(256) void kda_grad_absmax(const bf16* __restrict__ dout, size_t n_out,
+                                                       const float* __restrict__ dfin, size_t n_fin,
+                                                       float* __restrict__ part) {
+  __shared__ float red[8];
+  const size_t stride = (size_t)gridDim.x * 256, i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  float m = 0.f;   // fmaxf drops NaN operands
+  for (size_t v = i0; v < n_out / 8; v += stride) {
+    const u32x4 x = reinterpret_cast<const u32x4*>(dout)[v];
+    const bf16* e = reinterpret_cast<const bf16*>(&x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f32(e[i])));
+  }
+  for (size_t v = i0; v < n_fin / 4; v += stride) {
+    const f32x4 x = reinterpret_cast<const f32x4*>(dfin)[v];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(x[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane_id() == 0) red[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void kda_grad_scale(const float* __restrict__ part, int n, float* __restrict__ gs) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, part[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane_id() == 0) red[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float s = 1.f;
+    if (m > 0.f && m <= 3.4e38f) {
+      int e;
+      (void)frexpf(m, &e);            // m = f 2^e, f in [0.5, 1)
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+      s = ldexpf(1.f, -e);
+    }
+    gs[0] = s;
+    gs[1] = 1.f / s;
+  }
+}
+
+static hipError_t launch_grad_scale(const Args& a, hipStream_t st) {
+  const size_t n_out = (size_t)a.B * a.T * a.H * a.dv;
+  const size_t n_fin = a.dfinal ? (size_t)a.N * a.H * a.dk * a.dv : 0;
+  KDA_TIMED("kda_grad_absmax", st,
+            hipLaunchKernelGGL(kda_grad_absmax, dim3(GS_PARTS), dim3(256), 0, st,
+                               reinterpret_cast<const bf16*>(a.dout), n_out, a.dfinal, n_fin, a.gs_part));
+  KDA_TIMED("kda_grad_scale", st, hipLaunchKernelGGL(kda_grad_scale, dim3(1), dim3(256), 0, st, a.gs_part, GS_PARTS, a.gscale));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // reverse sequential pass
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV, int DVS>
@@ -105,6 +171,11 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   float* gDInit = a.dinit;
   const float scale = a.scale;
   const size_t ro = (size_t)H * DV;
+  // gradient scale: dO and the caller's dS_final are read times s; d_init_state is
+  // stored times 1/s (a stretch's gradient for the segment scan stays scaled)
+  const float gs = a.gscale ? a.gscale[0] : 1.f;
+  const float gs_fin = a.dfinal_scaled ? 1.f : gs;
+  const float gs_inv = (a.gscale && !LOCAL) ? a.gscale[1] : 1.f;
 
   f32x4 dS[SPW];
   const size_t st_off = ((size_t)seq * H + h) * DK * DV;
@@ -114,7 +185,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int ch = 16 * mt + 4 * q4 + ii, col = n0 + 16 * nt + r16;
-      dS[i][ii] = (gDFin && t < NST) ? gDFin[st_off + (size_t)ch * DV + col] : 0.f;
+      dS[i][ii] = (gDFin && t < NST) ? gs_fin * gDFin[st_off + (size_t)ch * DV + col] : 0.f;
     }
   }
 
@@ -161,7 +232,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
       const bool ok = row < p.dolen;
       const E* e = reinterpret_cast<const E*>(&p.dov);
 #pragma unroll
-      for (int i = 0; i < EPV; ++i) sDOT[(cv * EPV + i) * L::LDT + row] = cvt<OP>(ok ? f32(e[i]) : 0.f);
+      for (int i = 0; i < EPV; ++i) sDOT[(cv * EPV + i) * L::LDT + row] = cvt<OP>(ok ? gs * f32(e[i]) : 0.f);
     }
   };
 
@@ -262,7 +333,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int ch = 16 * mt + 4 * q4 + ii, col = n0 + 16 * nt + r16;
-          gDInit[st_off + (size_t)ch * DV + col] = dS[i][ii];
+          gDInit[st_off + (size_t)ch * DV + col] = gs_inv * dS[i][ii];
         }
       }
     }
@@ -297,17 +368,15 @@ struct BwdLds {
   // phase A: quarters with the value column contiguous, so every MFMA operand
   // (contraction over the value dimension) is one 16-byte row read
   static constexpr int LSV = QC + PO;   // OP [DK][LSV] S, dS';  [CH][LSV] U, dU, dO, V
-  static constexpr int LST = CH + PO;   // OP [QC][LST] dU^T (token contiguous, for T^T dU)
-  static constexpr size_t A_S = 0;
-  static constexpr size_t A_DSH = A_S + (size_t)DK * LSV * OPB;
+  static constexpr size_t A_SH = 0;
+  static constexpr size_t A_SL = A_SH + (size_t)DK * LSV * OPB;
+  static constexpr size_t A_DSH = A_SL + (SPLIT ? (size_t)DK * LSV * OPB : 0);
   static constexpr size_t A_DSL = A_DSH + (size_t)DK * LSV * OPB;
   static constexpr size_t A_UH = A_DSL + (SPLIT ? (size_t)DK * LSV * OPB : 0);
   static constexpr size_t A_UL = A_UH + (size_t)CH * LSV * OPB;
   static constexpr size_t A_DUH = A_UL + (SPLIT ? (size_t)CH * LSV * OPB : 0);
   static constexpr size_t A_DUL = A_DUH + (size_t)CH * LSV * OPB;
-  static constexpr size_t A_DUTH = A_DUL + (SPLIT ? (size_t)CH * LSV * OPB : 0);
-  static constexpr size_t A_DUTL = A_DUTH + (size_t)QC * LST * OPB;
-  static constexpr size_t A_DO = A_DUTL + (SPLIT ? (size_t)QC * LST * OPB : 0);
+  static constexpr size_t A_DO = A_DUL + (SPLIT ? (size_t)CH * LSV * OPB : 0);
   static constexpr size_t A_V = A_DO + (size_t)CH * LSV * OPB;
   static constexpr size_t A_END = A_V + (size_t)CH * LSV * OPB;
   // phase B (shares the first region with phase A)
@@ -336,14 +405,16 @@ struct BwdLds {
   static constexpr size_t KP = DW + (size_t)CH * LDO * OPB;           // OP    [CH][LDO]  K+
   static constexpr size_t BETA = KP + (size_t)CH * LDO * OPB;         // float [CH]
   static constexpr size_t RED = BETA + CH * 4;                        // float [512]  scan / column-sum partials
-  static constexpr size_t DGAM = RED + 512 * 4;                       // float [DK]  dGamma_C
+  static constexpr size_t DGAM = RED + 512 * (sizeof(E) == 4 ? 8 : 4);   // float [DK]  dGamma_C (fp32 inputs:
+                                                                          // RED holds the scan's fp64 part sums)
   static constexpr size_t BV = DGAM + DK * 4;                         // float [2][CH] rowsum(V * T^T dU) halves
   static constexpr size_t DBP = BV + 2 * CH * 4;                      // float [2][CH] dbeta halves
   static constexpr size_t NRM = DBP + 2 * CH * 4;                     // float [2][CH] 1/|q_r|, 1/|k_r| (qk_norm)
   static constexpr size_t NDOT = NRM + 2 * CH * 4;                    // float [2][2][CH] q^.dq^, k^.dk^ halves
   static constexpr size_t END0 = NDOT + 4 * CH * 4;
-  static constexpr size_t Y = DW;                                     // OP [CH][LDT]
-  static_assert(LDT <= LDO, "Y fits in the dW region");
+  static constexpr size_t Y = DW;                                     // OP hi, lo [CH][LDT] (dW, K+ dead by then)
+  static constexpr size_t YL = Y + (size_t)CH * LDT * OPB;
+  static_assert(2 * (size_t)CH * LDT <= 2 * (size_t)CH * LDO, "split Y fits in the dW and K+ regions");
   // gated products, per pass of 32 channels: fp32 tables [channel][token] of
   // q_r e^{g_r - g_m(R)}, k_r e^{g_r - g_m(R)} (row side) and k_i e^{g_m(C) - g_i}
   // (column side), R, C the tokens' 8-token groups.  They reuse the dW and K+ regions
@@ -358,12 +429,16 @@ struct BwdLds {
   static constexpr size_t BYTES = TAB_REUSE ? END0 : END0 + TAB_SZ;
   static_assert(KR % 16 == 0 && TK % 16 == 0 && TQ % 16 == 0, "table rows stay 16-byte aligned");
   static_assert(BYTES <= 163840, "backward chunk kernel LDS");
+  static_assert(RED % 8 == 0, "fp64 scan partials stay 8-byte aligned");
   static_assert(A_END % 16 == 0 && B_END % 16 == 0, "LDS regions stay 16-byte aligned");
 };
 
 // QKN: q and k rows are L2-normalised on load and dq, dk go through the norm's
-// chain rule at the end (KDA_FLAG_QK_L2NORM).
-template <typename E, typename O, int DK, int DV, bool QKN>
+// chain rule at the end (KDA_FLAG_QK_L2NORM).  PATH 0 takes the chunk-heads the prep
+// left unflagged in a.steep, PATH 1 the flagged ones (decayed products through
+// 8-token groups); two instantiations keep the usual path's registers free of the
+// other one's.
+template <typename E, typename O, int DK, int DV, bool QKN, int PATH>
 __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   using L = BwdLds<E, DK, DV>;
   using OP = typename L::OP;
@@ -373,6 +448,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const int j = blockIdx.x, h = blockIdx.y, H = a.H;
   const ChunkInfo ci = a.chunks[j];
   if (ci.len <= 0) return;
+  if ((a.steep[(size_t)j * H + h] != 0) != (PATH == 1)) return;
   const int len = ci.len;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
   // token tile tw and column half hf of this wave.  Waves w and w + 4 share a
@@ -384,15 +460,14 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const size_t rk = (size_t)H * DK, rv = (size_t)H * DV;
   const float scale = a.scale;
 
-  OP* sS = reinterpret_cast<OP*>(smem + L::A_S);
+  OP* sSh = reinterpret_cast<OP*>(smem + L::A_SH);
+  OP* sSl = reinterpret_cast<OP*>(smem + L::A_SL);
   OP* sDSh = reinterpret_cast<OP*>(smem + L::A_DSH);
   OP* sDSl = reinterpret_cast<OP*>(smem + L::A_DSL);
   OP* sUh = reinterpret_cast<OP*>(smem + L::A_UH);
   OP* sUl = reinterpret_cast<OP*>(smem + L::A_UL);
   OP* sDUh = reinterpret_cast<OP*>(smem + L::A_DUH);
   OP* sDUl = reinterpret_cast<OP*>(smem + L::A_DUL);
-  OP* sDUTh = reinterpret_cast<OP*>(smem + L::A_DUTH);
-  OP* sDUTl = reinterpret_cast<OP*>(smem + L::A_DUTL);
   OP* sDO = reinterpret_cast<OP*>(smem + L::A_DO);
   OP* sV = reinterpret_cast<OP*>(smem + L::A_V);
   float* sG = reinterpret_cast<float*>(smem + L::G);
@@ -420,6 +495,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   };
   OP* sDW = reinterpret_cast<OP*>(smem + L::DW);
   OP* sY = reinterpret_cast<OP*>(smem + L::Y);
+  OP* sYl = reinterpret_cast<OP*>(smem + L::YL);
   OP* sKp = reinterpret_cast<OP*>(smem + L::KP);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sRed = reinterpret_cast<float*>(smem + L::RED);
@@ -452,6 +528,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const OP* gT = reinterpret_cast<const OP*>(a.wsT) + blk * WB::TT;
   const float* gGm = a.wsG + blk * WB::G;
   O* gdV = reinterpret_cast<O*>(a.dv_) + (size_t)ci.t0 * rv + (size_t)h * DV;
+  // gradient scale: dO is read times s, every gradient stored times 1/s
+  const float gs = a.gscale ? a.gscale[0] : 1.f;
+  const float gs_inv = a.gscale ? a.gscale[1] : 1.f;
 
   // phase B's inputs (q, k, log_alpha rows), loaded after phase A
   TileCopy<E, CH, DK, NT> pk, pq, pl;
@@ -509,25 +588,11 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   for (int qq = 0; qq < NQ; ++qq) {
     const int cq = qq * QC;
     __syncthreads();  // the previous quarter's LDS reads are done
-    qs.s.template store_cvt<OP>(sS, L::LSV, DK);
+    qs.s.template store_split<OP>(sSh, sSl, L::LSV);
     qs.ds.template store_split<OP>(sDSh, sDSl, L::LSV);
     qs.u.template store_split<OP>(sUh, sUl, L::LSV);
     qs.du.template store_split<OP>(sDUh, sDUl, L::LSV);
-    // dU^T copy (token contiguous) for T^T dU
-    static_for<0, decltype(qs.du)::PER>([&](auto I) __attribute__((always_inline)) {
-      const int v = tid + I * NT;
-      if (decltype(qs.du)::NV % NT == 0 || v < decltype(qs.du)::NV) {
-        const int row = v / (QC / 4), c0 = (v % (QC / 4)) * 4;
-        const float* x = reinterpret_cast<const float*>(&qs.du.r[I]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const OP hi = cvt<OP>(x[u]);
-          sDUTh[(c0 + u) * L::LST + row] = hi;
-          if constexpr (L::SPLIT) sDUTl[(c0 + u) * L::LST + row] = cvt<OP>(x[u] - f32(hi));
-        }
-      }
-    });
-    qs.dov.template store_cvt<OP>(sDO, L::LSV, len);
+    qs.dov.template store_map<OP>(sDO, L::LSV, len, [gs](float x) { return gs * x; });
     qs.vv.template store_cvt<OP>(sV, L::LSV, len);
     // dGamma_C = value sums of dS' * S, in fp32 from the registers the quarter was loaded
     // into (before the next quarter's loads reuse them): a thread holds the same 4-column pieces of S and dS'
@@ -550,9 +615,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
     for (int jj = 0; jj < NKH; ++jj) {
       const int nt = hf * NKH + jj;
-      const Frag<OP> fs = frag_row<OP>(sS, L::LSV, 16 * nt + r16, kq);
-      accQ[jj] = mma(fdo, fs, accQ[jj]);
-      accW[jj] = mma_sp(fdu, fs, accW[jj]);
+      const SFrag<OP> fs = sfrag_pair<OP>(sSh, sSl, L::LSV, 16 * nt + r16, kq);   // S split: it reaches dlog alpha
+      accQ[jj] = mma_ps(fdo, fs, accQ[jj]);
+      accW[jj] = mma_ss(fdu, fs, accW[jj]);
       accK[jj] = mma_ss(fu, sfrag_pair<OP>(sDSh, sDSl, L::LSV, 16 * nt + r16, kq), accK[jj]);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -562,7 +627,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
       for (int k = 0; k < CH; k += 32)
         x = mma_ps(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq),
-                   sfrag_pair<OP>(sDUTh, sDUTl, L::LST, 16 * hf + r16, k + kq), x);
+                   sfrag_col_pair<OP>(sDUh, sDUl, L::LSV, 16 * hf + r16, k + kq), x);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * tw + 4 * q4 + ii, col = 16 * hf + r16;
@@ -572,7 +637,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         p += __shfl_xor(p, 4);
         p += __shfl_xor(p, 8);
         bv[ii] += p;
-        if (r < len) gdV[(size_t)r * rv + cq + col] = cvt<O>(sBeta[r] * x[ii]);
+        if (r < len) gdV[(size_t)r * rv + cq + col] = cvt<O>(gs_inv * (sBeta[r] * x[ii]));
       }
     }
   }
@@ -630,25 +695,43 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   else
     pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(x); });
   __syncthreads();
-  // cumulative sum of log_alpha over the chunk (per channel, NT / DK row parts)
+  // cumulative sum of log_alpha over the chunk (per channel, NT / DK row parts); for
+  // fp32 inputs in fp64 with one rounding of each g to fp32, as in the forward's prep
   constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
-  {
+  if constexpr (sizeof(E) == 4) {
+    double* sTot = reinterpret_cast<double*>(sRed);
     const int c = tid % DK, s = tid / DK;
-    float acc = 0.f;
+    double tot = 0.0;
+#pragma unroll
+    for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) tot += (double)sG[rr * L::LDG + c];
+    sTot[s * DK + c] = tot;
+    __syncthreads();
+    double acc = 0.0;
+    for (int s2 = 0; s2 < s; ++s2) acc += sTot[s2 * DK + c];
 #pragma unroll
     for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
-      acc += sG[rr * L::LDG + c];
-      sG[rr * L::LDG + c] = acc;
+      acc += (double)sG[rr * L::LDG + c];
+      sG[rr * L::LDG + c] = (float)acc;
     }
-    sRed[s * DK + c] = acc;
-  }
-  __syncthreads();
-  {
-    const int c = tid % DK, s = tid / DK;
-    float off = 0.f;
-    for (int s2 = 0; s2 < s; ++s2) off += sRed[s2 * DK + c];
+  } else {
+    {
+      const int c = tid % DK, s = tid / DK;
+      float acc = 0.f;
 #pragma unroll
-    for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
+      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
+        acc += sG[rr * L::LDG + c];
+        sG[rr * L::LDG + c] = acc;
+      }
+      sRed[s * DK + c] = acc;
+    }
+    __syncthreads();
+    {
+      const int c = tid % DK, s = tid / DK;
+      float off = 0.f;
+      for (int s2 = 0; s2 < s; ++s2) off += sRed[s2 * DK + c];
+#pragma unroll
+      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
+    }
   }
   __syncthreads();
   for (int o = tid; o < CH * DK; o += NT) {
@@ -690,7 +773,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     }
   }
   __syncthreads();  // dT complete; dW and K+ are dead
-  // ---- Y = dT T^T -> sY
+  // ---- Y = dT T^T -> sY.  dT and Y are split operands: dA reaches dg through both
+  // sides of every gated product, and dlog alpha sums their nearly cancelling difference
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     const int nt = 2 * hf + jj;
@@ -700,10 +784,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       float y8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) y8[u] = sA2[(16 * tw + r16) * L::LDA + k + kq + u];
-      x = mma(frag_from<OP>(y8), frag_col<OP>(sTT, L::LDT, 16 * nt + r16, k + kq), x);
+      x = mma_sp(sfrag_from<OP>(y8), frag_col<OP>(sTT, L::LDT, 16 * nt + r16, k + kq), x);
     }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) sY[(16 * tw + 4 * q4 + ii) * L::LDT + 16 * nt + r16] = cvt<OP>(x[ii]);
+    for (int ii = 0; ii < 4; ++ii) {
+      const int o = (16 * tw + 4 * q4 + ii) * L::LDT + 16 * nt + r16;
+      const OP hi = cvt<OP>(x[ii]);
+      sY[o] = hi;
+      if constexpr (L::SPLIT) sYl[o] = cvt<OP>(x[ii] - f32(hi));
+    }
   }
   __syncthreads();
   // ---- dA = -strict(T^T Y); dG = beta dA -> sA2; dbeta += rowsum(dA * G)
@@ -713,7 +802,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     f32x4 x = zero4();
 #pragma unroll
     for (int k = 0; k < CH; k += 32)
-      x = mma(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq), frag_col<OP>(sY, L::LDT, 16 * nt + r16, k + kq), x);
+      x = mma_ps(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq), sfrag_col_pair<OP>(sY, sYl, L::LDT, 16 * nt + r16, k + kq), x);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;
@@ -725,8 +814,10 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   __syncthreads();
 
   // ---- per channel tile of half hf: gated products, then the assembly of dq, dk, dg.
-  // Every decayed product e^{g_r - g_i} (i <= r) goes through reference rows in the
-  // middle of 8-token groups (group_ref), split bf16 operands, with ch(R, C) =
+  // PATH 0 (no 8-token span decaying past e^-STEEP_SPAN, see steep_block) uses one
+  // reference row in the middle of each 16-row block and one product per step.
+  // PATH 1 puts every decayed product e^{g_r - g_i} (i <= r) through reference rows
+  // in the middle of 8-token groups (group_ref), split bf16 operands, with ch(R, C) =
   // e^{g_m(R) - g_m(C)} <= 1 the chain factor of groups C < R (1 for C = R, 0 above):
   // row side, tile a = tw:
   //   dq_g[r] = e^{g_r - g_m(R)} sum_i dAqk[r][i] k_i e^{g_m(C) - g_i} ch(R, C),  dkp_g likewise with dG;
@@ -772,7 +863,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     {
       const int cl = tid % TC, r0 = 4 * (tid / TC);
       const int c = 16 * ((cl >> 4) * NKH + jj) + (cl & 15);   // channel tile jj of half cl >> 4
-      const float gm = sG[group_ref(r0 >> 3) * L::LDG + c];
+      const float gm = sG[(PATH == 0 ? 16 * (r0 >> 4) + 8 : group_ref(r0 >> 3)) * L::LDG + c];
       float eq[4], ek[4], kr[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -792,64 +883,105 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     const int cl = 16 * hf + r16, cc = 16 * (hf * NKH + jj) + r16;
     const int hh = q4 >> 1;   // group 2 tw + hh holds this lane's output rows 16 tw + 4 q4 + ii
     f32x4 dqg = zero4(), dkpg = zero4(), dkm = zero4();
-    {
-      const int ab = tw, kmax = 16 * (ab + 1);   // columns i < kmax can be nonzero
-      for (int k = 0; k < kmax; k += 32) {
-        const int i0 = k + kq, C = i0 >> 3;   // this lane's 8 columns form group C
-#pragma unroll 1
-        for (int g2 = 0; g2 < 2; ++g2) {
-          const int R = 2 * ab + g2;
-          const float f = chain(R, C, cc);   // zero past the diagonal block
+    if constexpr (PATH == 0) {   // reference rows in the middle of 16-row blocks, one product per step
+      {
+        const int ab = tw, kmax = 16 * (ab + 1);   // columns i < kmax can be nonzero
+        const float gma = sG[(16 * ab + 8) * L::LDG + cc];
+        for (int k = 0; k < kmax; k += 32) {
+          const int i0 = k + kq, bb = i0 >> 4;
+          const float f = i0 >= kmax ? 0.f : (bb == ab ? 1.f : __expf(gma - sG[(16 * bb + 8) * L::LDG + cc]));
           float xr[8];
           scaled(tKR, cl, i0, f, xr);
-          if (__any(C < R && f < CHAIN_MIN) && C < R) {   // k_i e^{g_m(R) - g_i}, one exponential each
-            const float gmr = sG[group_ref(R) * L::LDG + cc];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) xr[u] = kn(i0 + u, cc) * __expf(gmr - sG[(i0 + u) * L::LDG + cc]);
-          }
           const SFrag<SE> fr = sfrag_from<SE>(xr);
-          const bool mine = (r16 >> 3) == g2;   // this lane supplies row r16 of the tile
-          dqg = mma_ss(sfrag_keep(sfrag_pair<SE>(sA1h, sA1l, L::LDQ, 16 * ab + r16, k + kq), mine), fr, dqg);
-          dkpg = mma_ss(sfrag_keep(sfrag_pair<SE>(sA2h, sA2l, L::LDQ, 16 * ab + r16, k + kq), mine), fr, dkpg);
+          dqg = mma_ss(sfrag_pair<SE>(sA1h, sA1l, L::LDQ, 16 * ab + r16, k + kq), fr, dqg);
+          dkpg = mma_ss(sfrag_pair<SE>(sA2h, sA2l, L::LDQ, 16 * ab + r16, k + kq), fr, dkpg);
+        }
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gma);
+          dqg[ii] *= e;
+          dkpg[ii] *= e;
         }
       }
-      const float gmr = sG[group_ref(2 * ab + hh) * L::LDG + cc];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gmr);
-        dqg[ii] *= e;
-        dkpg[ii] *= e;
-      }
-    }
-    {
-      const int b = tw;
-      // A[m = i][k = r'] : r' < 16 -> dAqk[16a + r'][i], r' >= 16 -> dG[16a + r' - 16][i];
-      // B[k = r'][n] : decayed q rows of block a for r' < 16, decayed k rows for r' >= 16
-      const bool useq = q4 < 2;
-      const SE* aH = useq ? sA1h : sA2h;
-      const SE* aL = useq ? sA1l : sA2l;
-      const float* bT = useq ? tQ : tK;
-      for (int ab = b; ab < 4; ++ab) {
-        const int rbase = 16 * ab + 8 * (q4 & 1), R = rbase >> 3;   // this lane's 8 rows form group R
-#pragma unroll 1
-        for (int g2 = 0; g2 < 2; ++g2) {
-          const int C = 2 * b + g2;
-          const float f = chain(R, C, cc);   // zero for rows above the output group
+      {
+        const int b = tw;
+        const float gmb = sG[(16 * b + 8) * L::LDG + cc];
+        const bool useq = q4 < 2;
+        const SE* aH = useq ? sA1h : sA2h;
+        const SE* aL = useq ? sA1l : sA2l;
+        const float* bT = useq ? tQ : tK;
+        for (int ab = b; ab < 4; ++ab) {
+          const int rbase = 16 * ab + 8 * (q4 & 1);
           float xb[8];
-          scaled(bT, cl, rbase, f, xb);
-          if (__any(C < R && f < CHAIN_MIN) && C < R) {   // w_r e^{g_r - g_m(C)}, one exponential each
-            const float gmc = sG[group_ref(C) * L::LDG + cc];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-              xb[u] = (useq ? qn(rbase + u, cc) : kn(rbase + u, cc)) * __expf(sG[(rbase + u) * L::LDG + cc] - gmc);
+          scaled(bT, cl, rbase, 1.f, xb);
+          const f32x4 y = mma_ss(sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase), sfrag_from<SE>(xb), zero4());
+          const float f = ab == b ? 1.f : __expf(sG[(16 * ab + 8) * L::LDG + cc] - gmb);
+  #pragma unroll
+          for (int ii = 0; ii < 4; ++ii) dkm[ii] += f * y[ii];
+        }
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) dkm[ii] *= __expf(gmb - sG[(16 * b + 4 * q4 + ii) * L::LDG + cc]);
+      }
+    } else {
+      {
+        const int ab = tw, kmax = 16 * (ab + 1);   // columns i < kmax can be nonzero
+        for (int k = 0; k < kmax; k += 32) {
+          const int i0 = k + kq, C = i0 >> 3;   // this lane's 8 columns form group C
+  #pragma unroll 1
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int R = 2 * ab + g2;
+            const float f = chain(R, C, cc);   // zero past the diagonal block
+            float xr[8];
+            scaled(tKR, cl, i0, f, xr);
+            if (__any(C < R && f < CHAIN_MIN) && C < R) {   // k_i e^{g_m(R) - g_i}, one exponential each
+              const float gmr = sG[group_ref(R) * L::LDG + cc];
+  #pragma unroll
+              for (int u = 0; u < 8; ++u) xr[u] = kn(i0 + u, cc) * __expf(gmr - sG[(i0 + u) * L::LDG + cc]);
+            }
+            const SFrag<SE> fr = sfrag_from<SE>(xr);
+            const bool mine = (r16 >> 3) == g2;   // this lane supplies row r16 of the tile
+            dqg = mma_ss(sfrag_keep(sfrag_pair<SE>(sA1h, sA1l, L::LDQ, 16 * ab + r16, k + kq), mine), fr, dqg);
+            dkpg = mma_ss(sfrag_keep(sfrag_pair<SE>(sA2h, sA2l, L::LDQ, 16 * ab + r16, k + kq), mine), fr, dkpg);
           }
-          dkm = mma_ss(sfrag_keep(sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase), (r16 >> 3) == g2),
-                       sfrag_from<SE>(xb), dkm);
+        }
+        const float gmr = sG[group_ref(2 * ab + hh) * L::LDG + cc];
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float e = __expf(sG[(16 * ab + 4 * q4 + ii) * L::LDG + cc] - gmr);
+          dqg[ii] *= e;
+          dkpg[ii] *= e;
         }
       }
-      const float gmc = sG[group_ref(2 * b + hh) * L::LDG + cc];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) dkm[ii] *= __expf(gmc - sG[(16 * b + 4 * q4 + ii) * L::LDG + cc]);
+      {
+        const int b = tw;
+        // A[m = i][k = r'] : r' < 16 -> dAqk[16a + r'][i], r' >= 16 -> dG[16a + r' - 16][i];
+        // B[k = r'][n] : decayed q rows of block a for r' < 16, decayed k rows for r' >= 16
+        const bool useq = q4 < 2;
+        const SE* aH = useq ? sA1h : sA2h;
+        const SE* aL = useq ? sA1l : sA2l;
+        const float* bT = useq ? tQ : tK;
+        for (int ab = b; ab < 4; ++ab) {
+          const int rbase = 16 * ab + 8 * (q4 & 1), R = rbase >> 3;   // this lane's 8 rows form group R
+  #pragma unroll 1
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int C = 2 * b + g2;
+            const float f = chain(R, C, cc);   // zero for rows above the output group
+            float xb[8];
+            scaled(bT, cl, rbase, f, xb);
+            if (__any(C < R && f < CHAIN_MIN) && C < R) {   // w_r e^{g_r - g_m(C)}, one exponential each
+              const float gmc = sG[group_ref(C) * L::LDG + cc];
+  #pragma unroll
+              for (int u = 0; u < 8; ++u)
+                xb[u] = (useq ? qn(rbase + u, cc) : kn(rbase + u, cc)) * __expf(sG[(rbase + u) * L::LDG + cc] - gmc);
+            }
+            dkm = mma_ss(sfrag_keep(sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase), (r16 >> 3) == g2),
+                         sfrag_from<SE>(xb), dkm);
+          }
+        }
+        const float gmc = sG[group_ref(2 * b + hh) * L::LDG + cc];
+  #pragma unroll
+        for (int ii = 0; ii < 4; ++ii) dkm[ii] *= __expf(gmc - sG[(16 * b + 4 * q4 + ii) * L::LDG + cc]);
+      }
     }
     // assembly (rows 16tw + 4q4 + ii)
     {
@@ -874,8 +1006,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
           qdot[ii] += qv * dq;
           kdot[ii] += kv * dkt;
         } else if (rr < len) {
-          dqo[(size_t)rr * rk + cc] = cvt<O>(dq);
-          dko[(size_t)rr * rk + cc] = cvt<O>(dkt);
+          dqo[(size_t)rr * rk + cc] = cvt<O>(gs_inv * dq);
+          dko[(size_t)rr * rk + cc] = cvt<O>(gs_inv * dkt);
         }
       }
     }
@@ -921,7 +1053,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     const int rr = tid;
     if (rr < len)
       reinterpret_cast<O*>(a.dbeta)[((size_t)ci.t0 + rr) * H + h] =
-          cvt<O>((sDbp[rr] + sDbp[CH + rr]) + (sBv[rr] + sBv[CH + rr]));
+          cvt<O>(gs_inv * ((sDbp[rr] + sDbp[CH + rr]) + (sBv[rr] + sBv[CH + rr])));
   } else if (tid >= 64 && tid < 64 + DK) {
     // dg_C: the last row collects sum_r dKh * Kh and dGamma_C * Gamma_C
     const int c = tid - 64;
@@ -948,7 +1080,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       if (rr < len) {
         // through the gate's map and the floor of log alpha (flat below it)
         const float x = f32(lh[(size_t)rr * rk + c]);
-        const float d = a.gate_ls ? acc * sigmoid_neg(x) : acc;
+        const float d = gs_inv * (a.gate_ls ? acc * sigmoid_neg(x) : acc);
         dlo[(size_t)rr * rk + c] = cvt<O>(above_floor(a.gate_ls ? logsigmoid(x) : x) ? d : 0.f);
       }
     }
@@ -967,7 +1099,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       O* dst = (which ? dko : dqo) + (size_t)rr * rk + c0;
       float y[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] = sc * (g[u] - f32(xh[rr * L::LDK + c0 + u]) * sc * dot);
+      for (int u = 0; u < 4; ++u) y[u] = gs_inv * (sc * (g[u] - f32(xh[rr * L::LDK + c0 + u]) * sc * dot));
       store4<O>(dst, y[0], y[1], y[2], y[3]);
     }
   }
@@ -1016,6 +1148,7 @@ static hipError_t launch_segmented_rev(const Args& a, hipStream_t st) {
   if ((e = launch_segment_rscan<DK, DV>(a, st)) != hipSuccess) return e;   // seg_in, d_init_state
   Args af = av;
   af.dfinal = a.seg_in;
+  af.dfinal_scaled = 1;
   af.dinit = nullptr;
   return launch_rev_auto<E, DK, DV>(af, st);
 }
@@ -1029,15 +1162,26 @@ hipError_t launch_bwd(const Args& a, hipStream_t st, bool saved) {
     e = launch_bwd_front<E, DK, DV>(a, st);
     if (e != hipSuccess) return e;
   }
+  if (a.gscale && (e = launch_grad_scale(a, st)) != hipSuccess) return e;
   e = a.segs > 1 ? launch_segmented_rev<E, DK, DV>(a, st) : launch_rev_auto<E, DK, DV>(a, st);
   if (e != hipSuccess) return e;
   if (a.max_chunks > 0) {
+    // bf16: the usual chunk-heads, then the ones the prep flagged as steep; the fp32
+    // prep flags every chunk-head
+#define KDA_BWDC(QKN)                                                                                      \
+  do {                                                                                                     \
+    if constexpr (sizeof(E) == 2)                                                                          \
+      KDA_TIMED("kda_bwd_chunk", st, hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV, QKN, 0>),             \
+                                                        dim3(a.max_chunks, a.H), dim3(512), 0, st, a));    \
+    KDA_TIMED(sizeof(E) == 2 ? "kda_bwd_chunk_steep" : "kda_bwd_chunk", st,                                \
+              hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV, QKN, 1>), dim3(a.max_chunks, a.H), dim3(512), \
+                                 0, st, a));                                                               \
+  } while (0)
     if (a.qk_norm)
-      KDA_TIMED("kda_bwd_chunk", st,
-                hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV, true>), dim3(a.max_chunks, a.H), dim3(512), 0, st, a));
+      KDA_BWDC(true);
     else
-      KDA_TIMED("kda_bwd_chunk", st,
-                hipLaunchKernelGGL((kda_bwd_chunk<E, O, DK, DV, false>), dim3(a.max_chunks, a.H), dim3(512), 0, st, a));
+      KDA_BWDC(false);
+#undef KDA_BWDC
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

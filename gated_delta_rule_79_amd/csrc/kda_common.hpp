@@ -398,6 +398,20 @@ __device__ __forceinline__ int pair_c(int pi) { const int R = pair_r(pi); return
 // whatever then falls out of fp32 range was below e^-23 of the result.
 constexpr float CHAIN_MIN = 1.8e-35f;   // e^-80
 
+// The usual path keeps one reference row in the middle of each 16-row block
+// (m = 16a + 8): its row factors span up to 8 tokens and its column factors 7.
+// While every such span decays by less than e^-STEEP_SPAN, a product's factors above 1
+// stay below e^{2 STEEP_SPAN} = e^64 together, so whatever falls out of fp32 range
+// was below e^-23 of the result.  steep_block: does thread (channel tid % dk, block
+// tid / dk < 4) see a span at or past that limit in the cumulated log decay g?
+constexpr float STEEP_SPAN = 32.f;
+__device__ __forceinline__ bool steep_block(const float* g, int ldg, int tid, int dk) {
+  const int c = tid % dk, a = tid / dk;
+  if (a >= CH / 16) return false;
+  const float g0 = g[(16 * a) * ldg + c], gm = g[(16 * a + 8) * ldg + c], g1 = g[(16 * a + 15) * ldg + c];
+  return g0 - gm >= STEEP_SPAN || gm - g1 >= STEEP_SPAN;
+}
+
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------

@@ -135,7 +135,7 @@ struct PrepLds {
   static constexpr size_t VT = KPT + (size_t)DK * LDT * sizeof(OP);
   static constexpr size_t A = VT + (size_t)DV * LDT * sizeof(OP);
   static constexpr size_t TOT = A + (size_t)CH * LDA * 4;
-  static constexpr size_t BETA = TOT + 4 * DK * 4;
+  static constexpr size_t BETA = TOT + 256 * 8;   // TOT: double [256 / DK][DK] part sums of the scan
   static constexpr size_t X = BETA + CH * 4;
   static constexpr size_t BYTES = X + 3 * 256 * 4;
   // aliases used once the Gram blocks are done
@@ -144,6 +144,7 @@ struct PrepLds {
   static_assert((size_t)CH * LDA * 4 <= (size_t)CH * LDG * 4, "T alias");
   static_assert((size_t)CH * LDT * sizeof(OP) <= (size_t)CH * LDK * sizeof(E), "Te alias");
   static_assert(BYTES <= 163840, "prep LDS");
+  static_assert(TOT % 8 == 0, "fp64 scan partials stay 8-byte aligned");
 };
 
 // QKN: q and k rows are L2-normalised on load (KDA_FLAG_QK_L2NORM).
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
   OP* sKpT = reinterpret_cast<OP*>(smem + L::KPT);
   OP* sVT = reinterpret_cast<OP*>(smem + L::VT);
   float* sA = reinterpret_cast<float*>(smem + L::A);
-  float* sTot = reinterpret_cast<float*>(smem + L::TOT);
+  double* sTot = reinterpret_cast<double*>(smem + L::TOT);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sX = reinterpret_cast<float*>(smem + L::X);
 
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
 
   using WB = WsBlock<E, DK, DV>;
   const size_t blk = (size_t)j * H + h;
+  if (tid == 0) a.steep[blk] = 1;   // this kernel always forms its Gram blocks through 8-token groups
   OP* wW = reinterpret_cast<OP*>(a.wsW) + blk * WB::W;
   OP* wKhT = reinterpret_cast<OP*>(a.wsKhT) + blk * WB::KHT;
   OP* wQt = reinterpret_cast<OP*>(a.wsQt) + blk * WB::QT;
@@ -242,26 +244,28 @@ __global__ __launch_bounds__(256) void kda_prep(const Args a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) sVT[(32 * vs + 8 * q4 + i) * L::LDT + r] = cvt<OP>(xv[vs][i]);
   __syncthreads();
-  // cumulative sum over tokens, in place: thread (channel c, part s) scans RPS rows
+  // cumulative sum over tokens, in place: thread (channel c, part s) scans RPS rows.
+  // The sums are taken in fp64 and each g is rounded to fp32 once: under the log
+  // alpha floor |g| reaches 64 * 16 within a chunk, where one fp32 rounding is
+  // already 2^-14 (and the decayed factors carry the error of g as a relative one).
   {
     constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
     const int c = tid % DK, s = tid / DK;
-    float acc = 0.f;
+    double tot = 0.0;
 #pragma unroll 8
-    for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
-      acc += sG[rr * L::LDG + c];
-      sG[rr * L::LDG + c] = acc;
-    }
-    sTot[s * DK + c] = acc;
+    for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) tot += (double)sG[rr * L::LDG + c];
+    sTot[s * DK + c] = tot;
   }
   __syncthreads();
   {
     constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
     const int c = tid % DK, s = tid / DK;
-    if (s > 0) {
-      float off = 0.f;
-      for (int s2 = 0; s2 < s; ++s2) off += sTot[s2 * DK + c];
-      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
+    double acc = 0.0;
+    for (int s2 = 0; s2 < s; ++s2) acc += sTot[s2 * DK + c];
+#pragma unroll 8
+    for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
+      acc += (double)sG[rr * L::LDG + c];
+      sG[rr * L::LDG + c] = (float)acc;
     }
   }
   __syncthreads();
@@ -504,7 +508,12 @@ __device__ __forceinline__ f32x4 mm16_f32(const float* A, int lda, const float* 
 
 // GATE: log_alpha holds a raw gate x (KDA_FLAG_GATE_LOGSIGMOID).  Both options
 // are compile-time so the plain kernel keeps its register budget.
-template <int DK, int DV, bool BWD, bool QKN, bool GATE>
+// PATH 0: the usual chunk-heads; a chunk-head where some channel decays by more than
+// e^-STEEP_SPAN within 8 tokens is flagged in a.steep and left for PATH 1, which
+// visits only the flagged ones and forms the decayed Gram blocks through 8-token
+// groups (see group_ref).  Two instantiations keep the usual path's registers free of
+// the other one's.
+template <int DK, int DV, bool BWD, bool QKN, bool GATE, int PATH>
 __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   using L = Prep8Lds<DK, DV>;
   using E = bf16;
@@ -554,7 +563,15 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
     pb = tid < c.len ? f32(gb[(t0 + tid) * H + h]) : 0.f;
   };
 
-  int item = blockIdx.x;
+  // PATH 1 walks only the flagged items (the slots past the last chunk, never flagged
+  // by PATH 0, are empty and end the walk wherever they are met)
+  const int32_t* steep = a.steep;
+  auto advance = [&](int it) __attribute__((always_inline)) {
+    if constexpr (PATH == 1)
+      while (it < n_items && steep[it] == 0) it += (int)gridDim.x;
+    return it;
+  };
+  int item = advance((int)blockIdx.x);
   ChunkInfo ci = item < n_items ? a.chunks[item / H] : ChunkInfo{0, 0, 0, 0};
   if (ci.len > 0) fetch(item, ci);
   while (ci.len > 0) {   // the same value in every thread
@@ -601,7 +618,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       });
     }
     if (tid < CH) sBeta[tid] = pb;
-    const int nitem = item + (int)gridDim.x;
+    const int nitem = advance(item + (int)gridDim.x);
     const ChunkInfo nci = nitem < n_items ? a.chunks[nitem / H] : ChunkInfo{0, 0, 0, 0};
     if (nci.len > 0) fetch(nitem, nci);
     __syncthreads();
@@ -627,6 +644,12 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
     }
     __syncthreads();
+    bool skip = false;
+    if constexpr (PATH == 0) {
+      skip = __syncthreads_or(steep_block(sG, L::LDG, tid, DK));
+      if (tid == 0) a.steep[blk] = skip ? 1 : 0;
+    }
+    if (!skip) {
 
     // ---- elementwise: Qt (token rows), K+^T to LDS and Kh^T (channel rows), Gamma_C
     {
@@ -664,107 +687,103 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
         }
         store4<OP>(sKpT + c * L::LDT + t0, kp[0], kp[1], kp[2], kp[3]);
         store4<OP>(sKpT + c * L::LDT + t0 + 4, kp[4], kp[5], kp[6], kp[7]);
-        store4<OP>(wKhT + c * CH + t0, kh[0], kh[1], kh[2], kh[3]);
-        store4<OP>(wKhT + c * CH + t0 + 4, kh[4], kh[5], kh[6], kh[7]);
+        if constexpr (BWD) {   // training mode: split, for the state update (see StateLds)
+          OP* wKhTL = reinterpret_cast<OP*>(a.wsKhTL) + blk * WB::KHT;
+          store4_split<OP>(wKhT + c * CH + t0, wKhTL + c * CH + t0, kh[0], kh[1], kh[2], kh[3]);
+          store4_split<OP>(wKhT + c * CH + t0 + 4, wKhTL + c * CH + t0 + 4, kh[4], kh[5], kh[6], kh[7]);
+        } else {
+          store4<OP>(wKhT + c * CH + t0, kh[0], kh[1], kh[2], kh[3]);
+          store4<OP>(wKhT + c * CH + t0 + 4, kh[4], kh[5], kh[6], kh[7]);
+        }
       }
       if (tid < DK) wGam[tid] = __expf(sG[(CH - 1) * L::LDG + tid]);
     }
 
-    // ---- decayed Gram blocks (split bf16 operands; reference rows in the middle of
-    // 8-token groups, m(R) = 8R + 4).  For row r in group R and column i in group C <= R,
-    //   e^{g_r - g_i} = e^{g_r - g_m(R)} e^{g_m(R) - g_m(C)} e^{g_m(C) - g_i},
-    // the outer two factors tabulated per (token, channel), the middle one per (R, C) pair.
-    // With log alpha >= -LOG_ALPHA_FLOOR no factor exceeds e^{4 LOG_ALPHA_FLOOR}: the row
-    // and column factors span at most 4 and 3 tokens and the chain factor is at most 1.
-    // A 16x16 tile (a, b) is computed once per row group R in {2a, 2a+1} with the chain
-    // folded into the column operand (zero for C > R, where the pairs lie above the
-    // diagonal); each lane keeps the rows of its own group.  The channels go in passes of
-    // GC; the 20 tile halves are dealt to the waves so each SIMD gets five.
-    {
-      constexpr int GC = L::GC, NPASS = DK / GC;
-      bf16* tKh = reinterpret_cast<bf16*>(smem + L::GKH);
-      bf16* tKl = reinterpret_cast<bf16*>(smem + L::GKL);
-      bf16* tQh = reinterpret_cast<bf16*>(smem + L::GQH);
-      bf16* tQl = reinterpret_cast<bf16*>(smem + L::GQL);
-      float* tKR = reinterpret_cast<float*>(smem + L::GKR);
-      float* tF = reinterpret_cast<float*>(smem + L::GF);
-      // tile halves (a, b, h): list index w, w + 8, w + 16 for wave w
-      constexpr int HA[20] = {0, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3, 3, 3, 3, 3, 0, 1, 2, 3};
-      constexpr int HB[20] = {0, 0, 1, 0, 0, 1, 2, 0, 1, 0, 1, 2, 3, 0, 1, 2, 0, 1, 2, 3};
-      constexpr int HH[20] = {1, 0, 1, 1, 0, 0, 1, 1, 1, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0};
-      const int nitem = w < 4 ? 3 : 2;
-      f32x4 akk[3] = {zero4(), zero4(), zero4()}, aqk[3] = {zero4(), zero4(), zero4()};
-      static_assert(NT == CH * (GC / 4), "table build: one thread per (token, 4 channels)");
-      for (int ps = 0; ps < NPASS; ++ps) {
-        if (ps > 0) __syncthreads();   // the previous pass's table reads are done
-        {
-          const int r = tid / (GC / 4), cl0 = 4 * (tid % (GC / 4)), c0 = GC * ps + cl0;
-          const int mref = group_ref(r >> 3);
-          float ek[4], eq[4], kr[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float g = sG[r * L::LDG + c0 + u], gm = sG[mref * L::LDG + c0 + u];
-            const float kv = f32(sK[r * L::LDK + c0 + u]) * nk(r);
-            const float e = __expf(g - gm);
-            ek[u] = kv * e;
-            eq[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * e;
-            kr[u] = kv * __expf(gm - g);
+    // ---- decayed Gram blocks.  Usual chunks: reference rows in the middle of 16-row
+    // blocks, one product per tile.  Chunks where some channel decays by more than
+    // e^-32 within 8 tokens take the 8-token-group path, whose factors stay bounded
+    // for any gate (see group_ref and CHAIN_MIN).
+    if constexpr (PATH == 0) {
+      // ---- decayed Gram blocks (split bf16 operands; reference row m(b) = 16b + 8).
+      // Block (a, b), b <= a, of K+ K-^T is sum_c k~_r[c] (k_i[c] e^{g_m(b) - g_i}) e^{g_m(a) - g_m(b)}
+      // with k~_r = k_r e^{g_r - g_m(a)}; every factor stays within an 8-token decay.  The
+      // channels go in passes of GC: each pass tabulates k~ and q~ (split), k e^{g_m - g} and
+      // the block-to-block factors once, and every wave reads its operands as 16-byte rows.
+      // The ten blocks are dealt to the waves so each SIMD (waves w and w + 4) gets two or three.
+      {
+        constexpr int GC = L::GC, NPASS = DK / GC;
+        bf16* tKh = reinterpret_cast<bf16*>(smem + L::GKH);
+        bf16* tKl = reinterpret_cast<bf16*>(smem + L::GKL);
+        bf16* tQh = reinterpret_cast<bf16*>(smem + L::GQH);
+        bf16* tQl = reinterpret_cast<bf16*>(smem + L::GQL);
+        float* tKR = reinterpret_cast<float*>(smem + L::GKR);
+        float* tF = reinterpret_cast<float*>(smem + L::GF);
+        // this wave's blocks: list index w and w + 8 of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+        constexpr int BA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+        constexpr int BB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+        const int nblk = w < 2 ? 2 : 1;
+        f32x4 akk[2] = {zero4(), zero4()}, aqk[2] = {zero4(), zero4()};
+        static_assert(NT == CH * (GC / 4), "table build: one thread per (token, 4 channels)");
+        for (int ps = 0; ps < NPASS; ++ps) {
+          if (ps > 0) __syncthreads();   // the previous pass's table reads are done
+          {
+            const int r = tid / (GC / 4), cl0 = 4 * (tid % (GC / 4)), c0 = GC * ps + cl0;
+            const int mref = 16 * (r >> 4) + 8;
+            float ek[4], eq[4], kr[4];
+  #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float g = sG[r * L::LDG + c0 + u], gm = sG[mref * L::LDG + c0 + u];
+              const float e = __expf(g - gm);
+              const float kv = f32(sK[r * L::LDK + c0 + u]) * nk(r);
+              ek[u] = kv * e;
+              eq[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * e;
+              kr[u] = kv * __expf(gm - g);
+            }
+            store4_split<bf16>(tKh + r * L::LDQ + cl0, tKl + r * L::LDQ + cl0, ek[0], ek[1], ek[2], ek[3]);
+            store4_split<bf16>(tQh + r * L::LDQ + cl0, tQl + r * L::LDQ + cl0, eq[0], eq[1], eq[2], eq[3]);
+            *reinterpret_cast<f32x4*>(tKR + r * L::LDR + cl0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+            if (tid < 6 * GC) {   // pair (a, b), b < a, in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+              const int pi = tid / GC, c = GC * ps + tid % GC;
+              const int pa = pi < 1 ? 1 : (pi < 3 ? 2 : 3), pb = pi < 1 ? 0 : (pi < 3 ? pi - 1 : pi - 3);
+              tF[tid] = __expf(sG[(16 * pa + 8) * L::LDG + c] - sG[(16 * pb + 8) * L::LDG + c]);
+            }
           }
-          store4_split<bf16>(tKh + r * L::LDQ + cl0, tKl + r * L::LDQ + cl0, ek[0], ek[1], ek[2], ek[3]);
-          store4_split<bf16>(tQh + r * L::LDQ + cl0, tQl + r * L::LDQ + cl0, eq[0], eq[1], eq[2], eq[3]);
-          *reinterpret_cast<f32x4*>(tKR + r * L::LDR + cl0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
-          for (int e = tid; e < NGROUP_PAIRS * GC; e += NT) {   // chain factors of the group pairs C < R
-            const int pi = e / GC, c = GC * ps + e % GC;
-            tF[e] = __expf(sG[group_ref(pair_r(pi)) * L::LDG + c] - sG[group_ref(pair_c(pi)) * L::LDG + c]);
+          __syncthreads();
+  #pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if (j < nblk) {
+              const int li = w + 8 * j, ba = BA[li], bb = BB[li];
+              const SFrag<bf16> fk = sfrag_pair<bf16>(tKh, tKl, L::LDQ, 16 * ba + r16, 8 * q4);
+              const SFrag<bf16> fq = sfrag_pair<bf16>(tQh, tQl, L::LDQ, 16 * ba + r16, 8 * q4);
+              const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4);
+              const f32x4 v1 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4 + 4);
+              float xr[8];
+              if (bb == ba) {
+  #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  xr[u] = v0[u];
+                  xr[u + 4] = v1[u];
+                }
+              } else {
+                const float* f = tF + GC * (ba * (ba - 1) / 2 + bb) + 8 * q4;
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(f), f1 = *reinterpret_cast<const f32x4*>(f + 4);
+  #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  xr[u] = v0[u] * f0[u];
+                  xr[u + 4] = v1[u] * f1[u];
+                }
+              }
+              const SFrag<bf16> fr = sfrag_from<bf16>(xr);
+              akk[j] = mma_ss(fk, fr, akk[j]);
+              aqk[j] = mma_ss(fq, fr, aqk[j]);
+            }
           }
         }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          if (j < nitem) {
-            const int li = w + 8 * j, ba = HA[li], bb = HB[li], R = 2 * ba + HH[li];
-            const int C = 2 * bb + (r16 >> 3);   // group of this lane's column
-            const SFrag<bf16> fk = sfrag_pair<bf16>(tKh, tKl, L::LDQ, 16 * ba + r16, 8 * q4);
-            const SFrag<bf16> fq = sfrag_pair<bf16>(tQh, tQl, L::LDQ, 16 * ba + r16, 8 * q4);
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4 + 4);
-            float xr[8];
-            bool tiny = false;
-            if (C < R) {
-              const float* f = tF + GC * pair_index(R, C) + 8 * q4;
-              const f32x4 f0 = *reinterpret_cast<const f32x4*>(f), f1 = *reinterpret_cast<const f32x4*>(f + 4);
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                xr[u] = v0[u] * f0[u];
-                xr[u + 4] = v1[u] * f1[u];
-                tiny |= f0[u] < CHAIN_MIN || f1[u] < CHAIN_MIN;
-              }
-            } else {
-              const bool on = C == R;   // C > R: pairs above the diagonal (zero, and kept finite)
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                xr[u] = on ? v0[u] : 0.f;
-                xr[u + 4] = on ? v1[u] : 0.f;
-              }
-            }
-            if (__any(tiny) && C < R) {   // one exponential per element (see CHAIN_MIN)
-              const int i = 16 * bb + r16, c0 = GC * ps + 8 * q4, mr = group_ref(R);
-#pragma unroll
-              for (int u = 0; u < 8; ++u)
-                xr[u] = f32(sK[i * L::LDK + c0 + u]) * nk(i) * __expf(sG[mr * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
-            }
-            const SFrag<bf16> fr = sfrag_from<bf16>(xr);
-            akk[j] = mma_ss(fk, fr, akk[j]);
-            aqk[j] = mma_ss(fq, fr, aqk[j]);
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        if (j < nitem) {
-          const int li = w + 8 * j, ba = HA[li], bb = HB[li], hh = HH[li];
-          if ((q4 >> 1) == hh) {   // this lane's rows 4q4 .. 4q4 + 3 of the tile are in row group 2a + hh
-#pragma unroll
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (j < nblk) {
+            const int li = w + 8 * j, ba = BA[li], bb = BB[li];
+  #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
               const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
               sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[j][ii] : 0.f;
@@ -773,15 +792,131 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
             }
           }
         }
+        if (w < 6) {   // blocks above the diagonal: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+          const int ba = w < 3 ? 0 : (w < 5 ? 1 : 2), bb = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
+  #pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
+            sA[rr * L::LDA + cc] = 0.f;
+            wAqk[rr * CH + cc] = cvt<OP>(0.f);
+            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = 0.f;
+          }
+        }
       }
-      if (w < 6) {   // blocks above the diagonal: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-        const int ba = w < 3 ? 0 : (w < 5 ? 1 : 2), bb = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
-          sA[rr * L::LDA + cc] = 0.f;
-          wAqk[rr * CH + cc] = cvt<OP>(0.f);
-          if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = 0.f;
+    } else {
+      // ---- decayed Gram blocks (split bf16 operands; reference rows in the middle of
+      // 8-token groups, m(R) = 8R + 4).  For row r in group R and column i in group C <= R,
+      //   e^{g_r - g_i} = e^{g_r - g_m(R)} e^{g_m(R) - g_m(C)} e^{g_m(C) - g_i},
+      // the outer two factors tabulated per (token, channel), the middle one per (R, C) pair.
+      // With log alpha >= -LOG_ALPHA_FLOOR no factor exceeds e^{4 LOG_ALPHA_FLOOR}: the row
+      // and column factors span at most 4 and 3 tokens and the chain factor is at most 1.
+      // A 16x16 tile (a, b) is computed once per row group R in {2a, 2a+1} with the chain
+      // folded into the column operand (zero for C > R, where the pairs lie above the
+      // diagonal); each lane keeps the rows of its own group.  The channels go in passes of
+      // GC; the 20 tile halves are dealt to the waves so each SIMD gets five.
+      {
+        constexpr int GC = L::GC, NPASS = DK / GC;
+        bf16* tKh = reinterpret_cast<bf16*>(smem + L::GKH);
+        bf16* tKl = reinterpret_cast<bf16*>(smem + L::GKL);
+        bf16* tQh = reinterpret_cast<bf16*>(smem + L::GQH);
+        bf16* tQl = reinterpret_cast<bf16*>(smem + L::GQL);
+        float* tKR = reinterpret_cast<float*>(smem + L::GKR);
+        float* tF = reinterpret_cast<float*>(smem + L::GF);
+        // tile halves (a, b, h): list index w, w + 8, w + 16 for wave w
+        constexpr int HA[20] = {0, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3, 3, 3, 3, 3, 0, 1, 2, 3};
+        constexpr int HB[20] = {0, 0, 1, 0, 0, 1, 2, 0, 1, 0, 1, 2, 3, 0, 1, 2, 0, 1, 2, 3};
+        constexpr int HH[20] = {1, 0, 1, 1, 0, 0, 1, 1, 1, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0};
+        const int nitem = w < 4 ? 3 : 2;
+        f32x4 akk[3] = {zero4(), zero4(), zero4()}, aqk[3] = {zero4(), zero4(), zero4()};
+        static_assert(NT == CH * (GC / 4), "table build: one thread per (token, 4 channels)");
+        for (int ps = 0; ps < NPASS; ++ps) {
+          if (ps > 0) __syncthreads();   // the previous pass's table reads are done
+          {
+            const int r = tid / (GC / 4), cl0 = 4 * (tid % (GC / 4)), c0 = GC * ps + cl0;
+            const int mref = group_ref(r >> 3);
+            float ek[4], eq[4], kr[4];
+  #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float g = sG[r * L::LDG + c0 + u], gm = sG[mref * L::LDG + c0 + u];
+              const float kv = f32(sK[r * L::LDK + c0 + u]) * nk(r);
+              const float e = __expf(g - gm);
+              ek[u] = kv * e;
+              eq[u] = f32(sQ[r * L::LDK + c0 + u]) * nq(r) * e;
+              kr[u] = kv * __expf(gm - g);
+            }
+            store4_split<bf16>(tKh + r * L::LDQ + cl0, tKl + r * L::LDQ + cl0, ek[0], ek[1], ek[2], ek[3]);
+            store4_split<bf16>(tQh + r * L::LDQ + cl0, tQl + r * L::LDQ + cl0, eq[0], eq[1], eq[2], eq[3]);
+            *reinterpret_cast<f32x4*>(tKR + r * L::LDR + cl0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+            for (int e = tid; e < NGROUP_PAIRS * GC; e += NT) {   // chain factors of the group pairs C < R
+              const int pi = e / GC, c = GC * ps + e % GC;
+              tF[e] = __expf(sG[group_ref(pair_r(pi)) * L::LDG + c] - sG[group_ref(pair_c(pi)) * L::LDG + c]);
+            }
+          }
+          __syncthreads();
+  #pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            if (j < nitem) {
+              const int li = w + 8 * j, ba = HA[li], bb = HB[li], R = 2 * ba + HH[li];
+              const int C = 2 * bb + (r16 >> 3);   // group of this lane's column
+              const SFrag<bf16> fk = sfrag_pair<bf16>(tKh, tKl, L::LDQ, 16 * ba + r16, 8 * q4);
+              const SFrag<bf16> fq = sfrag_pair<bf16>(tQh, tQl, L::LDQ, 16 * ba + r16, 8 * q4);
+              const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4);
+              const f32x4 v1 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4 + 4);
+              float xr[8];
+              bool tiny = false;
+              if (C < R) {
+                const float* f = tF + GC * pair_index(R, C) + 8 * q4;
+                const f32x4 f0 = *reinterpret_cast<const f32x4*>(f), f1 = *reinterpret_cast<const f32x4*>(f + 4);
+  #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  xr[u] = v0[u] * f0[u];
+                  xr[u + 4] = v1[u] * f1[u];
+                  tiny |= f0[u] < CHAIN_MIN || f1[u] < CHAIN_MIN;
+                }
+              } else {
+                const bool on = C == R;   // C > R: pairs above the diagonal (zero, and kept finite)
+  #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  xr[u] = on ? v0[u] : 0.f;
+                  xr[u + 4] = on ? v1[u] : 0.f;
+                }
+              }
+              if (__any(tiny) && C < R) {   // one exponential per element (see CHAIN_MIN)
+                const int i = 16 * bb + r16, c0 = GC * ps + 8 * q4, mr = group_ref(R);
+  #pragma unroll
+                for (int u = 0; u < 8; ++u)
+                  xr[u] = f32(sK[i * L::LDK + c0 + u]) * nk(i) * __expf(sG[mr * L::LDG + c0 + u] - sG[i * L::LDG + c0 + u]);
+              }
+              const SFrag<bf16> fr = sfrag_from<bf16>(xr);
+              akk[j] = mma_ss(fk, fr, akk[j]);
+              aqk[j] = mma_ss(fq, fr, aqk[j]);
+            }
+          }
+        }
+  #pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          if (j < nitem) {
+            const int li = w + 8 * j, ba = HA[li], bb = HB[li], hh = HH[li];
+            if ((q4 >> 1) == hh) {   // this lane's rows 4q4 .. 4q4 + 3 of the tile are in row group 2a + hh
+  #pragma unroll
+              for (int ii = 0; ii < 4; ++ii) {
+                const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
+                sA[rr * L::LDA + cc] = cc < rr ? sBeta[rr] * akk[j][ii] : 0.f;
+                wAqk[rr * CH + cc] = cvt<OP>(cc <= rr ? aqk[j][ii] : 0.f);
+                if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = cc < rr ? akk[j][ii] : 0.f;
+              }
+            }
+          }
+        }
+        if (w < 6) {   // blocks above the diagonal: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+          const int ba = w < 3 ? 0 : (w < 5 ? 1 : 2), bb = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
+  #pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
+            sA[rr * L::LDA + cc] = 0.f;
+            wAqk[rr * CH + cc] = cvt<OP>(0.f);
+            if constexpr (BWD) a.wsG[blk * WB::G + rr * CH + cc] = 0.f;
+          }
         }
       }
     }
@@ -871,6 +1006,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
                      acc[1], acc[2], acc[3]);
       }
     }
+    }   // !skip
     item = nitem;
     ci = nci;
   }
@@ -886,10 +1022,15 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
 // copied to LDS in the operand type for the products that read it.  The next
 // chunk's matrices are loaded into registers while the current one computes.
 // UF: U~ is read in fp32 (the copy a training-mode prep writes) rather than in
-// the operand type.
+// the operand type.  With UF and 2-byte operands (KS) the state update takes Kh
+// and U as split (hi, lo) pairs: the backward's dlog alpha collects the rounding
+// of every saved state (through dGamma_C), and plain fp16 Kh and U would put
+// about 2^-11 of each chunk's update into it.  The training prep writes Kh^T's
+// lo half beside the hi half (wsKhTL).
 template <typename E, int DK, int DV, int DVS, bool OUT, bool SAVE, bool UF = SAVE>
 struct StateLds {
   using OP = typename OpOf<E>::T;
+  static constexpr bool KS = UF && sizeof(OP) == 2;
   static constexpr int P = PADE<OP>;
   static constexpr int LDK = DK + P;
   static constexpr int LDT = CH + P;
@@ -902,7 +1043,9 @@ struct StateLds {
   static constexpr size_t GAM = UT + (size_t)DVS * CH * sizeof(UTT);              // float [DK]
   static constexpr size_t ST = GAM + (size_t)DK * 4;                              // OP [DVS][LDK]  S^T
   static constexpr size_t UL = ST + (size_t)DVS * LDK * sizeof(OP);               // OP [DVS][LDT]  U^T
-  static constexpr size_t BYTES = UL + (size_t)DVS * LDT * sizeof(OP);
+  static constexpr size_t KHL = UL + (size_t)DVS * LDT * sizeof(OP);              // OP [DK][LDT]   Kh^T lo (KS)
+  static constexpr size_t ULL = KHL + (KS ? (size_t)DK * LDT * sizeof(OP) : 0);   // OP [DVS][LDT]  U^T lo (KS)
+  static constexpr size_t BYTES = ULL + (KS ? (size_t)DVS * LDT * sizeof(OP) : 0);
   static_assert(BYTES <= 163840, "state LDS");
 };
 
@@ -953,6 +1096,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   float* sGam = reinterpret_cast<float*>(smem + L::GAM);
   OP* sST = reinterpret_cast<OP*>(smem + L::ST);
   OP* sUL = reinterpret_cast<OP*>(smem + L::UL);
+  constexpr bool KS = L::KS;
+  OP* sKhL = reinterpret_cast<OP*>(smem + L::KHL);
+  OP* sULL = reinterpret_cast<OP*>(smem + L::ULL);
 
   // kernel-argument fields are copied to locals so the argument block never
   // has its address taken (that would place it in scratch)
@@ -960,6 +1106,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   const OP* gQt = reinterpret_cast<const OP*>(a.wsQt);
   const OP* gAqk = reinterpret_cast<const OP*>(a.wsAqk);
   const OP* gKhT = reinterpret_cast<const OP*>(a.wsKhT);
+  const OP* gKhTL = reinterpret_cast<const OP*>(a.wsKhTL);   // KS: Kh^T lo, same blocks as Kh^T
   const UTT* gUt = UF ? reinterpret_cast<const UTT*>(a.wsUtF) : reinterpret_cast<const UTT*>(a.wsUt);
   const float* gGam = a.wsGam;
   float* gS = reinterpret_cast<float*>(a.wsS);
@@ -991,6 +1138,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
     TileCopy<OP, CH, DK, NT> w;
     TileCopy<OP, (OUT ? CH : 1), (OUT ? DK : 16 / sizeof(OP)), NT> qt;
     TileCopy<OP, DK, CH, NT> kht;
+    TileCopy<OP, (KS ? DK : 1), (KS ? CH : 16 / sizeof(OP)), NT> khtl;   // Kh^T lo (KS)
     TileCopy<OP, (OUT ? CH : 1), (OUT ? CH : 16 / sizeof(OP)), NT> aqk;
     TileCopy<UTT, DVS, CH, NT> ut;
     TileCopy<float, 1, DK, NT> gam;
@@ -1006,6 +1154,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       p.aqk.load(gAqk + b * WB::AQK, CH);
     }
     p.kht.load(gKhT + b * WB::KHT, CH);
+    if constexpr (KS) p.khtl.load(gKhTL + b * WB::KHT, CH);
     if (!xf) p.ut.load(gUt + b * WB::UT + (size_t)n0 * CH, CH);  // UT == UTF element count
     p.gam.load(gGam + b * WB::GAM, DK);
   };
@@ -1016,6 +1165,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       p.aqk.store(sAqk, L::LDT);
     }
     p.kht.store(sKhT, L::LDT);
+    if constexpr (KS) p.khtl.store(sKhL, L::LDT);
     if (!xf) p.ut.store(sUt, CH);
     p.gam.store(sGam, DK);
   };
@@ -1052,8 +1202,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
                                     zero4());
         float ut[4] = {0.f, 0.f, 0.f, 0.f};
         if (!xf) load4<UTT>(sUt + (16 * nt + r16) * CH + 16 * w + 4 * q4, ut);
-        store4<OP>(sUL + (16 * nt + r16) * L::LDT + 16 * w + 4 * q4, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2],
-                   ut[3] - x[3]);
+        const int uo = (16 * nt + r16) * L::LDT + 16 * w + 4 * q4;
+        if constexpr (KS)
+          store4_split<OP>(sUL + uo, sULL + uo, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]);
+        else
+          store4<OP>(sUL + uo, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]);
         if constexpr (SAVE) {
           // and U in fp32, token-major [CH][DV]
           float* dst = gU + blk_of(n) * WB::U + (size_t)(16 * w + 4 * q4) * DV + n0 + 16 * nt + r16;
@@ -1092,9 +1245,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
     for (int i = 0; i < SPW; ++i) {
       const int t = w + 8 * i, mt = t % MTS, nt = t / MTS;
       if (t < NST) {
-        const f32x4 x = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sKhT, L::LDT, 16 * mt + rr, k); },
-                                    [&](int rr, int k) { return frag_row<OP>(sUL, L::LDT, 16 * nt + rr, k); },
-                                    zero4());
+        f32x4 x = zero4();
+        if constexpr (KS) {
+#pragma unroll
+          for (int k = 0; k < CH; k += 32)
+            x = mma_ss(sfrag_pair<OP>(sKhT, sKhL, L::LDT, 16 * mt + r16, k + 8 * q4),
+                       sfrag_pair<OP>(sUL, sULL, L::LDT, 16 * nt + r16, k + 8 * q4), x);
+        } else {
+          x = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sKhT, L::LDT, 16 * mt + rr, k); },
+                          [&](int rr, int k) { return frag_row<OP>(sUL, L::LDT, 16 * nt + rr, k); }, x);
+        }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) S[i][ii] = sGam[16 * mt + 4 * q4 + ii] * S[i][ii] + x[ii];
       }
@@ -1291,7 +1451,10 @@ __global__ __launch_bounds__(512) void kda_segment_rscan(const Args a) {
   const int w = wave_id(), l = lane_id(), r16 = l & 15, q4 = l >> 4;
   constexpr size_t SZ = (size_t)DK * DV, MZ = (size_t)DK * DK;
   const float* dfin = a.dfinal ? a.dfinal + ((size_t)n * a.H + h) * SZ : nullptr;
-  for (int o = tid; o < DK * DV; o += NT) sS[(o / DV) * LS + o % DV] = dfin ? dfin[o] : 0.f;
+  // the scan runs on scaled gradients (the stretches' local runs read dO times s);
+  // d_init_state is stored unscaled
+  const float gs = a.gscale ? a.gscale[0] : 1.f, gs_inv = a.gscale ? a.gscale[1] : 1.f;
+  for (int o = tid; o < DK * DV; o += NT) sS[(o / DV) * LS + o % DV] = dfin ? gs * dfin[o] : 0.f;
   __syncthreads();
   for (int p = P - 1; p >= 0; --p) {
     const size_t v = ((size_t)n * P + p) * a.H + h;
@@ -1323,7 +1486,7 @@ __global__ __launch_bounds__(512) void kda_segment_rscan(const Args a) {
     __syncthreads();
   }
   if (a.dinit)
-    for (int o = tid; o < DK * DV; o += NT) a.dinit[((size_t)n * a.H + h) * SZ + o] = sS[(o / DV) * LS + o % DV];
+    for (int o = tid; o < DK * DV; o += NT) a.dinit[((size_t)n * a.H + h) * SZ + o] = gs_inv * sS[(o / DV) * LS + o % DV];
 }
 
 hipError_t launch_segment_map(const Args& a, hipStream_t st) {
@@ -1388,8 +1551,12 @@ static hipError_t launch_prep(const Args& a, hipStream_t st, const char* name) {
   if constexpr (sizeof(E) == 2) {
     const long long items = (long long)a.max_chunks * a.H;
     const int grid = (int)std::min<long long>(items, device_cus());
-#define KDA_PREP8(QKN, GATE) \
-  KDA_TIMED(name, st, hipLaunchKernelGGL((kda_prep8<DK, DV, BWD, QKN, GATE>), dim3(grid), dim3(512), 0, st, a))
+#define KDA_PREP8(QKN, GATE)                                                                                \
+  do {                                                                                                       \
+    KDA_TIMED(name, st, hipLaunchKernelGGL((kda_prep8<DK, DV, BWD, QKN, GATE, 0>), dim3(grid), dim3(512), 0, st, a)); \
+    KDA_TIMED("kda_prep_steep", st,                                                                          \
+              hipLaunchKernelGGL((kda_prep8<DK, DV, BWD, QKN, GATE, 1>), dim3(grid), dim3(512), 0, st, a));  \
+  } while (0)
     if (a.qk_norm && a.gate_ls)
       KDA_PREP8(true, true);
     else if (a.qk_norm)

@@ -8,6 +8,8 @@
 
 namespace kda {
 
+constexpr int GS_PARTS = 2048;   // work-groups of the gradient-scale pre-pass (one partial maximum each)
+
 struct Args {
   // problem
   int B, T, H, dk, dv, N;   // N = number of sequences
@@ -31,14 +33,22 @@ struct Args {
   int32_t* seq_order;       // [N] sequences by decreasing chunk count
   void *wsW, *wsKhT, *wsQt, *wsUt, *wsAqk, *wsT;  // per (chunk, head) blocks, see WsBlock
   float* wsGam;
+  int32_t* steep;           // [chunk slots * H] 1 where the chunk-head takes the 8-token-group path
   // backward only (per chunk-head blocks; see WsBlock for shapes and types)
   float* wsUtF;             // U~^T in fp32 [DV][CH] (the backward's state pass reads it)
   float* wsG;               // un-beta strict Gram K+ K-^T
   float* wsKhF;             // Kh token-major: fp32, or a split pair of fp16 arrays (bf16 inputs)
+  void* wsKhTL;             // bf16 inputs: lo half of Kh^T (Kh^T itself is then the hi half)
   float* wsS;               // state entering each chunk, fp32 [DK][DV]
   float* wsU;               // U, fp32 [CH][DV]
   float* wsdS;              // gradient of the state leaving each chunk, fp32 [DK][DV]
   float* wsdU;              // dU, fp32 [CH][DV]
+  // power-of-two scale of the upstream gradients (bf16 inputs; null otherwise):
+  // gscale[0] = s multiplies dO and dS_final as the kernels read them, gscale[1] =
+  // 1/s every gradient they store; gs_part holds the pre-pass's partial maxima
+  float* gscale;
+  float* gs_part;
+  int dfinal_scaled;        // dfinal already carries s (a stretch's dS_out from the segment scan)
   int dvs;                  // value-column slice width of the sequential passes
   int out_bf16;             // outputs and gradients stored as bf16 (else fp32)
   // fused input preparation
