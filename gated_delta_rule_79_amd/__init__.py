@@ -55,7 +55,7 @@ KDA_CONV_IDENTITY, KDA_CONV_SILU = 0, 1
 class KdaError(RuntimeError):
     def __init__(self, fn, status):
         self.status = status
-        detail = last_error() if status == KDA_ERROR_LAUNCH else ""
+        detail = last_error() if status == KDA_ERROR_LAUNCH or fn == "kda_fwd_noalloc" else ""
         super().__init__(f"{fn} failed: {status_string(status)} (status {status})" + (f": {detail}" if detail else ""))
 
 
@@ -82,6 +82,8 @@ def load_library(path: str | None = None):
     lib.kda_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
@@ -248,6 +250,29 @@ def fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, scale=None, 
                      workspace.numel() * workspace.element_size(), _stream(dev))
     if rc:
         raise KdaError("kda_fwd", rc)
+    return out, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # KDA_NOALLOC_SCRATCH_BYTES in kda.h
+
+
+def fwd_noalloc(q, k, v, log_alpha, beta, out, final_state=None, init_state=None, cu_seqlens=None, scale=None,
+                out_dtype=None, qk_l2norm=False, gate_logsigmoid=False):
+    """kda_fwd_noalloc: the forward pass with the library's own device scratch as its
+    workspace.  The caller passes out (and final_state, or None) already allocated;
+    nothing is allocated here or in the library.  Returns (out, final_state)."""
+    lib = load_library()
+    desc, (B, T, H, dk, dv, N), dev, dt = _prepare(q, k, v, log_alpha, beta, init_state, cu_seqlens, scale,
+                                                   out_dtype)
+    desc.flags = _prep_flags(qk_l2norm, gate_logsigmoid)
+    _check("out", out, dt, (B, T, H, dv), dev)
+    if final_state is not None:
+        import torch
+        _check("final_state", final_state, torch.float32, (N, H, dk, dv), dev)
+    rc = lib.kda_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(init_state), _ptr(out), _ptr(final_state), _ptr(cu_seqlens), _stream(dev))
+    if rc:
+        raise KdaError("kda_fwd_noalloc", rc)
     return out, final_state
 
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_fwd.hip", "kda_bwd.hip", "kda_decode.hip", "kda_conv.hip"]
+SOURCES = ["kda_api.cpp", "kda_fwd.hip", "kda_bwd.hip", "kda_decode.hip", "kda_conv.hip", "kda_noalloc.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -437,6 +437,20 @@ size_t kda_workspace_bytes(const kda_desc* d, int backward) {
 kda_status kda_fwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
                    const void* beta, const float* init_state, void* out, float* final_state,
                    const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream) {
+  return kda::fwd_checked(d, q, k, v, log_alpha, beta, init_state, out, final_state, cu_seqlens, workspace,
+                          workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace kda {
+// kda_fwd's validation and dispatch; `need` (optional) receives the workspace the
+// problem needs once the descriptor and shapes are valid.
+kda_status fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
+                       const void* beta, const float* init_state, void* out, float* final_state,
+                       const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream,
+                       size_t* need) {
+  if (need) *need = 0;
   if (!d) return KDA_ERROR_INVALID_VALUE;
   if (!dims_ok(d)) return KDA_ERROR_NOT_SUPPORTED;
   int N, mc;
@@ -454,6 +468,7 @@ kda_status kda_fwd(const kda_desc* d, const void* q, const void* k, const void* 
   const bool save = (d->flags & KDA_FLAG_SAVE_FOR_BACKWARD) != 0;
   if (save && d->dtype == KDA_F32 && d->dk == 128) return KDA_ERROR_NOT_SUPPORTED;  // no fp32 backward at dk = 128
   const Plan p = make_plan(d, save, N, mc);
+  if (need) *need = p.total;
   if (!workspace || workspace_bytes < p.total) return KDA_ERROR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cu_seqlens && env_int("KDA_DEBUG", 0) && !cu_ok(cu_seqlens, N, d->T, st)) return KDA_ERROR_INVALID_VALUE;
@@ -468,6 +483,11 @@ kda_status kda_fwd(const kda_desc* d, const void* q, const void* k, const void* 
   clear_error();
   return launch_status(run_fwd(d, a, st));
 }
+
+void set_error(const char* msg) { std::snprintf(tl_error, sizeof tl_error, "%s", msg); }
+}  // namespace kda
+
+extern "C" {
 
 kda_status kda_bwd(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
                    const void* beta, const float* init_state, const int32_t* cu_seqlens, const void* d_out,

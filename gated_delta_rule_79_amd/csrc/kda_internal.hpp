@@ -4,6 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kda.h"
 #include "kda_common.hpp"
 
 namespace kda {
@@ -91,6 +92,14 @@ void note_launch(const char* name);   // keeps the first failing launch of this 
     ::kda::note_launch(name);       \
     ::kda::timing_end(st);          \
   } while (0)
+
+// kda_fwd's host validation and dispatch (kda_api.cpp); `need`, when given, receives
+// the workspace bytes the problem needs (0 until the descriptor and shapes pass).
+kda_status fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const void* log_alpha,
+                       const void* beta, const float* init_state, void* out, float* final_state,
+                       const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream,
+                       size_t* need);
+void set_error(const char* msg);   // the text kda_last_error returns on this host thread
 
 hipError_t launch_chunk_map(const Args& a, hipStream_t st);
 int device_cus();                  // compute units of the current device

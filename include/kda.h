@@ -131,6 +131,22 @@ kda_status kda_fwd(const kda_desc *desc, const void *q, const void *k, const voi
                    void *out, float *final_state, const int32_t *cu_seqlens,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Forward pass for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as kda_fwd, without the workspace: the library
+ * takes it from a device array of KDA_NOALLOC_SCRATCH_BYTES that it holds on
+ * every GPU it runs on until the process ends (allocated when the library's
+ * device code is loaded on that GPU, never by this call).  A problem whose
+ * kda_workspace_bytes(desc, 0) exceeds that returns KDA_ERROR_WORKSPACE_TOO_SMALL
+ * with the sizes in kda_last_error(); KDA_FLAG_SAVE_FOR_BACKWARD is rejected
+ * (KDA_ERROR_INVALID_VALUE).  All calls on one GPU share the array: calls that
+ * may overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  The call enqueues on `stream` and allocates nothing. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+kda_status kda_fwd_noalloc(const kda_desc *desc, const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *beta, const float *init_state,
+                           void *out, float *final_state, const int32_t *cu_seqlens, void *stream);
+
 /* Backward pass: recomputes the forward internally, unless desc->flags has
  * KDA_FLAG_USE_SAVED (see above).  d_final_state may be NULL (zero);
  * d_init_state may be NULL (not written). */

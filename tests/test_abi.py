@@ -28,7 +28,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kda_bwd", "kda_decode", "kda_fwd", "kda_last_error",
+    assert declared_functions() == sorted(["kda_bwd", "kda_decode", "kda_fwd", "kda_fwd_noalloc", "kda_last_error",
                                           "kda_status_string",
                                           "kda_timing_enable", "kda_timing_read", "kda_workspace_bytes",
                                           "kda_conv_workspace_bytes", "kda_conv_fwd", "kda_conv_bwd",
