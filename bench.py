@@ -4,7 +4,9 @@
 One step = kda_fwd followed by kda_bwd (every kernel of the path) over one
 batch of seeded synthetic inputs already resident in HBM: the varlen workload
 of 8 packed sequences with lengths drawn from U[1K, 32K] (~128K tokens),
-H=16, dk=dv=128, bf16 inputs, fp32 states, fp32 outputs and gradients.
+H=16, dk=dv=128, bf16 inputs, fp32 states and accumulation, outputs and
+gradients stored in their primal's dtype (bf16; --out-dtype f32 stores them
+in fp32).
 
 Prints one JSON line: tokens/s for the whole step, the roofline of the
 dominant kernel (HIP-event durations recorded live around every launch of the
@@ -74,22 +76,16 @@ def _counter_rows(path):
 
 
 def _bools(name):
-    """Trailing bool template arguments of a kernel name (mangled 'Lb1E' or demangled 'true')."""
+    """Bool template arguments of a kernel name, in order: mangled 'Lb1E' and demangled 'true'
+    (rocprofv3 can print a name half-demangled, with both forms in it)."""
     import re
-    m = re.findall(r"Lb([01])E", name)
-    if m:
-        return [x == "1" for x in m]
-    return [x == "true" for x in re.findall(r"\b(true|false)\b", name)]
+    return [(m[0] == "1") if m[0] else (m[1] == "true") for m in re.findall(r"Lb([01])(?:E|(?=\)))|\b(true|false)\b", name)]
 
 
 def _ints(name):
-    """Integer template arguments of a kernel name (mangled 'Li64E' or demangled ', 64')."""
+    """Integer template arguments of a kernel name, in order: mangled 'Li64E' and demangled ', 64'."""
     import re
-    m = re.findall(r"Li(\d+)E", name)
-    if m:
-        return [int(x) for x in m]
-    inner = name[name.find("<") + 1:name.rfind(">")] if "<" in name else ""
-    return [int(x) for x in re.findall(r"(?:^|,)\s*(\d+)\s*(?=,|$)", inner)]
+    return [int(m[0] or m[1]) for m in re.findall(r"Li(\d+)E|(?:<|,)\s*(\d+)\s*(?=[,>])", name)]
 
 
 def _short_name(name, train=True):
@@ -103,7 +99,15 @@ def _short_name(name, train=True):
     if "kda_segment_scan" in name:
         return "kda_seg_scan"
     if "kda_bwd_chunk" in name:
-        return "kda_bwd_chunk"
+        # kda_bwd_chunk<E, O, DK, DV, QKN, PATH>: bf16 inputs run the flagged (steep) chunk-heads in
+        # a PATH 1 launch of their own; fp32 inputs run every chunk-head through PATH 1
+        ints = _ints(name)
+        steep = bool(ints) and ints[-1] == 1 and ("DF16b" in name or "bf16" in name or "__bf16" in name)
+        return "kda_bwd_chunk_steep" if steep else "kda_bwd_chunk"
+    if "kda_grad_absmax" in name:
+        return "kda_grad_absmax"
+    if "kda_grad_scale" in name:
+        return "kda_grad_scale"
     if "kda_chunk_map" in name:
         return "kda_chunk_map"
     if "kda_decode_step" in name:
@@ -112,7 +116,11 @@ def _short_name(name, train=True):
         if f"kda_conv_{k}_k" in name:
             return f"kda_conv_{k}"
     if "kda_prep" in name:
-        bwd = (_bools(name) or [False])[0]   # <..., BWD, QKN[, GATE]>
+        bwd = (_bools(name) or [False])[0]   # <..., BWD, QKN[, GATE][, PATH]>
+        if "kda_prep8" in name:
+            ints = _ints(name)
+            if ints and ints[-1] == 1:   # the 8-token-group walk over the flagged chunk-heads
+                return "kda_prep_steep"
         return ("kda_prep_save" if train else "kda_prep_bwd") if bwd else "kda_prep"
     if "kda_state" in name:
         # kda_state<E, O, DK, DV, DVS, OUT, SAVE, PF, MODE, UF>: the bools are OUT, SAVE, UF and the
@@ -286,7 +294,7 @@ def decode_bench(args, dev) -> int:
     B, T = (int(x) for x in args.decode.split(","))
     H, dk, dv = 16, 128, 128
     P = B
-    odt = torch.bfloat16 if args.out_bf16 else torch.float32
+    odt = torch.bfloat16 if (args.out_dtype == "bf16") else torch.float32
     print(f"[bench] decode inputs B={B} T={T}", file=sys.stderr, flush=True)
     inp = ki.decode_inputs(B, T, H, dk, dv, P, dtype="bf16", seed=99)
     idx_np = np.random.default_rng(99).permutation(P)[:B].astype(np.int32)
@@ -342,7 +350,7 @@ def decode_bench(args, dev) -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"decode_B{B}_T{T}", "sequences": B, "tokens_per_sequence": T, "H": H, "dk": dk,
-                   "dv": dv, "out_dtype": "bf16" if args.out_bf16 else "f32", "commit": "all tokens"},
+                   "dv": dv, "out_dtype": "bf16" if (args.out_dtype == "bf16") else "f32", "commit": "all tokens"},
         "roofline": roof, "kernels_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in kt.items()},
         "cpu_baseline": cpu,
     }
@@ -365,7 +373,7 @@ def conv_bench(args, dev) -> int:
     D, W = 6144, 4
     lengths = list(ki.config(4).lengths)
     tokens, N = int(sum(lengths)), len(lengths)
-    odt = torch.bfloat16 if args.out_bf16 else torch.float32
+    odt = torch.bfloat16 if (args.out_dtype == "bf16") else torch.float32
     print(f"[bench] conv inputs: {N} sequences, {tokens} tokens, D={D}, W={W}", file=sys.stderr, flush=True)
     c = ki.conv_inputs(lengths, D, W, dtype="bf16", seed=4)
     g = {n: torch.from_numpy(c[n]).to(dev, torch.bfloat16).unsqueeze(0) for n in ("x", "dy")}
@@ -435,7 +443,7 @@ def conv_bench(args, dev) -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl, "tokens": tokens, "sequences": N, "D": D, "W": W, "activation": "silu",
-                   "out_dtype": "bf16" if args.out_bf16 else "f32", "pass": "fwd+bwd"},
+                   "out_dtype": "bf16" if (args.out_dtype == "bf16") else "f32", "pass": "fwd+bwd"},
         "roofline": roof,
         "step_roofline": {"alg_bytes": int(step_bytes), "roofline_ms": round(step_bytes / HBM_PEAK_GBS / 1e6, 4),
                           "frac": round(step_bytes / HBM_PEAK_GBS / 1e6 / ms_step, 4), "bound": "hbm"},
@@ -460,7 +468,9 @@ def main() -> int:
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="skip the forward timings of the T = 4K, 32K and 128K single-sequence workloads that "
                          "the default training-step run adds under configs_fwd")
-    ap.add_argument("--out-bf16", action="store_true", help="bf16 outputs/gradients instead of fp32")
+    ap.add_argument("--out-dtype", choices=("bf16", "f32"), default="bf16",
+                    help="storage of outputs and gradients: the primal dtype (bf16, default) or fp32; states and "
+                         "accumulation are fp32 either way")
     ap.add_argument("--recompute", action="store_true",
                     help="self-contained backward (recomputes the forward) instead of the training step in which "
                          "the forward keeps the backward's intermediates")
@@ -548,7 +558,7 @@ def run_workload(args, dev, w, with_cpu, steps, warmup, force_fwd=False):
     inp = ki.make_inputs(w, with_grads=not fwd_only, raw=args.fused_prep)
     prep = dict(qk_l2norm=True, gate_logsigmoid=True) if args.fused_prep else {}
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    odt = torch.bfloat16 if args.out_bf16 else torch.float32
+    odt = torch.bfloat16 if (args.out_dtype == "bf16") else torch.float32
     t = {k: torch.from_numpy(inp[k]).to(dev, dt).unsqueeze(0) for k in ("q", "k", "v", "log_alpha", "beta")}
     init = torch.from_numpy(inp["init_state"]).to(dev) if inp["init_state"] is not None else None
     varlen = w.lengths is not None
@@ -660,7 +670,7 @@ def run_workload(args, dev, w, with_cpu, steps, warmup, force_fwd=False):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": tokens, "sequences": n_seqs, "H": w.H, "dk": w.dk, "dv": w.dv,
-                   "out_dtype": "bf16" if args.out_bf16 else "f32", "pass": "fwd" if fwd_only else "fwd+bwd",
+                   "out_dtype": "bf16" if (args.out_dtype == "bf16") else "f32", "pass": "fwd" if fwd_only else "fwd+bwd",
                    "backward": None if fwd_only else ("recomputes the forward" if args.recompute
                                                       else "uses the forward's saved intermediates"),
                    "input_prep": "fused (raw q, k, gate)" if args.fused_prep else "inputs already prepared"},

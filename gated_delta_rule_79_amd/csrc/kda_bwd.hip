@@ -344,7 +344,10 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
 // chunk-parallel gradients: one workgroup per chunk-head, 8 waves
 // ---------------------------------------------------------------------------
 // Wave w owns token tile tw = w & 3 (rows 16tw..16tw+15) and half hf = w >> 2
-// of the column tiles of every product it computes.
+// of the column tiles of every product it computes; over the key channels, that
+// half is the tiles 2 jj + hf (the even or the odd ones), so the two halves of
+// every pass jj cover 32 adjacent channels and a token row's gradient stores for
+// them land in one 64-byte segment.
 //
 // Phase A walks the value dimension in quarters of 32 columns and accumulates
 // the contractions over it (dAqk = scale tril(dO U^T), dT_U = dU V^T,
@@ -614,7 +617,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     }
 #pragma unroll
     for (int jj = 0; jj < NKH; ++jj) {
-      const int nt = hf * NKH + jj;
+      const int nt = 2 * jj + hf;
       const SFrag<OP> fs = sfrag_pair<OP>(sSh, sSl, L::LSV, 16 * nt + r16, kq);   // S split: it reaches dlog alpha
       accQ[jj] = mma_ps(fdo, fs, accQ[jj]);
       accW[jj] = mma_ss(fdu, fs, accW[jj]);
@@ -656,7 +659,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       put_split(sA1h, sA1l, rr * L::LDQ + cc, cc <= rr ? scale * accA[jj][ii] : 0.f);
     }
 #pragma unroll
-    for (int jj = 0; jj < NKH; ++jj) sDW[rr * L::LDO + 16 * (hf * NKH + jj) + r16] = cvt<OP>(-accW[jj][ii]);
+    for (int jj = 0; jj < NKH; ++jj) sDW[rr * L::LDO + 16 * (2 * jj + hf) + r16] = cvt<OP>(-accW[jj][ii]);
     if (r16 == 0) sBv[hf * CH + rr] = bv[ii];
   }
   {
@@ -741,12 +744,12 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   __syncthreads();
 
   // per-lane C-tile layout below: rows 16tw + 4q4 + ii, columns 16nt + r16
-  // ---- T^T dW (channel tiles of half hf) and rowsum(K+ * T^T dW)
+  // ---- T^T dW (channel tiles 2 jj + hf) and rowsum(K+ * T^T dW)
   f32x4 tdw[NKH];
   float dbeta[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < NKH; ++jj) {
-    const int nt = hf * NKH + jj;
+    const int nt = 2 * jj + hf;
     f32x4 x = zero4();
 #pragma unroll
     for (int k = 0; k < CH; k += 32)
@@ -813,7 +816,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   }
   __syncthreads();
 
-  // ---- per channel tile of half hf: gated products, then the assembly of dq, dk, dg.
+  // ---- per channel tile 2 jj + hf: gated products, then the assembly of dq, dk, dg.
   // PATH 0 (no 8-token span decaying past e^-STEEP_SPAN, see steep_block) uses one
   // reference row in the middle of each 16-row block and one product per step.
   // PATH 1 puts every decayed product e^{g_r - g_i} (i <= r) through reference rows
@@ -827,8 +830,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   // each tile is two products, one per 8-token group of its output rows, accumulated
   // into one tile with the other group's rows of the token-side operand zeroed.  A
   // chain factor below CHAIN_MIN makes the wave form those channel-side values as one
-  // exponential each instead.  One pass per channel tile: the pass's 32 channels (tile
-  // jj of both halves) get tables [channel][token] of the outer factors times q or k,
+  // exponential each instead.  One pass per channel tile: the pass's 32 channels (tiles
+  // 2 jj and 2 jj + 1) get tables [channel][token] of the outer factors times q or k,
   // so the usual operand is a 16-byte LDS row read and each exponential is taken once
   // per element.
   O* dqo = reinterpret_cast<O*>(a.dq) + (size_t)ci.t0 * rk + (size_t)h * DK;
@@ -862,7 +865,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     if (jj > 0) __syncthreads();   // the previous pass's table reads are done
     {
       const int cl = tid % TC, r0 = 4 * (tid / TC);
-      const int c = 16 * ((cl >> 4) * NKH + jj) + (cl & 15);   // channel tile jj of half cl >> 4
+      const int c = 32 * jj + cl;   // channel tiles 2 jj (cl < 16) and 2 jj + 1
       const float gm = sG[(PATH == 0 ? 16 * (r0 >> 4) + 8 : group_ref(r0 >> 3)) * L::LDG + c];
       float eq[4], ek[4], kr[4];
 #pragma unroll
@@ -880,7 +883,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       *reinterpret_cast<f32x4*>(tKR + cl * L::LDR + r0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
     }
     __syncthreads();
-    const int cl = 16 * hf + r16, cc = 16 * (hf * NKH + jj) + r16;
+    const int cl = 16 * hf + r16, cc = 16 * (2 * jj + hf) + r16;
     const int hh = q4 >> 1;   // group 2 tw + hh holds this lane's output rows 16 tw + 4 q4 + ii
     f32x4 dqg = zero4(), dkpg = zero4(), dkm = zero4();
     if constexpr (PATH == 0) {   // reference rows in the middle of 16-row blocks, one product per step
@@ -1042,11 +1045,11 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
   for (int jj = 0; jj < NKH; ++jj) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) sG[(16 * tw + 4 * q4 + ii) * L::LDG + 16 * (hf * NKH + jj) + r16] = dgv[jj][ii];
+    for (int ii = 0; ii < 4; ++ii) sG[(16 * tw + 4 * q4 + ii) * L::LDG + 16 * (2 * jj + hf) + r16] = dgv[jj][ii];
     float p = khs[jj];
     p += __shfl_xor(p, 16);
     p += __shfl_xor(p, 32);
-    if (q4 == 0) sRed[tw * DK + 16 * (hf * NKH + jj) + r16] = p;
+    if (q4 == 0) sRed[tw * DK + 16 * (2 * jj + hf) + r16] = p;
   }
   __syncthreads();
   if (tid < CH) {

@@ -564,11 +564,28 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   };
 
   // PATH 1 walks only the flagged items (the slots past the last chunk, never flagged
-  // by PATH 0, are empty and end the walk wherever they are met)
+  // by PATH 0, are empty and end the walk wherever they are met).  The work-group looks
+  // at 512 of its items at once: each thread reads one flag, and the first flagged one
+  // (wave ballots, then the lowest wave) is the next item.
   const int32_t* steep = a.steep;
+  __shared__ int sFirst[NT / 64];
   auto advance = [&](int it) __attribute__((always_inline)) {
-    if constexpr (PATH == 1)
-      while (it < n_items && steep[it] == 0) it += (int)gridDim.x;
+    if constexpr (PATH == 1) {
+      const long long G = gridDim.x;
+      while (it < n_items) {
+        const long long c = (long long)it + (long long)tid * G;
+        const unsigned long long b = __ballot(c < n_items && steep[c] != 0);
+        if (lane_id() == 0) sFirst[wave_id()] = b ? __ffsll((long long)b) - 1 : 64;
+        __syncthreads();
+        int first = -1;
+#pragma unroll
+        for (int ww = NT / 64 - 1; ww >= 0; --ww)
+          if (sFirst[ww] < 64) first = ww * 64 + sFirst[ww];
+        __syncthreads();
+        if (first >= 0) return (int)(it + first * G);
+        it = (int)std::min<long long>((long long)it + NT * G, n_items);
+      }
+    }
     return it;
   };
   int item = advance((int)blockIdx.x);
