@@ -37,11 +37,19 @@
  * Aliasing: final_state may alias init_state (each state slice is read before
  * it is written).  out and the gradient outputs must not overlap any input.
  *
- * Precision: all accumulation is fp32.  With bf16 inputs the products whose
- * rounding would reach the outputs (decayed Gram blocks, the state, U, and the
- * chunk matrices that multiply them) use a two-term bf16 split of the fp32
- * operand (x = hi + lo), so their error is that of fp32 operands; the rest use
- * plain bf16 operands.  A bf16 out_dtype rounds the results once at the end.
+ * Precision: all accumulation is fp32, and states are fp32.  With bf16 inputs
+ * the matrix products take fp16 operands (bf16 for the decayed factors); those
+ * whose rounding would reach the outputs or gradients beyond the bf16 error
+ * bound take a two-term split of the fp32 operand (x = hi + lo): the decayed
+ * Gram blocks, the states and U wherever they are multiplied, Kh and U in the
+ * training-mode state update, dS' and dU, and dT and Y in the backward's
+ * dA = -T^T dT T^T.  Their error is then that of fp32 operands.  The bf16
+ * backward multiplies d_out and d_final_state by a power of two that puts their
+ * largest magnitude in [0.5, 1) before anything is narrowed to fp16, and every
+ * gradient by its inverse (both exact), so the relative error does not depend on
+ * the scale of the upstream gradients.  fp32 inputs use fp32 operands; the
+ * in-chunk sums of log alpha are taken in fp64 and rounded to fp32 once.  A bf16
+ * out_dtype rounds the results once at the end.
  *
  * Errors: arguments are validated on the host before anything is enqueued; on
  * an error nothing is launched.  Launch failures return KDA_ERROR_LAUNCH.
@@ -110,8 +118,8 @@ typedef struct {
  * KDA_FLAG_QK_L2NORM: q and k arrive raw; each (token, head) row is scaled to
  *   x / sqrt(sum(x^2) + 1e-6) over the dk channels inside the kernels, and dq,
  *   dk are gradients with respect to the raw rows.  With bf16 inputs the
- *   normalised rows are rounded to bf16 once (as a separate bf16 normalisation
- *   pass would round them).
+ *   normalised rows are never rounded to bf16: every use multiplies the raw
+ *   row by its 1/|x|.
  * KDA_FLAG_GATE_LOGSIGMOID: log_alpha holds a raw gate x; the kernels use
  *   log alpha = logsigmoid(x) (alpha = sigmoid(x)), and dlog_alpha is the
  *   gradient with respect to x.
