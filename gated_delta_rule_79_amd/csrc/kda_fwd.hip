@@ -473,7 +473,8 @@ struct Prep8Lds {
   // once the Gram blocks are done, T and Te take the place of g, k and q
   static constexpr size_t T = 0;
   static constexpr size_t TE = T + (size_t)CH * LDA * 4;
-  static_assert(TE + (size_t)CH * LDT * 2 <= GKQ_END, "T, Te alias g, k, q");
+  static constexpr size_t TEL = TE + (size_t)CH * LDT * 2;    // lo half of Te (training mode)
+  static_assert(TEL + (size_t)CH * LDT * 2 <= GKQ_END, "T, Te alias g, k, q");
   static constexpr size_t KPT = GKQ_END;                      // fp16  [DK][LDT]
   static constexpr size_t VT = KPT + (size_t)DK * LDT * 2;    // fp16  [DV][LDT]
   static constexpr size_t A = VT + (size_t)DV * LDT * 2;      // float [CH][LDA]  beta * strict Gram
@@ -531,6 +532,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   E* sQ = reinterpret_cast<E*>(smem + L::Q);
   float* sT = reinterpret_cast<float*>(smem + L::T);
   OP* sTe = reinterpret_cast<OP*>(smem + L::TE);
+  OP* sTeL = reinterpret_cast<OP*>(smem + L::TEL);
   OP* sKpT = reinterpret_cast<OP*>(smem + L::KPT);
   OP* sVT = reinterpret_cast<OP*>(smem + L::VT);
   float* sA = reinterpret_cast<float*>(smem + L::A);
@@ -989,11 +991,16 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       __syncthreads();
     }
 
-    // ---- Te = T diag(beta) in fp16; W = Te K+, U~ = Te V
+    // ---- Te = T diag(beta) in fp16; W = Te K+, U~ = Te V.  In training mode Te is a
+    // split pair: W and U~ reach every saved state, whose rounding dlog alpha collects
     for (int o = tid; o < CH * CH / 4; o += NT) {
       const int rr = (4 * o) / CH, cc = (4 * o) % CH;
       const f32x4 t = *reinterpret_cast<const f32x4*>(sT + rr * L::LDA + cc);
-      store4<OP>(sTe + rr * L::LDT + cc, t[0] * sBeta[cc], t[1] * sBeta[cc + 1], t[2] * sBeta[cc + 2], t[3] * sBeta[cc + 3]);
+      const float t0 = t[0] * sBeta[cc], t1 = t[1] * sBeta[cc + 1], t2 = t[2] * sBeta[cc + 2], t3 = t[3] * sBeta[cc + 3];
+      if constexpr (BWD)
+        store4_split<OP>(sTe + rr * L::LDT + cc, sTeL + rr * L::LDT + cc, t0, t1, t2, t3);
+      else
+        store4<OP>(sTe + rr * L::LDT + cc, t0, t1, t2, t3);
       if constexpr (BWD)   // the backward uses T only as an MFMA operand
         store4<OP>(reinterpret_cast<OP*>(a.wsT) + blk * WB::TT + rr * CH + cc, t[0], t[1], t[2], t[3]);
     }
@@ -1003,9 +1010,12 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       constexpr int NTI = (CH / 16) * (DK / 16);
       for (int t = w; t < NTI; t += 8) {
         const int mt = t % (CH / 16), nt = t / (CH / 16);
-        const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sKpT, L::LDT, 16 * nt + rr, k); },
-                                      [&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); },
-                                      zero4());
+        f32x4 acc = zero4();
+        if constexpr (BWD)
+          acc = tile_mm_ps<OP, CH>(sKpT, L::LDT, 16 * nt, sTe, sTeL, L::LDT, 16 * mt);
+        else
+          acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sKpT, L::LDT, 16 * nt + rr, k); },
+                            [&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); }, acc);
         store4<OP>(wW + (16 * mt + r16) * DK + 16 * nt + 4 * q4, acc[0], acc[1], acc[2], acc[3]);
       }
       // U~ tiles: C[tok][dv]; lane holds 4 consecutive tokens of one value column -> U~^T rows
@@ -1013,9 +1023,16 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       constexpr int NTU = (CH / 16) * (DV / 16);
       for (int t = w; t < NTU; t += 8) {
         const int mt = t % (CH / 16), nt = t / (CH / 16);
-        const f32x4 acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); },
-                                      [&](int rr, int k) { return frag_row<OP>(sVT, L::LDT, 16 * nt + rr, k); },
-                                      zero4());
+        f32x4 acc = zero4();
+        if constexpr (BWD) {
+#pragma unroll
+          for (int k = 0; k < CH; k += 32)
+            acc = mma_sp(sfrag_pair<OP>(sTe, sTeL, L::LDT, 16 * mt + r16, k + 8 * q4),
+                         frag_row<OP>(sVT, L::LDT, 16 * nt + r16, k + 8 * q4), acc);
+        } else {
+          acc = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sTe, L::LDT, 16 * mt + rr, k); },
+                            [&](int rr, int k) { return frag_row<OP>(sVT, L::LDT, 16 * nt + rr, k); }, acc);
+        }
         if constexpr (BWD)
           *reinterpret_cast<f32x4*>(a.wsUtF + blk * WB::UTF + (16 * nt + r16) * CH + 16 * mt + 4 * q4) = acc;
         else
