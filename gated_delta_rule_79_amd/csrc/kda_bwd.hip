@@ -371,9 +371,8 @@ struct BwdLds {
   // phase A: quarters with the value column contiguous, so every MFMA operand
   // (contraction over the value dimension) is one 16-byte row read
   static constexpr int LSV = QC + PO;   // OP [DK][LSV] S, dS';  [CH][LSV] U, dU, dO, V
-  static constexpr size_t A_SH = 0;
-  static constexpr size_t A_SL = A_SH + (size_t)DK * LSV * OPB;
-  static constexpr size_t A_DSH = A_SL + (SPLIT ? (size_t)DK * LSV * OPB : 0);
+  static constexpr size_t A_SH = 0;                                  // S in the operand type
+  static constexpr size_t A_DSH = A_SH + (size_t)DK * LSV * OPB;      // dS' split (hi, lo)
   static constexpr size_t A_DSL = A_DSH + (size_t)DK * LSV * OPB;
   static constexpr size_t A_UH = A_DSL + (SPLIT ? (size_t)DK * LSV * OPB : 0);
   static constexpr size_t A_UL = A_UH + (size_t)CH * LSV * OPB;
@@ -464,7 +463,6 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const float scale = a.scale;
 
   OP* sSh = reinterpret_cast<OP*>(smem + L::A_SH);
-  OP* sSl = reinterpret_cast<OP*>(smem + L::A_SL);
   OP* sDSh = reinterpret_cast<OP*>(smem + L::A_DSH);
   OP* sDSl = reinterpret_cast<OP*>(smem + L::A_DSL);
   OP* sUh = reinterpret_cast<OP*>(smem + L::A_UH);
@@ -591,7 +589,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   for (int qq = 0; qq < NQ; ++qq) {
     const int cq = qq * QC;
     __syncthreads();  // the previous quarter's LDS reads are done
-    qs.s.template store_split<OP>(sSh, sSl, L::LSV);
+    qs.s.template store_cvt<OP>(sSh, L::LSV, DK);
     qs.ds.template store_split<OP>(sDSh, sDSl, L::LSV);
     qs.u.template store_split<OP>(sUh, sUl, L::LSV);
     qs.du.template store_split<OP>(sDUh, sDUl, L::LSV);
@@ -618,9 +616,11 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
     for (int jj = 0; jj < NKH; ++jj) {
       const int nt = 2 * jj + hf;
-      const SFrag<OP> fs = sfrag_pair<OP>(sSh, sSl, L::LSV, 16 * nt + r16, kq);   // S split: it reaches dlog alpha
-      accQ[jj] = mma_ps(fdo, fs, accQ[jj]);
-      accW[jj] = mma_ss(fdu, fs, accW[jj]);
+      // S in the operand type: these products tolerate its rounding (dGamma_C, which
+      // does not, comes from the fp32 registers above)
+      const Frag<OP> fs = frag_row<OP>(sSh, L::LSV, 16 * nt + r16, kq);
+      accQ[jj] = mma(fdo, fs, accQ[jj]);
+      accW[jj] = mma_sp(fdu, fs, accW[jj]);
       accK[jj] = mma_ss(fu, sfrag_pair<OP>(sDSh, sDSl, L::LSV, 16 * nt + r16, kq), accK[jj]);
     }
     __builtin_amdgcn_sched_barrier(0);
