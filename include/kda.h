@@ -104,7 +104,11 @@ typedef struct {
 
 /* kda_fwd: also leave in the workspace everything kda_bwd would recompute
  * (training step).  The workspace must then have kda_workspace_bytes(desc, 1)
- * bytes.  Not available where kda_bwd is not (fp32 inputs with dk = 128). */
+ * bytes.  Not available where kda_bwd is not (fp32 inputs with dk = 128).  With
+ * bf16 inputs this pass splits more of its operands than the forward-only pass
+ * (the states it keeps feed the gradients), so out and final_state can differ
+ * from a call without the flag in the last bits; both are within the same
+ * error bound. */
 #define KDA_FLAG_SAVE_FOR_BACKWARD 1
 /* kda_bwd: the workspace holds what a kda_fwd call with KDA_FLAG_SAVE_FOR_BACKWARD
  * left there, for the same descriptor, inputs (q, k, v, log_alpha, beta,
