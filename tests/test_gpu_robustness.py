@@ -220,3 +220,32 @@ def test_forward_value_scale(dtype, dk):
     errs = _errs(pairs)
     print(f"value scale 1e3 {dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL[dtype] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_hard_forget_through_the_fused_gate(dk, dv):
+    """Raw gates far below zero (x in [-1e4, -12] on runs of channels, so logsigmoid(x) ~ x is floored)
+    through the fused preparation (in-kernel L2 norm and logsigmoid), bf16, forward and backward, with
+    the gradients taken with respect to the raw inputs."""
+    import torch
+
+    import gated_delta_rule_79_amd as kda
+    import oracle
+    w = ki.small(dtype="bf16", lengths=(260, 1, 130), H=2, dk=dk, dv=dv, seed=36)
+    inp = ki.make_inputs(w, with_grads=True, raw=True)
+    inp = _hard_forget(inp, "bf16", seed=10)   # the raw gate takes the hard-forget runs
+    g = to_gpu(inp, "bf16")
+    prep = dict(qk_l2norm=True, gate_logsigmoid=True)
+    o, f = gpu_fwd(g, **prep)
+    grads = gpu_bwd(g, **prep)
+    torch.cuda.synchronize()
+    ro, rf = oracle.kda_fwd_prepped(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"],
+                                    init_state=inp["init_state"])
+    rg = oracle.kda_bwd_prepped(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["cu_seqlens"],
+                                inp["d_out"], init_state=inp["init_state"], d_final_state=inp["d_final_state"])
+    pairs = {"o": (np_of(o)[0], ro), "final": (np_of(f), rf)}
+    for name, a, b in zip(GRADS, grads, rg):
+        pairs[name] = (np_of(a)[0] if name != "d_init" else np_of(a), b)
+    errs = _errs(pairs)
+    print(f"hard forget, fused gate {dk}x{dv}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
