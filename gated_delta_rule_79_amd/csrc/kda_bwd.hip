@@ -1089,7 +1089,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     }
   }
   if constexpr (qk_norm) {
-    // d x = (1/|x|) (d x^ - x^ (x^ . d x^)) for the raw q and k rows
+    // d x = (1/|x|) (d x^ - x^ (x^ . d x^)) for the raw q and k rows (unrolled, so the
+    // loads of dq^, dk^ are all in flight together)
+#pragma unroll
     for (int o = tid; o < 2 * CH * DK / 4; o += NT) {
       const int which = o / (CH * DK / 4), e = 4 * (o % (CH * DK / 4));
       const int rr = e / DK, c0 = e % DK;
