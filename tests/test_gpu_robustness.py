@@ -45,7 +45,7 @@ def _hard_forget(inp, dtype, seed, frac=0.15, with_inf=False):
     for h in range(H):
         for c in rng.choice(dk, size=max(1, int(frac * dk)), replace=False):
             for _ in range(int(rng.integers(1, 5))):
-                L = int(rng.integers(1, 25))
+                L = min(int(rng.integers(1, 25)), n)   # a run never outgrows a short input
                 t0 = int(rng.integers(0, max(1, n - L)))
                 la[t0:t0 + L, h, c] = -np.exp(rng.uniform(np.log(12.0), np.log(1e4), size=L))
                 if with_inf and rng.random() < 0.3:
