@@ -414,7 +414,7 @@ struct BwdLds {
   static constexpr size_t NRM = DBP + 2 * CH * 4;                     // float [2][CH] 1/|q_r|, 1/|k_r| (qk_norm)
   static constexpr size_t NDOT = NRM + 2 * CH * 4;                    // float [2][2][CH] q^.dq^, k^.dk^ halves
   static constexpr size_t END0 = NDOT + 4 * CH * 4;
-  static constexpr size_t Y = DW;                                     // OP hi, lo [CH][LDT] (dW, K+ dead by then)
+  static constexpr size_t Y = DW;                                     // OP hi, lo [CH][LDT] Y^T (dW, K+ dead by then)
   static constexpr size_t YL = Y + (size_t)CH * LDT * OPB;
   static_assert(2 * (size_t)CH * LDT <= 2 * (size_t)CH * LDO, "split Y fits in the dW and K+ regions");
   // gated products, per pass of 32 channels: fp32 tables [channel][token] of
@@ -538,6 +538,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   // Gamma_C of the channel whose dg_C this thread finishes in the tail (read now:
   // a load issued after the gradient stores would wait for them to drain)
   const float gam_c = (tid >= 64 && tid < 64 + DK) ? a.wsGam[blk * WB::GAM + tid - 64] : 0.f;
+  // beta of row tid, issued ahead of the tile loads so that waiting for it does not wait for them
+  const float beta_t = (tid < CH && tid < len) ? f32(bh[(size_t)tid * H]) : 0.f;
 
   // ---- phase A staging: contractions over the value dimension, a quarter of the columns at a time
   struct QStage {
@@ -545,8 +547,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     TileCopy<float, CH, QC, NT> u, du;
     TileCopy<E, CH, QC, NT> dov, vv;
   };
-  QStage qs;
-  auto qload = [&](int qq) __attribute__((always_inline)) {
+  // two quarters in flight: quarter qq sits in stage qq % 2
+  QStage qst[2];
+  auto qload = [&](QStage& qs, int qq) __attribute__((always_inline)) {
     const int cq = qq * QC;
     qs.s.load(gS + cq, DV);
     qs.ds.load(gdS + cq, DV);
@@ -560,7 +563,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   {
     TileCopy<OP, CH, CH, NT> tt;
     tt.load(gT, CH);
-    qload(0);
+    qload(qst[0], 0);
+    if (NQ > 1) qload(qst[1], 1);
     constexpr int EPV = 16 / (int)sizeof(OP);
     static_for<0, decltype(tt)::PER>([&](auto I) __attribute__((always_inline)) {
       const int v = tid + I * NT;
@@ -572,7 +576,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       }
     });
   }
-  if (tid < CH) sBeta[tid] = tid < len ? f32(bh[(size_t)tid * H]) : 0.f;
+  if (tid < CH) sBeta[tid] = beta_t;
 
   // ---- phase A
   f32x4 accA[2], accT[2], accQ[NKH], accK[NKH], accW[NKH];
@@ -586,8 +590,10 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
   for (int i = 0; i < GPER; ++i) gp[i] = 0.f;
 
+#pragma unroll
   for (int qq = 0; qq < NQ; ++qq) {
     const int cq = qq * QC;
+    QStage& qs = qst[qq & 1];
     __syncthreads();  // the previous quarter's LDS reads are done
     qs.s.template store_cvt<OP>(sSh, L::LSV, DK);
     qs.ds.template store_split<OP>(sDSh, sDSl, L::LSV);
@@ -602,7 +608,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       const float* y = reinterpret_cast<const float*>(&qs.ds.r[I]);
       gp[I] += (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
     });
-    if (qq + 1 < NQ) qload(qq + 1);
+    if (qq + 2 < NQ) qload(qs, qq + 2);
     __syncthreads();
     const Frag<OP> fdo = frag_row<OP>(sDO, L::LSV, 16 * tw + r16, kq);
     const SFrag<OP> fdu = sfrag_pair<OP>(sDUh, sDUl, L::LSV, 16 * tw + r16, kq);
@@ -789,12 +795,19 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       for (int u = 0; u < 8; ++u) y8[u] = sA2[(16 * tw + r16) * L::LDA + k + kq + u];
       x = mma_sp(sfrag_from<OP>(y8), frag_col<OP>(sTT, L::LDT, 16 * nt + r16, k + kq), x);
     }
+    // stored transposed (Y^T[col][row]): this lane's four rows are one 8-byte run, and dA
+    // below reads Y's columns as rows
+    {
+      OP hi[4], lo[4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int o = (16 * tw + 4 * q4 + ii) * L::LDT + 16 * nt + r16;
-      const OP hi = cvt<OP>(x[ii]);
-      sY[o] = hi;
-      if constexpr (L::SPLIT) sYl[o] = cvt<OP>(x[ii] - f32(hi));
+      for (int ii = 0; ii < 4; ++ii) {
+        hi[ii] = cvt<OP>(x[ii]);
+        lo[ii] = cvt<OP>(x[ii] - f32(hi[ii]));
+      }
+      using V4 = typename std::conditional<sizeof(OP) == 2, uint2, uint4>::type;   // four OP values
+      const int o = (16 * nt + r16) * L::LDT + 16 * tw + 4 * q4;
+      *reinterpret_cast<V4*>(sY + o) = *reinterpret_cast<const V4*>(hi);
+      if constexpr (L::SPLIT) *reinterpret_cast<V4*>(sYl + o) = *reinterpret_cast<const V4*>(lo);
     }
   }
   __syncthreads();
@@ -805,7 +818,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     f32x4 x = zero4();
 #pragma unroll
     for (int k = 0; k < CH; k += 32)
-      x = mma_ps(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq), sfrag_col_pair<OP>(sY, sYl, L::LDT, 16 * nt + r16, k + kq), x);
+      x = mma_ps(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq), sfrag_pair<OP>(sY, sYl, L::LDT, 16 * nt + r16, k + kq), x);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = 16 * tw + 4 * q4 + ii, cc = 16 * nt + r16;
@@ -914,13 +927,13 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         const SE* aL = useq ? sA1l : sA2l;
         const float* bT = useq ? tQ : tK;
         for (int ab = b; ab < 4; ++ab) {
+          // block ab's reference factor goes into the channel-side operand, so the blocks
+          // accumulate in the matrix core
           const int rbase = 16 * ab + 8 * (q4 & 1);
-          float xb[8];
-          scaled(bT, cl, rbase, 1.f, xb);
-          const f32x4 y = mma_ss(sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase), sfrag_from<SE>(xb), zero4());
           const float f = ab == b ? 1.f : __expf(sG[(16 * ab + 8) * L::LDG + cc] - gmb);
-  #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) dkm[ii] += f * y[ii];
+          float xb[8];
+          scaled(bT, cl, rbase, f, xb);
+          dkm = mma_ss(sfrag_col_pair<SE>(aH, aL, L::LDQ, 16 * b + r16, rbase), sfrag_from<SE>(xb), dkm);
         }
   #pragma unroll
         for (int ii = 0; ii < 4; ++ii) dkm[ii] *= __expf(gmb - sG[(16 * b + 4 * q4 + ii) * L::LDG + cc]);
@@ -1015,6 +1028,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       }
     }
   }
+  // the raw gate values of the rows this thread finishes in the reverse sum below (channel
+  // tid % DK, rows of part tid / DK), all issued now so that their latency overlaps the
+  // reductions; rows past the chunk read the last row and are not stored
+  E xlr[RPS];
+  {
+    const int c = tid % DK, s = tid / DK;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) xlr[u] = lh[(size_t)min(s * RPS + u, len - 1) * rk + c];
+  }
   // dbeta partials: reduce over the 16 column lanes; halves meet in LDS
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
@@ -1078,11 +1100,12 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     float acc = 0.f;
     for (int s2 = s + 1; s2 < NSPLIT; ++s2) acc += sRed[s2 * DK + c];
 #pragma unroll
-    for (int rr = (s + 1) * RPS - 1; rr >= s * RPS; --rr) {
+    for (int u = RPS - 1; u >= 0; --u) {
+      const int rr = s * RPS + u;
       acc += sG[rr * L::LDG + c];
       if (rr < len) {
         // through the gate's map and the floor of log alpha (flat below it)
-        const float x = f32(lh[(size_t)rr * rk + c]);
+        const float x = f32(xlr[u]);
         const float d = gs_inv * (a.gate_ls ? acc * sigmoid_neg(x) : acc);
         dlo[(size_t)rr * rk + c] = cvt<O>(above_floor(a.gate_ls ? logsigmoid(x) : x) ? d : 0.f);
       }
