@@ -640,12 +640,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * tw + 4 * q4 + ii, col = 16 * hf + r16;
-        float p = f32(sV[r * L::LSV + col]) * x[ii];
-        p += __shfl_xor(p, 1);
-        p += __shfl_xor(p, 2);
-        p += __shfl_xor(p, 4);
-        p += __shfl_xor(p, 8);
-        bv[ii] += p;
+        bv[ii] += f32(sV[r * L::LSV + col]) * x[ii];   // reduced over the column lanes after phase A
         if (r < len) gdV[(size_t)r * rv + cq + col] = cvt<O>(gs_inv * (sBeta[r] * x[ii]));
       }
     }
@@ -666,15 +661,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     }
 #pragma unroll
     for (int jj = 0; jj < NKH; ++jj) sDW[rr * L::LDO + 16 * (2 * jj + hf) + r16] = cvt<OP>(-accW[jj][ii]);
-    if (r16 == 0) sBv[hf * CH + rr] = bv[ii];
+    const float p = lane_sum16(bv[ii]);
+    if (r16 == 0) sBv[hf * CH + rr] = p;
   }
   {
     // a row's QC / 4 column pieces sit in consecutive lanes
     constexpr int VPR = QC / 4;
     static_for<0, GPER>([&](auto I) __attribute__((always_inline)) {
-      float p = gp[I];
-#pragma unroll
-      for (int m = 1; m < VPR; m <<= 1) p += __shfl_xor(p, m);
+      static_assert(VPR == 8, "a row's pieces fill one half-row of lanes");
+      const float p = lane_sum8(gp[I]);
       const int v = tid + I * NT;
       if (v % VPR == 0 && v < DK * VPR) sDGam[v / VPR] = p;
     });
@@ -1040,22 +1035,13 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   // dbeta partials: reduce over the 16 column lanes; halves meet in LDS
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
-    float p = dbeta[ii];
-    p += __shfl_xor(p, 1);
-    p += __shfl_xor(p, 2);
-    p += __shfl_xor(p, 4);
-    p += __shfl_xor(p, 8);
+    const float p = lane_sum16(dbeta[ii]);
     if (r16 == 0) sDbp[hf * CH + 16 * tw + 4 * q4 + ii] = p;
   }
   if constexpr (qk_norm) {   // row dots: reduce over the 16 column lanes; halves meet in LDS
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      float pq = qdot[ii], pk = kdot[ii];
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        pq += __shfl_xor(pq, m);
-        pk += __shfl_xor(pk, m);
-      }
+      const float pq = lane_sum16(qdot[ii]), pk = lane_sum16(kdot[ii]);
       if (r16 == 0) {
         sDot[hf * CH + 16 * tw + 4 * q4 + ii] = pq;
         sDot[2 * CH + hf * CH + 16 * tw + 4 * q4 + ii] = pk;

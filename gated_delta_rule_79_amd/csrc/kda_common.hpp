@@ -56,6 +56,26 @@ template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 cvt<bf16>(float x) { return (bf16)x; }  // RNE
 template <> __device__ __forceinline__ f16 cvt<f16>(float x) { return (f16)x; }     // RNE
 
+// Sums over aligned groups of 8 or 16 consecutive lanes, every lane of the group
+// receiving the group's total.  DPP lane permutes inside a 16-lane row (swap
+// neighbours, swap pairs, mirror each half-row, mirror the row) are plain vector ALU
+// operations, where a shuffle would go through the LDS crossbar; every lane of the wave
+// must be active.
+template <int CTRL> __device__ __forceinline__ float dpp_take(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_sum8(float v) {
+  v += dpp_take<0xB1>(v);    // quad_perm [1, 0, 3, 2]: lane ^ 1
+  v += dpp_take<0x4E>(v);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+  v += dpp_take<0x141>(v);   // row_half_mirror: lane i <-> 7 - i, so each quad meets the other
+  return v;
+}
+__device__ __forceinline__ float lane_sum16(float v) {
+  v = lane_sum8(v);
+  v += dpp_take<0x140>(v);   // row_mirror: lane i <-> 15 - i, so each half-row meets the other
+  return v;
+}
+
 // Row padding of LDS arrays, in elements (16 bytes).
 template <typename E> constexpr int PADE = 16 / (int)sizeof(E);
 
