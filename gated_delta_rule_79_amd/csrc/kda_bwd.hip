@@ -428,8 +428,21 @@ struct BwdLds {
   static constexpr size_t TQ = TAB_REUSE ? DW : END0;
   static constexpr size_t TK = TQ + TAB1;
   static constexpr size_t KR = TK + TAB1;
-  static constexpr size_t BYTES = TAB_REUSE ? END0 : END0 + TAB_SZ;
+  static constexpr size_t BYTES1 = TAB_REUSE ? END0 : END0 + TAB_SZ;
+  // a second table set, so the next pass's tables are built while the current pass reads
+  // its own: T^T's block (dead after dA) holds one table; the rest go into the dW and K+
+  // regions past the first set (or into them, when the first set follows the rest), and
+  // what is left past the end of the layout
+  static constexpr size_t DWKP = 2 * (size_t)CH * LDO * OPB;   // dW and K+ regions together
+  static constexpr size_t TQ2 = T;
+  static constexpr size_t TK2 = TAB_REUSE ? DW + TAB_SZ : DW;
+  static constexpr size_t KR2 = TAB_REUSE ? (DW + TAB_SZ + TAB1 <= DW + DWKP ? BYTES1 : 0) : DW + TAB1;
+  static constexpr size_t BYTES2 = TAB_REUSE ? BYTES1 + TAB1 : BYTES1;
+  static constexpr bool TDB = (size_t)CH * LDT * OPB >= TAB1 && BYTES2 <= 163840 &&
+                              (TAB_REUSE ? DW + TAB_SZ + TAB1 <= DW + DWKP : 2 * TAB1 <= DWKP);
+  static constexpr size_t BYTES = TDB ? BYTES2 : BYTES1;
   static_assert(KR % 16 == 0 && TK % 16 == 0 && TQ % 16 == 0, "table rows stay 16-byte aligned");
+  static_assert(KR2 % 16 == 0 && TK2 % 16 == 0 && TQ2 % 16 == 0, "table rows stay 16-byte aligned");
   static_assert(BYTES <= 163840, "backward chunk kernel LDS");
   static_assert(RED % 8 == 0, "fp64 scan partials stay 8-byte aligned");
   static_assert(A_END % 16 == 0 && B_END % 16 == 0, "LDS regions stay 16-byte aligned");
@@ -484,6 +497,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   float* tQ = reinterpret_cast<float*>(smem + L::TQ);
   float* tK = reinterpret_cast<float*>(smem + L::TK);
   float* tKR = reinterpret_cast<float*>(smem + L::KR);
+  float* tQ2 = reinterpret_cast<float*>(smem + L::TQ2);   // second set (used when L::TDB)
+  float* tK2 = reinterpret_cast<float*>(smem + L::TK2);
+  float* tKR2 = reinterpret_cast<float*>(smem + L::KR2);
   // x as a split pair hi + lo (hi only on the fp32 path)
   auto put_split = [&](SE* hi, SE* lo, int idx, float x) __attribute__((always_inline)) {
     if constexpr (L::SSPLIT) {
@@ -867,10 +883,8 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       x[u + 4] = v1[u] * f;
     }
   };
-  // (dk = 128 keeps the pass loop rolled: unrolled, it no longer fits the registers)
-#pragma unroll(DK == 128 ? 1 : NKH)
-  for (int jj = 0; jj < NKH; ++jj) {
-    if (jj > 0) __syncthreads();   // the previous pass's table reads are done
+  // the tables of pass jj: one thread per (channel, 4 tokens)
+  auto build_tables = [&](int jj, float* tq, float* tk, float* tkr) __attribute__((always_inline)) {
     {
       const int cl = tid % TC, r0 = 4 * (tid / TC);
       const int c = 32 * jj + cl;   // channel tiles 2 jj (cl < 16) and 2 jj + 1
@@ -886,11 +900,25 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         ek[u] = kv * e;
         kr[u] = kv * __expf(gm - g);
       }
-      *reinterpret_cast<f32x4*>(tQ + cl * L::LDR + r0) = f32x4{eq[0], eq[1], eq[2], eq[3]};
-      *reinterpret_cast<f32x4*>(tK + cl * L::LDR + r0) = f32x4{ek[0], ek[1], ek[2], ek[3]};
-      *reinterpret_cast<f32x4*>(tKR + cl * L::LDR + r0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+      *reinterpret_cast<f32x4*>(tq + cl * L::LDR + r0) = f32x4{eq[0], eq[1], eq[2], eq[3]};
+      *reinterpret_cast<f32x4*>(tk + cl * L::LDR + r0) = f32x4{ek[0], ek[1], ek[2], ek[3]};
+      *reinterpret_cast<f32x4*>(tkr + cl * L::LDR + r0) = f32x4{kr[0], kr[1], kr[2], kr[3]};
     }
-    __syncthreads();
+  };
+  build_tables(0, tQ, tK, tKR);
+  __syncthreads();
+  // (dk = 128 keeps the pass loop rolled: unrolled, it no longer fits the registers)
+#pragma unroll(DK == 128 ? 1 : NKH)
+  for (int jj = 0; jj < NKH; ++jj) {
+    // with two table sets, pass jj reads set jj % 2 while it builds the next pass's
+    // tables in the other (last read by pass jj - 1, which every wave has finished)
+    const bool odd = L::TDB && (jj & 1);
+    const float* cQ = odd ? tQ2 : tQ;
+    const float* cK = odd ? tK2 : tK;
+    const float* cKR = odd ? tKR2 : tKR;
+    if constexpr (L::TDB) {
+      if (jj + 1 < NKH) build_tables(jj + 1, odd ? tQ : tQ2, odd ? tK : tK2, odd ? tKR : tKR2);
+    }
     const int cl = 16 * hf + r16, cc = 16 * (2 * jj + hf) + r16;
     const int hh = q4 >> 1;   // group 2 tw + hh holds this lane's output rows 16 tw + 4 q4 + ii
     f32x4 dqg = zero4(), dkpg = zero4(), dkm = zero4();
@@ -902,7 +930,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
           const int i0 = k + kq, bb = i0 >> 4;
           const float f = i0 >= kmax ? 0.f : (bb == ab ? 1.f : __expf(gma - sG[(16 * bb + 8) * L::LDG + cc]));
           float xr[8];
-          scaled(tKR, cl, i0, f, xr);
+          scaled(cKR, cl, i0, f, xr);
           const SFrag<SE> fr = sfrag_from<SE>(xr);
           dqg = mma_ss(sfrag_pair<SE>(sA1h, sA1l, L::LDQ, 16 * ab + r16, k + kq), fr, dqg);
           dkpg = mma_ss(sfrag_pair<SE>(sA2h, sA2l, L::LDQ, 16 * ab + r16, k + kq), fr, dkpg);
@@ -920,7 +948,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         const bool useq = q4 < 2;
         const SE* aH = useq ? sA1h : sA2h;
         const SE* aL = useq ? sA1l : sA2l;
-        const float* bT = useq ? tQ : tK;
+        const float* bT = useq ? cQ : cK;
         for (int ab = b; ab < 4; ++ab) {
           // block ab's reference factor goes into the channel-side operand, so the blocks
           // accumulate in the matrix core
@@ -943,7 +971,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
             const int R = 2 * ab + g2;
             const float f = chain(R, C, cc);   // zero past the diagonal block
             float xr[8];
-            scaled(tKR, cl, i0, f, xr);
+            scaled(cKR, cl, i0, f, xr);
             if (__any(C < R && f < CHAIN_MIN) && C < R) {   // k_i e^{g_m(R) - g_i}, one exponential each
               const float gmr = sG[group_ref(R) * L::LDG + cc];
   #pragma unroll
@@ -970,7 +998,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         const bool useq = q4 < 2;
         const SE* aH = useq ? sA1h : sA2h;
         const SE* aL = useq ? sA1l : sA2l;
-        const float* bT = useq ? tQ : tK;
+        const float* bT = useq ? cQ : cK;
         for (int ab = b; ab < 4; ++ab) {
           const int rbase = 16 * ab + 8 * (q4 & 1), R = rbase >> 3;   // this lane's 8 rows form group R
   #pragma unroll 1
@@ -1021,6 +1049,13 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
           dko[(size_t)rr * rk + cc] = cvt<O>(gs_inv * dkt);
         }
       }
+    }
+    if (jj + 1 < NKH) {
+      if constexpr (!L::TDB) {   // one set: the pass's table reads end before the next build
+        __syncthreads();
+        build_tables(jj + 1, tQ, tK, tKR);
+      }
+      __syncthreads();   // the next pass's tables are complete
     }
   }
   // the raw gate values of the rows this thread finishes in the reverse sum below (channel
