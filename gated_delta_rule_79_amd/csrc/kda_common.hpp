@@ -76,6 +76,42 @@ __device__ __forceinline__ float lane_sum16(float v) {
   return v;
 }
 
+// 4x4 transpose across each quad of lanes (lanes 4g .. 4g + 3): lane 4g + c holds
+// x[r] = M[r][c] and receives x[c] = M[lane & 3][c].  Two exchange stages, across lane ^ 1
+// and lane ^ 2, each trade the two values whose register bit differs from the lane bit.
+// Used to turn an MFMA output tile (a lane holds four rows of one column) into four
+// consecutive columns of one row for a 16-byte store.  Every lane of the wave must be active.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
+  const int i = (int)threadIdx.x & 3;
+  {
+    const bool odd = i & 1;
+    float s0 = odd ? x[0] : x[1], s1 = odd ? x[2] : x[3];
+    s0 = dpp_take<0xB1>(s0);   // lane ^ 1
+    s1 = dpp_take<0xB1>(s1);
+    if (odd) {
+      x[0] = s0;
+      x[2] = s1;
+    } else {
+      x[1] = s0;
+      x[3] = s1;
+    }
+  }
+  {
+    const bool hi = i & 2;
+    float s0 = hi ? x[0] : x[2], s1 = hi ? x[1] : x[3];
+    s0 = dpp_take<0x4E>(s0);   // lane ^ 2
+    s1 = dpp_take<0x4E>(s1);
+    if (hi) {
+      x[0] = s0;
+      x[1] = s1;
+    } else {
+      x[2] = s0;
+      x[3] = s1;
+    }
+  }
+  return x;
+}
+
 // Row padding of LDS arrays, in elements (16 bytes).
 template <typename E> constexpr int PADE = 16 / (int)sizeof(E);
 

@@ -1217,10 +1217,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       if (t < NST) {
         store4<OP>(sST + (16 * nt + r16) * L::LDK + 16 * mt + 4 * q4, S[i][0], S[i][1], S[i][2], S[i][3]);
         if constexpr (SAVE) {
-          // backward needs the state entering every chunk: fp32 [DK][DV] per chunk-head
-          float* dst = gS + blk_of(n) * WB::S + (size_t)(16 * mt + 4 * q4) * DV + n0 + 16 * nt + r16;
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = S[i][ii];
+          // backward needs the state entering every chunk: fp32 [DK][DV] per chunk-head; after
+          // a quad transpose a lane stores 4 columns of row 16 mt + 4 q4 + (r16 & 3)
+          const int g4 = r16 & ~3, ri = r16 & 3;
+          *reinterpret_cast<f32x4*>(gS + blk_of(n) * WB::S + (size_t)(16 * mt + 4 * q4 + ri) * DV + n0 + 16 * nt + g4) =
+              quad_transpose(S[i]);
         }
       }
     }
@@ -1242,10 +1243,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
         else
           store4<OP>(sUL + uo, ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]);
         if constexpr (SAVE) {
-          // and U in fp32, token-major [CH][DV]
-          float* dst = gU + blk_of(n) * WB::U + (size_t)(16 * w + 4 * q4) * DV + n0 + 16 * nt + r16;
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) dst[(size_t)ii * DV] = ut[ii] - x[ii];
+          // and U in fp32, token-major [CH][DV] (quad transpose, as S above)
+          const int g4 = r16 & ~3, ri = r16 & 3;
+          *reinterpret_cast<f32x4*>(gU + blk_of(n) * WB::U + (size_t)(16 * w + 4 * q4 + ri) * DV + n0 + 16 * nt + g4) =
+              quad_transpose(f32x4{ut[0] - x[0], ut[1] - x[1], ut[2] - x[2], ut[3] - x[3]});
         }
       }
     } else if constexpr (OUT) {
@@ -1266,11 +1267,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
           const f32x4 x =
               tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sAqk, L::LDT, 16 * tt + rr, k); },
                           [&](int rr, int k) { return frag_row<OP>(sUL, L::LDT, 16 * nt + rr, k); }, o1[nt]);
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int tok = 16 * tt + 4 * q4 + ii;
-            if (tok < clen) oh[(size_t)tok * ro + 16 * nt + r16] = cvt<O>(scale * x[ii]);
-          }
+          // quad transpose: this lane stores 4 columns of token 16 tt + 4 q4 + (r16 & 3)
+          const f32x4 y = quad_transpose(scale * x);
+          const int tok = 16 * tt + 4 * q4 + (r16 & 3);
+          if (tok < clen) store4<O>(oh + (size_t)tok * ro + 16 * nt + (r16 & ~3), y[0], y[1], y[2], y[3]);
         }
       }
     }
