@@ -237,7 +237,6 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   };
 
   auto chunk = [&](int n, Stage& ld, const Stage& nx) __attribute__((always_inline)) {
-    stage_load(ld, max(n - 2, 0));
     // dS' (gradient of the state leaving chunk n) -> LDS split, and -> workspace fp32
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -253,6 +252,9 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
       }
     }
     __syncthreads();
+    // chunk n - 2 -> registers, issued after this step's dS' stores: stores issued behind
+    // the loads would wait for them in the memory queue
+    stage_load(ld, max(n - 2, 0));
 
     // dU = scale Aqk^T dO + Kh dS' : tiles (token tile tt, value tile nt) dealt to all eight waves
     constexpr int NDU = 4 * NTS, DPW = (NDU + 7) / 8;

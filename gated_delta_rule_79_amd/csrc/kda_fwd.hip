@@ -1165,9 +1165,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
     }
   }
 
-  // Staging registers: two sets, so chunk n+2 is in flight while chunk n+1
-  // waits in registers and chunk n is in LDS (loads of two chunks overlap the
-  // compute of one).  Separate objects of a native vector type stay in VGPRs.
+  // Staging registers: chunk n + PF is loaded while chunk n is in LDS.  With PF = 2
+  // (a build option) a second set lets chunk n + 2 be in flight while chunk n + 1
+  // waits in registers; the default PF = 1 measures as fast.  Separate objects of a
+  // native vector type stay in VGPRs.
   struct Stage {
     TileCopy<OP, CH, DK, NT> w;
     TileCopy<OP, (OUT ? CH : 1), (OUT ? DK : 16 / sizeof(OP)), NT> qt;
@@ -1208,8 +1209,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   // one chunk: LDS holds chunk n; `ld` receives chunk n+PF (clamped, so its
   // registers are always defined); `nx` holds chunk n+1 and goes to LDS at the end
   auto chunk = [&](int n, Stage& ld, const Stage& nx) __attribute__((always_inline)) {
-    stage_load(ld, min(n + PF, nch - 1));
-
     // S -> LDS in the operand type, transposed ([column][channel])
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -1256,6 +1255,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
                              [&](int rr, int k) { return frag_row<OP>(sST, L::LDK, 16 * nt + rr, k); }, zero4());
     }
     __syncthreads();
+    // chunk n + PF -> registers, issued after this step's S and U stores: stores issued
+    // behind the loads would wait for them in the memory queue
+    stage_load(ld, min(n + PF, nch - 1));
 
     if constexpr (OUT) {
       if (w >= 4) {
