@@ -354,9 +354,9 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
 // Phase A walks the value dimension in quarters of 32 columns and accumulates
 // the contractions over it (dAqk = scale tril(dO U^T), dT_U = dU V^T,
 // dQS = dO S^T, dKh = U dS'^T, dW = -dU S^T), writes dV = beta T^T dU, and
-// the value sums of V * T^T dU (for dbeta) and dS' * S (dGamma_C).  The
-// quarter after the current one is loaded into registers while the current
-// one is multiplied.
+// the value sums of V * T^T dU (for dbeta) and dS' * S (dGamma_C).  Two
+// quarters are in flight: the one after next is loaded into registers while the
+// current one is multiplied.
 //
 // Phase B works over tokens and channels: T^T dW, dT, dA = -strict(T^T dT T^T),
 // the gated products with per-block reference rows, and the assembly of dq,
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   const float gs = a.gscale ? a.gscale[0] : 1.f;
   const float gs_inv = a.gscale ? a.gscale[1] : 1.f;
 
-  // phase B's inputs (q, k, log_alpha rows), loaded after phase A
+  // phase B's inputs (q, k, log_alpha rows), loaded during the last value quarter
   TileCopy<E, CH, DK, NT> pk, pq, pl;
   // Gamma_C of the channel whose dg_C this thread finishes in the tail (read now:
   // a load issued after the gradient stores would wait for them to drain)
@@ -626,8 +626,15 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       const float* y = reinterpret_cast<const float*>(&qs.ds.r[I]);
       gp[I] += (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
     });
-    if (qq + 2 < NQ) qload(qs, qq + 2);
     __syncthreads();
+    // the quarter after next, and in the last quarter phase B's inputs, issued once the
+    // barrier has passed (issued before it, they hold up the waves still storing)
+    if (qq + 2 < NQ) qload(qs, qq + 2);
+    if (qq + 1 == NQ) {
+      pk.load(kh, rk, len);
+      pq.load(qh, rk, len);
+      pl.load(lh, rk, len);
+    }
     const Frag<OP> fdo = frag_row<OP>(sDO, L::LSV, 16 * tw + r16, kq);
     const SFrag<OP> fdu = sfrag_pair<OP>(sDUh, sDUl, L::LSV, 16 * tw + r16, kq);
     const SFrag<OP> fu = sfrag_pair<OP>(sUh, sUl, L::LSV, 16 * tw + r16, kq);
@@ -663,9 +670,6 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       }
     }
   }
-  pk.load(kh, rk, len);
-  pq.load(qh, rk, len);
-  pl.load(lh, rk, len);
   __syncthreads();  // phase A's LDS reads are done; its region is reused below
 
   // ---- hand-over: dAqk, dW to LDS; partial sums; phase B inputs to LDS
@@ -720,6 +724,10 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   // cumulative sum of log_alpha over the chunk (per channel, NT / DK row parts); for
   // fp32 inputs in fp64 with one rounding of each g to fp32, as in the forward's prep
   constexpr int NSPLIT = NT / DK, RPS = CH / NSPLIT;
+  // each thread finishes the rows of its part and forms K+ = k e^g for them at once
+  auto put_kp = [&](int rr, int c, float g) __attribute__((always_inline)) {
+    sKp[rr * L::LDO + c] = cvt<OP>(kn(rr, c) * __expf(g));
+  };
   if constexpr (sizeof(E) == 4) {
     double* sTot = reinterpret_cast<double*>(sRed);
     const int c = tid % DK, s = tid / DK;
@@ -733,7 +741,9 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
 #pragma unroll
     for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
       acc += (double)sG[rr * L::LDG + c];
-      sG[rr * L::LDG + c] = (float)acc;
+      const float g = (float)acc;
+      sG[rr * L::LDG + c] = g;
+      put_kp(rr, c, g);
     }
   } else {
     {
@@ -752,13 +762,12 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       float off = 0.f;
       for (int s2 = 0; s2 < s; ++s2) off += sRed[s2 * DK + c];
 #pragma unroll
-      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) sG[rr * L::LDG + c] += off;
+      for (int rr = s * RPS; rr < (s + 1) * RPS; ++rr) {
+        const float g = sG[rr * L::LDG + c] + off;
+        sG[rr * L::LDG + c] = g;
+        put_kp(rr, c, g);
+      }
     }
-  }
-  __syncthreads();
-  for (int o = tid; o < CH * DK; o += NT) {
-    const int rr = o / DK, cc = o % DK;
-    sKp[rr * L::LDO + cc] = cvt<OP>(kn(rr, cc) * __expf(sG[rr * L::LDG + cc]));
   }
   __syncthreads();
 
