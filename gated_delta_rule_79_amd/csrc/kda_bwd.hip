@@ -204,12 +204,17 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   static_assert(NVO <= NT, "dO slice staging");
   Stage st0, st1;
   auto blk_of = [&](int n) { return (size_t)(c0 + n) * H + h; };
-  auto stage_load = [&](Stage& p, int n) __attribute__((always_inline)) {
+  // a chunk's operands -> registers, in two parts issued at different points of a step
+  // (the memory queue then never holds all of them ahead of the step's stores)
+  auto stage_load_a = [&](Stage& p, int n) __attribute__((always_inline)) {
     const size_t b = blk_of(n);
     p.aqk.load(gAqk + b * WB::AQK, CH);
     const OP* kb = reinterpret_cast<const OP*>(gKh + b * WB::KHF * sizeof(float));
     p.khh.load(kb, DK);
     if constexpr (L::SPLIT) p.khl.load(kb + CH * DK, DK);
+  };
+  auto stage_load = [&](Stage& p, int n) __attribute__((always_inline)) {
+    const size_t b = blk_of(n);
     p.qt.load(gQt + b * WB::QT, DK);
     p.w.load(gW + b * WB::W, DK);
     p.gam.load(gGam + b * WB::GAM, DK);
@@ -252,9 +257,9 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
       }
     }
     __syncthreads();
-    // chunk n - 2 -> registers, issued after this step's dS' stores: stores issued behind
-    // the loads would wait for them in the memory queue
-    stage_load(ld, max(n - 2, 0));
+    // chunk n - 2 -> registers, first part, issued after this step's dS' stores: stores
+    // issued behind the loads would wait for them in the memory queue
+    stage_load_a(ld, max(n - 2, 0));
 
     // dU = scale Aqk^T dO + Kh dS' : tiles (token tile tt, value tile nt) dealt to all eight waves
     constexpr int NDU = 4 * NTS, DPW = (NDU + 7) / 8;
@@ -295,6 +300,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
       }
     }
     __syncthreads();
+    stage_load(ld, max(n - 2, 0));   // second part, after this step's dU stores
     // dS = Gamma_C dS' + scale Qt^T dO - W^T dU
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
@@ -315,8 +321,10 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   };
 
   if (nch > 0) {
+    stage_load_a(st0, nch - 1);
     stage_load(st0, nch - 1);
     stage_store(st0);
+    stage_load_a(st1, max(nch - 2, 0));
     stage_load(st1, max(nch - 2, 0));
   }
   // chunks in reverse order; stage sets alternate so their registers stay static

@@ -1181,6 +1181,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   Stage st0;
   [[maybe_unused]] Stage st1;
   auto blk_of = [&](int n) { return (size_t)(c0 + n) * H + h; };
+  // a chunk's operands -> registers, in two parts issued at different points of a step
+  // (the memory queue then never holds all of them ahead of the step's stores)
+  auto stage_load_a = [&](Stage& p, int n) __attribute__((always_inline)) {
+    const size_t b = blk_of(n);
+    p.kht.load(gKhT + b * WB::KHT, CH);
+    if constexpr (KS) p.khtl.load(gKhTL + b * WB::KHT, CH);
+  };
   auto stage_load = [&](Stage& p, int n) __attribute__((always_inline)) {
     const size_t b = blk_of(n);
     p.w.load(gW + b * WB::W, DK);
@@ -1188,8 +1195,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       p.qt.load(gQt + b * WB::QT, DK);
       p.aqk.load(gAqk + b * WB::AQK, CH);
     }
-    p.kht.load(gKhT + b * WB::KHT, CH);
-    if constexpr (KS) p.khtl.load(gKhTL + b * WB::KHT, CH);
     if (!xf) p.ut.load(gUt + b * WB::UT + (size_t)n0 * CH, CH);  // UT == UTF element count
     p.gam.load(gGam + b * WB::GAM, DK);
   };
@@ -1225,6 +1230,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
       }
     }
     __syncthreads();
+    stage_load_a(ld, min(n + PF, nch - 1));   // first part, after this step's S stores
 
     f32x4 o1[NTS];
     if (w < 4) {
@@ -1255,8 +1261,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
                              [&](int rr, int k) { return frag_row<OP>(sST, L::LDK, 16 * nt + rr, k); }, zero4());
     }
     __syncthreads();
-    // chunk n + PF -> registers, issued after this step's S and U stores: stores issued
-    // behind the loads would wait for them in the memory queue
+    // second part, after this step's U stores: stores issued behind the loads would wait
+    // for them in the memory queue
     stage_load(ld, min(n + PF, nch - 1));
 
     if constexpr (OUT) {
@@ -1300,9 +1306,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   };
 
   if (nch > 0) {
+    stage_load_a(st0, 0);
     stage_load(st0, 0);
     stage_store(st0);
-    if constexpr (PF == 2) stage_load(st1, min(1, nch - 1));
+    if constexpr (PF == 2) {
+      stage_load_a(st1, min(1, nch - 1));
+      stage_load(st1, min(1, nch - 1));
+    }
   }
   if constexpr (PF == 2) {
     for (int n = 0; n < nch; n += 2) {
