@@ -670,12 +670,17 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       for (int k = 0; k < CH; k += 32)
         x = mma_ps(frag_row<OP>(sTT, L::LDT, 16 * tw + r16, k + kq),
                    sfrag_col_pair<OP>(sDUh, sDUl, L::LSV, 16 * hf + r16, k + kq), x);
+      f32x4 y;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * tw + 4 * q4 + ii, col = 16 * hf + r16;
         bv[ii] += f32(sV[r * L::LSV + col]) * x[ii];   // reduced over the column lanes after phase A
-        if (r < len) gdV[(size_t)r * rv + cq + col] = cvt<O>(gs_inv * (sBeta[r] * x[ii]));
+        y[ii] = gs_inv * (sBeta[r] * x[ii]);
       }
+      // dV after a quad transpose: row 16 tw + 4 q4 + (r16 & 3), 4 columns
+      y = quad_transpose(y);
+      const int rt = 16 * tw + 4 * q4 + (r16 & 3);
+      if (rt < len) store4<O>(gdV + (size_t)rt * rv + cq + 16 * hf + (r16 & ~3), y[0], y[1], y[2], y[3]);
     }
   }
   __syncthreads();  // phase A's LDS reads are done; its region is reused below
@@ -1045,6 +1050,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
     {
       khs[jj] = 0.f;
       const float gl = sG[(CH - 1) * L::LDG + cc];
+      f32x4 vq, vk;   // this lane's dq, dk tile values (rows 4 q4 + ii)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int rr = 16 * tw + 4 * q4 + ii;
@@ -1058,15 +1064,24 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
         dgv[jj][ii] = dq * qv + (dkp - dkmv - dkh) * kv;
         khs[jj] += dkh * kv;
         const float dkt = dkp + dkmv + dkh;
-        if constexpr (qk_norm) {   // gradients of the normalised rows; the chain rule follows below
-          wDQ[rr * DK + cc] = dq;
-          wDK[rr * DK + cc] = dkt;
+        vq[ii] = dq;
+        vk[ii] = dkt;
+        if constexpr (qk_norm) {
           qdot[ii] += qv * dq;
           kdot[ii] += kv * dkt;
-        } else if (rr < len) {
-          dqo[(size_t)rr * rk + cc] = cvt<O>(gs_inv * dq);
-          dko[(size_t)rr * rk + cc] = cvt<O>(gs_inv * dkt);
         }
+      }
+      // stores after a quad transpose: this lane holds row 16 tw + 4 q4 + (r16 & 3),
+      // columns cc - (r16 & 3) .. + 3
+      vq = quad_transpose(vq);
+      vk = quad_transpose(vk);
+      const int rt = 16 * tw + 4 * q4 + (r16 & 3), ct = cc - (r16 & 3);
+      if constexpr (qk_norm) {   // gradients of the normalised rows; the chain rule follows below
+        *reinterpret_cast<f32x4*>(wDQ + rt * DK + ct) = vq;
+        *reinterpret_cast<f32x4*>(wDK + rt * DK + ct) = vk;
+      } else if (rt < len) {
+        store4<O>(dqo + (size_t)rt * rk + ct, gs_inv * vq[0], gs_inv * vq[1], gs_inv * vq[2], gs_inv * vq[3]);
+        store4<O>(dko + (size_t)rt * rk + ct, gs_inv * vk[0], gs_inv * vk[1], gs_inv * vk[2], gs_inv * vk[3]);
       }
     }
     if (jj + 1 < NKH) {
