@@ -507,6 +507,45 @@ __device__ __forceinline__ f32x4 mm16_f32(const float* A, int lda, const float* 
   return c;
 }
 
+// The chunk's V rows ([64][DV] bf16, row pitch ld) for V^T in LDS: a thread loads rows
+// 2p and 2p + 1 of one 8-column piece and writes the eight (row 2p, row 2p + 1) pairs,
+// converted to the operand type, as 4-byte words at V^T[col][2p]; the 32 lanes of a
+// half-wave take the 32 row pairs of one piece, so their words fall in distinct banks.
+// Rows >= nrows are not read (row 0 is re-read) and are stored as zeros.
+template <int DV, int NT>
+struct VPairs {
+  static constexpr int NP = CH / 2, NI = NP * (DV / 8), PER = (NI + NT - 1) / NT;
+  u32x4 r0[PER], r1[PER];
+  __device__ __forceinline__ void load(const bf16* __restrict__ src, size_t ld, int nrows) {
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v0 = threadIdx.x + I * NT, v = (NI % NT == 0 || v0 < NI) ? v0 : 0;
+      const int p = v % NP, cp = v / NP;
+      const int ra = 2 * p < nrows ? 2 * p : 0, rb = 2 * p + 1 < nrows ? 2 * p + 1 : 0;
+      r0[I] = *reinterpret_cast<const u32x4*>(src + (size_t)ra * ld + 8 * cp);
+      r1[I] = *reinterpret_cast<const u32x4*>(src + (size_t)rb * ld + 8 * cp);
+    });
+  }
+  template <typename OP>
+  __device__ __forceinline__ void store_t(OP* dst, int dst_ld, int nrows) const {
+    static_assert(sizeof(OP) == 2, "pairs of 2-byte elements");
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = threadIdx.x + I * NT;
+      if (NI % NT == 0 || v < NI) {
+        const int p = v % NP, cp = v / NP;
+        const bool oka = 2 * p < nrows, okb = 2 * p + 1 < nrows;
+        const bf16* a = reinterpret_cast<const bf16*>(&r0[I]);
+        const bf16* b = reinterpret_cast<const bf16*>(&r1[I]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const OP x = cvt<OP>(oka ? f32(a[u]) : 0.f), y = cvt<OP>(okb ? f32(b[u]) : 0.f);
+          *reinterpret_cast<uint32_t*>(dst + (8 * cp + u) * dst_ld + 2 * p) =
+              (uint32_t)__builtin_bit_cast(unsigned short, x) | ((uint32_t)__builtin_bit_cast(unsigned short, y) << 16);
+        }
+      }
+    });
+  }
+};
+
 // GATE: log_alpha holds a raw gate x (KDA_FLAG_GATE_LOGSIGMOID).  Both options
 // are compile-time so the plain kernel keeps its register budget.
 // PATH 0: the usual chunk-heads; a chunk-head where some channel decays by more than
@@ -553,7 +592,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   const E* gb = reinterpret_cast<const E*>(a.beta);
 
   TileCopy<E, CH, DK, NT> pq, pk, pl;
-  TileCopy<E, CH, DV, NT> pv;
+  VPairs<DV, NT> pv;
   float pb = 0.f;
   auto fetch = [&](int item, const ChunkInfo& c) __attribute__((always_inline)) {
     const int h = item % H;
@@ -622,20 +661,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
       pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(logsigmoid(x)); });
     else
       pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(x); });
-    {
-      // V^T: each 16-byte piece is 8 value columns of one token
-      constexpr int VPR = DV / 8;
-      static_for<0, decltype(pv)::PER>([&](auto I) __attribute__((always_inline)) {
-        const int v = tid + I * NT;
-        if (decltype(pv)::NV % NT == 0 || v < decltype(pv)::NV) {
-          const int row = v / VPR, c0 = (v % VPR) * 8;
-          const E* e = reinterpret_cast<const E*>(&pv.r[I]);
-          const bool ok = row < len;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sVT[(c0 + i) * L::LDT + row] = cvt<OP>(ok ? f32(e[i]) : 0.f);
-        }
-      });
-    }
+    pv.template store_t<OP>(sVT, L::LDT, len);   // V^T
     if (tid < CH) sBeta[tid] = pb;
     const int nitem = advance(item + (int)gridDim.x);
     const ChunkInfo nci = nitem < n_items ? a.chunks[nitem / H] : ChunkInfo{0, 0, 0, 0};
