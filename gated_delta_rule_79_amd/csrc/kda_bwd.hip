@@ -105,12 +105,14 @@ struct RevLds {
   static constexpr int LDK = DK + P;
   static constexpr int LDT = CH + P;
   static constexpr bool SPLIT = sizeof(OP) == 2;
-  static constexpr size_t AQK = 0;                                          // OP    [CH][LDT]
+  // Aqk, Qt and W contract over tokens here, so they are staged transposed (token index
+  // contiguous): their MFMA operands are then 16-byte row reads
+  static constexpr size_t AQK = 0;                                          // OP    [CH][LDT]  Aqk^T
   static constexpr size_t KHH = AQK + (size_t)CH * LDT * sizeof(OP);        // OP    [CH][LDK]  Kh (hi)
   static constexpr size_t KHL = KHH + (size_t)CH * LDK * sizeof(OP);        // OP    [CH][LDK]  Kh (lo)
-  static constexpr size_t QT = KHL + (SPLIT ? (size_t)CH * LDK * sizeof(OP) : 0);  // OP [CH][LDK]
-  static constexpr size_t W = QT + (size_t)CH * LDK * sizeof(OP);           // OP    [CH][LDK]
-  static constexpr size_t GAM = W + (size_t)CH * LDK * sizeof(OP);          // float [DK]
+  static constexpr size_t QT = KHL + (SPLIT ? (size_t)CH * LDK * sizeof(OP) : 0);  // OP [DK][LDT]  Qt^T
+  static constexpr size_t W = QT + (size_t)DK * LDT * sizeof(OP);           // OP    [DK][LDT]  W^T
+  static constexpr size_t GAM = W + (size_t)DK * LDT * sizeof(OP);          // float [DK]
   static constexpr size_t DOT = GAM + (size_t)DK * 4;                       // OP    [DVS][LDT]  dO^T slice
   static constexpr size_t DSH = DOT + (size_t)DVS * LDT * sizeof(OP);       // OP    [DVS][LDK]  dS'^T split
   static constexpr size_t DSL = DSH + (size_t)DVS * LDK * sizeof(OP);
@@ -118,6 +120,53 @@ struct RevLds {
   static constexpr size_t DUL = DUH + (size_t)DVS * LDT * sizeof(OP);
   static constexpr size_t BYTES = DUL + (size_t)DVS * LDT * sizeof(OP);
   static_assert(BYTES <= 163840, "reverse pass LDS");
+};
+
+// Copy of a 64-row tile ([64][COLS], row pitch src_ld) into LDS transposed
+// ([COLS][dst_ld]).  Wide tiles of 2-byte elements: a thread loads rows 2p and 2p + 1
+// of one 8-column piece and writes the eight (row 2p, row 2p + 1) pairs as 4-byte words;
+// the 32 lanes of a half-wave take the 32 row pairs of one piece, so the words they
+// write fall in distinct banks.  Otherwise (4-byte elements, or too few pairs to give
+// every thread one) a thread loads one row of a piece and the lanes of a wave take 64
+// different rows.
+template <typename T, int COLS, int NT>
+struct TransTile {
+  static constexpr bool PAIR = sizeof(T) == 2 && (CH / 2) * (COLS / 8) >= NT;
+  static constexpr int EPV = 16 / (int)sizeof(T);            // elements per 16-byte piece
+  static constexpr int NP = PAIR ? CH / 2 : CH;              // row units (pairs or rows)
+  static constexpr int NI = NP * (COLS / EPV), PER = (NI + NT - 1) / NT;
+  u32x4 r0[PER], r1[PAIR ? PER : 1];
+  __device__ __forceinline__ void load(const T* __restrict__ src, size_t src_ld) {
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v0 = threadIdx.x + I * NT, v = (NI % NT == 0 || v0 < NI) ? v0 : 0;
+      const int p = v % NP, cp = v / NP;
+      if constexpr (PAIR) {
+        r0[I] = *reinterpret_cast<const u32x4*>(src + (size_t)(2 * p) * src_ld + EPV * cp);
+        r1[I] = *reinterpret_cast<const u32x4*>(src + (size_t)(2 * p + 1) * src_ld + EPV * cp);
+      } else {
+        r0[I] = *reinterpret_cast<const u32x4*>(src + (size_t)p * src_ld + EPV * cp);
+      }
+    });
+  }
+  __device__ __forceinline__ void store(T* dst, int dst_ld) const {
+    static_for<0, PER>([&](auto I) __attribute__((always_inline)) {
+      const int v = threadIdx.x + I * NT;
+      if (NI % NT == 0 || v < NI) {
+        const int p = v % NP, cp = v / NP;
+        if constexpr (PAIR) {
+          const unsigned short* a = reinterpret_cast<const unsigned short*>(&r0[I]);
+          const unsigned short* b = reinterpret_cast<const unsigned short*>(&r1[I]);
+#pragma unroll
+          for (int u = 0; u < EPV; ++u)
+            *reinterpret_cast<uint32_t*>(dst + (EPV * cp + u) * dst_ld + 2 * p) = (uint32_t)a[u] | ((uint32_t)b[u] << 16);
+        } else {
+          const T* a = reinterpret_cast<const T*>(&r0[I]);
+#pragma unroll
+          for (int u = 0; u < EPV; ++u) dst[(EPV * cp + u) * dst_ld + p] = a[u];
+        }
+      }
+    });
+  }
 };
 
 // LOCAL: a stretch's run from dS' = 0 for the segment scan; only the gradient
@@ -192,11 +241,11 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   // dO slice: 64 token rows x DVS columns of the input, rows past the chunk zeroed
   constexpr int EPV = 16 / (int)sizeof(E), VPR = DVS / EPV, NVO = CH * VPR;
   struct Stage {
-    TileCopy<OP, CH, CH, NT> aqk;
+    TransTile<OP, CH, NT> aqk;
     TileCopy<OP, CH, DK, NT> khh;
     TileCopy<OP, (L::SPLIT ? CH : 1), (L::SPLIT ? DK : 16 / sizeof(OP)), NT> khl;
-    TileCopy<OP, CH, DK, NT> qt;
-    TileCopy<OP, CH, DK, NT> w;
+    TransTile<OP, DK, NT> qt;
+    TransTile<OP, DK, NT> w;
     TileCopy<float, 1, DK, NT> gam;
     u32x4 dov;  // one 16-byte piece of the dO slice (threads < NVO)
     int dolen;
@@ -229,8 +278,8 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
     p.aqk.store(sAqk, L::LDT);
     p.khh.store(sKhH, L::LDK);
     if constexpr (L::SPLIT) p.khl.store(sKhL, L::LDK);
-    p.qt.store(sQt, L::LDK);
-    p.w.store(sW, L::LDK);
+    p.qt.store(sQt, L::LDT);
+    p.w.store(sW, L::LDT);
     p.gam.store(sGam, DK);
     if (tid < NVO) {
       const int row = tid / VPR, cv = tid % VPR;
@@ -270,7 +319,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
         f32x4 x1 = zero4(), x2 = zero4();
 #pragma unroll
         for (int k = 0; k < CH; k += 32)
-          x1 = mma(frag_col<OP>(sAqk, L::LDT, 16 * tt + r16, k + 8 * q4),
+          x1 = mma(frag_row<OP>(sAqk, L::LDT, 16 * tt + r16, k + 8 * q4),
                    frag_row<OP>(sDOT, L::LDT, 16 * nt + r16, k + 8 * q4), x1);
 #pragma unroll
         for (int k = 0; k < DK; k += 32)
@@ -295,7 +344,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
       if (t < NST) {
 #pragma unroll
         for (int k = 0; k < CH; k += 32)
-          qd[i] = mma(frag_col<OP>(sQt, L::LDK, 16 * mt + r16, k + 8 * q4),
+          qd[i] = mma(frag_row<OP>(sQt, L::LDT, 16 * mt + r16, k + 8 * q4),
                       frag_row<OP>(sDOT, L::LDT, 16 * nt + r16, k + 8 * q4), qd[i]);
       }
     }
@@ -309,7 +358,7 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
         f32x4 x = zero4();
 #pragma unroll
         for (int k = 0; k < CH; k += 32)
-          x = mma_ps(frag_col<OP>(sW, L::LDK, 16 * mt + r16, k + 8 * q4),
+          x = mma_ps(frag_row<OP>(sW, L::LDT, 16 * mt + r16, k + 8 * q4),
                      sfrag_pair<OP>(sDUh, sDUl, L::LDT, 16 * nt + r16, k + 8 * q4), x);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
