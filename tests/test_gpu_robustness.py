@@ -201,6 +201,42 @@ def test_upstream_gradient_scale(dtype, dk, scale):
 
 
 @pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64)])
+def test_zero_upstream_gradients(dtype, dk):
+    """d_out = 0 and d_final_state = 0 (the gradient-scale pre-pass sees a largest
+    magnitude of 0 and keeps s = 1): every gradient is exactly zero, as the backward is
+    linear in (d_out, d_final_state); a stray value would come from stale workspace."""
+    import torch
+    w = ki.small(dtype=dtype, lengths=(200, 77), H=2, dk=dk, dv=dk, seed=36)
+    inp = ki.make_inputs(w, with_grads=True)
+    inp["d_out"] = np.zeros_like(inp["d_out"])
+    inp["d_final_state"] = np.zeros_like(inp["d_final_state"])
+    g = to_gpu(inp, dtype)
+    grads = gpu_bwd(g)
+    torch.cuda.synchronize()
+    nonzero = {name: int(np.count_nonzero(np_of(a))) for name, a in zip(GRADS, grads)}
+    assert all(v == 0 for v in nonzero.values()), nonzero
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64)])
+def test_gradient_through_the_final_state_only(dtype, dk):
+    """d_out = 0 with a d_final_state scaled by 1e-5: the gradient-scale pre-pass takes its
+    scale from d_final_state alone, and every gradient stays within the bound."""
+    import torch
+    w = ki.small(dtype=dtype, lengths=(300, 129), H=2, dk=dk, dv=dk, seed=37)
+    inp = ki.make_inputs(w, with_grads=True)
+    inp["d_out"] = np.zeros_like(inp["d_out"])
+    inp["d_final_state"] = (inp["d_final_state"] * 1e-5).astype(np.float32)
+    g = to_gpu(inp, dtype)
+    grads = gpu_bwd(g)
+    torch.cuda.synchronize()
+    rg = oracle_bwd(inp)
+    errs = {name: rel_err(np_of(a)[0] if name != "d_init" else np_of(a), b) for name, a, b in zip(GRADS, grads, rg)}
+    print(f"final state only {dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, f"errors above {TOL[dtype]}: {bad}"
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64)])
 def test_forward_value_scale(dtype, dk):
     """v and init_state scaled by 1e3 (states far above unit scale)."""
     import torch
