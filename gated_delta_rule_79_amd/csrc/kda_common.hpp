@@ -48,6 +48,19 @@ struct ChunkInfo {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Small lists of 2-bit values packed into one 64-bit word: a lookup with a run-time
+// index is then a shift in registers.  (A constexpr array indexed at run time is
+// placed in global memory, and the wait for its load also waits for every vector
+// load and store the wave still has in flight.)
+template <int N>
+__host__ __device__ constexpr uint64_t pack2(const int (&v)[N]) {
+  static_assert(N <= 32, "at most 32 entries");
+  uint64_t p = 0;
+  for (int i = 0; i < N; ++i) p |= (uint64_t)(v[i] & 3) << (2 * i);
+  return p;
+}
+__device__ __forceinline__ int unpack2(uint64_t p, int i) { return (int)((p >> (2 * i)) & 3); }
+
 __device__ __forceinline__ float f32(float x) { return x; }
 __device__ __forceinline__ float f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float f32(f16 x) { return (float)x; }

@@ -593,7 +593,10 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
 
   TileCopy<E, CH, DK, NT> pq, pk, pl;
   VPairs<DV, NT> pv;
-  float pb = 0.f;
+  E pb = E(0.f);
+  // The loads are issued without a branch and their values are not touched until the
+  // next item is staged: a value used at once (or a load inside a branch) makes the
+  // wave wait for every load and store it still has in flight.
   auto fetch = [&](int item, const ChunkInfo& c) __attribute__((always_inline)) {
     const int h = item % H;
     const size_t t0 = (size_t)c.t0;
@@ -601,7 +604,26 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
     pk.load(gk + t0 * rk + (size_t)h * DK, rk, c.len);
     pl.load(gl + t0 * rk + (size_t)h * DK, rk, c.len);
     pv.load(gv + t0 * rv + (size_t)h * DV, rv, c.len);
-    pb = tid < c.len ? f32(gb[(t0 + tid) * H + h]) : 0.f;
+    pb = gb[(t0 + (size_t)min(tid % CH, c.len - 1)) * H + h];   // rows past len: zeroed when staged
+  };
+  // The chunk record (t0, len) of each item is read one item before its inputs, through
+  // a lane-varying offset that is always zero, so it stays in vector registers until the
+  // fetch makes scalars of it (a uniform load is moved to scalar registers at once, and
+  // that move waits for every load and store in flight).  Slot 0 always exists.
+  struct Rec {
+    int t0, len;
+    bool valid;
+  };
+  auto record = [&](int it) __attribute__((always_inline)) {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    const bool valid = it < n_items;
+    const ChunkInfo* c = a.chunks + (valid ? it / H : 0) + z;
+    return Rec{c->t0, c->len, valid};
+  };
+  auto chunk_of = [&](const Rec& r) __attribute__((always_inline)) {
+    return r.valid ? ChunkInfo{0, __builtin_amdgcn_readfirstlane(r.t0), __builtin_amdgcn_readfirstlane(r.len), 0}
+                   : ChunkInfo{0, 0, 0, 0};
   };
 
   // PATH 1 walks only the flagged items (the slots past the last chunk, never flagged
@@ -630,8 +652,10 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
     return it;
   };
   int item = advance((int)blockIdx.x);
-  ChunkInfo ci = item < n_items ? a.chunks[item / H] : ChunkInfo{0, 0, 0, 0};
+  ChunkInfo ci = chunk_of(record(item));
   if (ci.len > 0) fetch(item, ci);
+  int nitem = ci.len > 0 ? advance(item + (int)gridDim.x) : n_items;
+  Rec nrec = record(nitem);
   while (ci.len > 0) {   // the same value in every thread
     const size_t blk = (size_t)item;   // == chunk * H + head
     const int len = ci.len;
@@ -662,10 +686,11 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
     else
       pl.template store_map<float>(sG, L::LDG, len, [](float x) { return floor_log_alpha(x); });
     pv.template store_t<OP>(sVT, L::LDT, len);   // V^T
-    if (tid < CH) sBeta[tid] = pb;
-    const int nitem = advance(item + (int)gridDim.x);
-    const ChunkInfo nci = nitem < n_items ? a.chunks[nitem / H] : ChunkInfo{0, 0, 0, 0};
+    if (tid < CH) sBeta[tid] = tid < len ? f32(pb) : 0.f;
+    const ChunkInfo nci = chunk_of(nrec);
     if (nci.len > 0) fetch(nitem, nci);
+    const int n2item = nci.len > 0 ? advance(nitem + (int)gridDim.x) : n_items;
+    const Rec n2rec = record(n2item);
     __syncthreads();
 
     // ---- cumulative sum of log_alpha over the chunk (per channel, NT / DK row parts)
@@ -764,9 +789,10 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
         float* tKR = reinterpret_cast<float*>(smem + L::GKR);
         float* tF = reinterpret_cast<float*>(smem + L::GF);
         // this wave's blocks: list index w and w + 8 of (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-        constexpr int BA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-        constexpr int BB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-        const int nblk = w < 2 ? 2 : 1;
+        constexpr uint64_t BA = pack2({0, 1, 1, 2, 2, 2, 3, 3, 3, 3});
+        constexpr uint64_t BB = pack2({0, 0, 1, 0, 1, 2, 0, 1, 2, 3});
+        const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform, so the block choice is scalar
+        const int nblk = wu < 2 ? 2 : 1;
         f32x4 akk[2] = {zero4(), zero4()}, aqk[2] = {zero4(), zero4()};
         static_assert(NT == CH * (GC / 4), "table build: one thread per (token, 4 channels)");
         for (int ps = 0; ps < NPASS; ++ps) {
@@ -797,7 +823,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   #pragma unroll
           for (int j = 0; j < 2; ++j) {
             if (j < nblk) {
-              const int li = w + 8 * j, ba = BA[li], bb = BB[li];
+              const int li = wu + 8 * j, ba = unpack2(BA, li), bb = unpack2(BB, li);
               const SFrag<bf16> fk = sfrag_pair<bf16>(tKh, tKl, L::LDQ, 16 * ba + r16, 8 * q4);
               const SFrag<bf16> fq = sfrag_pair<bf16>(tQh, tQl, L::LDQ, 16 * ba + r16, 8 * q4);
               const f32x4 v0 = *reinterpret_cast<const f32x4*>(tKR + (16 * bb + r16) * L::LDR + 8 * q4);
@@ -827,7 +853,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (j < nblk) {
-            const int li = w + 8 * j, ba = BA[li], bb = BB[li];
+            const int li = wu + 8 * j, ba = unpack2(BA, li), bb = unpack2(BB, li);
   #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
               const int rr = 16 * ba + 4 * q4 + ii, cc = 16 * bb + r16;
@@ -868,10 +894,11 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
         float* tKR = reinterpret_cast<float*>(smem + L::GKR);
         float* tF = reinterpret_cast<float*>(smem + L::GF);
         // tile halves (a, b, h): list index w, w + 8, w + 16 for wave w
-        constexpr int HA[20] = {0, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3, 3, 3, 3, 3, 0, 1, 2, 3};
-        constexpr int HB[20] = {0, 0, 1, 0, 0, 1, 2, 0, 1, 0, 1, 2, 3, 0, 1, 2, 0, 1, 2, 3};
-        constexpr int HH[20] = {1, 0, 1, 1, 0, 0, 1, 1, 1, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0};
-        const int nitem = w < 4 ? 3 : 2;
+        constexpr uint64_t HA = pack2({0, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3, 3, 3, 3, 3, 0, 1, 2, 3});
+        constexpr uint64_t HB = pack2({0, 0, 1, 0, 0, 1, 2, 0, 1, 0, 1, 2, 3, 0, 1, 2, 0, 1, 2, 3});
+        constexpr uint64_t HH = pack2({1, 0, 1, 1, 0, 0, 1, 1, 1, 0, 0, 0, 1, 1, 1, 1, 0, 0, 0, 0});
+        const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform, so the tile choice is scalar
+        const int nitem = wu < 4 ? 3 : 2;
         f32x4 akk[3] = {zero4(), zero4(), zero4()}, aqk[3] = {zero4(), zero4(), zero4()};
         static_assert(NT == CH * (GC / 4), "table build: one thread per (token, 4 channels)");
         for (int ps = 0; ps < NPASS; ++ps) {
@@ -901,7 +928,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   #pragma unroll
           for (int j = 0; j < 3; ++j) {
             if (j < nitem) {
-              const int li = w + 8 * j, ba = HA[li], bb = HB[li], R = 2 * ba + HH[li];
+              const int li = wu + 8 * j, ba = unpack2(HA, li), bb = unpack2(HB, li), R = 2 * ba + unpack2(HH, li);
               const int C = 2 * bb + (r16 >> 3);   // group of this lane's column
               const SFrag<bf16> fk = sfrag_pair<bf16>(tKh, tKl, L::LDQ, 16 * ba + r16, 8 * q4);
               const SFrag<bf16> fq = sfrag_pair<bf16>(tQh, tQl, L::LDQ, 16 * ba + r16, 8 * q4);
@@ -941,7 +968,7 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
   #pragma unroll
         for (int j = 0; j < 3; ++j) {
           if (j < nitem) {
-            const int li = w + 8 * j, ba = HA[li], bb = HB[li], hh = HH[li];
+            const int li = wu + 8 * j, ba = unpack2(HA, li), bb = unpack2(HB, li), hh = unpack2(HH, li);
             if ((q4 >> 1) == hh) {   // this lane's rows 4q4 .. 4q4 + 3 of the tile are in row group 2a + hh
   #pragma unroll
               for (int ii = 0; ii < 4; ++ii) {
@@ -1069,6 +1096,8 @@ __global__ __launch_bounds__(512) void kda_prep8(const Args a) {
     }   // !skip
     item = nitem;
     ci = nci;
+    nitem = n2item;
+    nrec = n2rec;
   }
 }
 
