@@ -226,16 +226,21 @@ __global__ __launch_bounds__(512) void kda_state_rev(const Args a) {
   const float gs_fin = a.dfinal_scaled ? 1.f : gs;
   const float gs_inv = (a.gscale && !LOCAL) ? a.gscale[1] : 1.f;
 
+  // every load is issued before the first use (a use between them would wait for each in turn)
   f32x4 dS[SPW];
   const size_t st_off = ((size_t)seq * H + h) * DK * DV;
+  if (gDFin) {
 #pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int t = w + 8 * i, mt = t % MTS, nt = t / MTS;
+    for (int i = 0; i < SPW; ++i) {
+      const int t = min(w + 8 * i, NST - 1), mt = t % MTS, nt = t / MTS;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int ch = 16 * mt + 4 * q4 + ii, col = n0 + 16 * nt + r16;
-      dS[i][ii] = (gDFin && t < NST) ? gs_fin * gDFin[st_off + (size_t)ch * DV + col] : 0.f;
+      for (int ii = 0; ii < 4; ++ii) dS[i][ii] = gDFin[st_off + (size_t)(16 * mt + 4 * q4 + ii) * DV + n0 + 16 * nt + r16];
     }
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) dS[i] = w + 8 * i < NST ? dS[i] * gs_fin : zero4();
+  } else {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) dS[i] = zero4();
   }
 
   // dO slice: 64 token rows x DVS columns of the input, rows past the chunk zeroed
