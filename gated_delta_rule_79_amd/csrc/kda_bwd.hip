@@ -616,10 +616,12 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
   // phase B's inputs (q, k, log_alpha rows), loaded during the last value quarter
   TileCopy<E, CH, DK, NT> pk, pq, pl;
   // Gamma_C of the channel whose dg_C this thread finishes in the tail (read now:
-  // a load issued after the gradient stores would wait for them to drain)
-  const float gam_c = (tid >= 64 && tid < 64 + DK) ? a.wsGam[blk * WB::GAM + tid - 64] : 0.f;
-  // beta of row tid, issued ahead of the tile loads so that waiting for it does not wait for them
-  const float beta_t = (tid < CH && tid < len) ? f32(bh[(size_t)tid * H]) : 0.f;
+  // a load issued after the gradient stores would wait for them to drain), and beta
+  // of row tid.  Both are issued ahead of the tile loads, without a branch, and not
+  // touched until used, so no wait for them holds up the loads behind them.
+  const float gam_c = a.wsGam[blk * WB::GAM + min(max(tid - 64, 0), DK - 1)];   // used by threads 64 .. 64 + DK - 1
+  const E beta_raw = bh[(size_t)min(tid % CH, len - 1) * H];                    // rows past the chunk: zeroed when staged
+  __builtin_amdgcn_sched_barrier(0);   // keep the two loads ahead of the tile loads
 
   // ---- phase A staging: contractions over the value dimension, a quarter of the columns at a time
   struct QStage {
@@ -656,7 +658,7 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk(const Args a) {
       }
     });
   }
-  if (tid < CH) sBeta[tid] = beta_t;
+  if (tid < CH) sBeta[tid] = tid < len ? f32(beta_raw) : 0.f;
 
   // ---- phase A
   f32x4 accA[2], accT[2], accQ[NKH], accK[NKH], accW[NKH];
