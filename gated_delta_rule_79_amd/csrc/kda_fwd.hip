@@ -1325,15 +1325,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
         const int tt = w - 4;
         const int t0 = tbeg + n * CH, clen = min(CH, tend - t0);
         O* oh = gOut + (size_t)t0 * ro + (size_t)h * DV + n0;
+        // all tiles' products first, then one guarded group of stores: a guard per tile
+        // would end a basic block after each tile and serialise their latencies
+        f32x4 y[NTS];
 #pragma unroll
-        for (int nt = 0; nt < NTS; ++nt) {
-          const f32x4 x =
-              tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sAqk, L::LDT, 16 * tt + rr, k); },
-                          [&](int rr, int k) { return frag_row<OP>(sUL, L::LDT, 16 * nt + rr, k); }, o1[nt]);
-          // quad transpose: this lane stores 4 columns of token 16 tt + 4 q4 + (r16 & 3)
-          const f32x4 y = quad_transpose(scale * x);
-          const int tok = 16 * tt + 4 * q4 + (r16 & 3);
-          if (tok < clen) store4<O>(oh + (size_t)tok * ro + 16 * nt + (r16 & ~3), y[0], y[1], y[2], y[3]);
+        for (int nt = 0; nt < NTS; ++nt)
+          y[nt] = tile_mm<CH>([&](int rr, int k) { return frag_row<OP>(sAqk, L::LDT, 16 * tt + rr, k); },
+                              [&](int rr, int k) { return frag_row<OP>(sUL, L::LDT, 16 * nt + rr, k); }, o1[nt]);
+        // quad transpose: this lane stores 4 columns of token 16 tt + 4 q4 + (r16 & 3)
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) y[nt] = quad_transpose(scale * y[nt]);
+        const int tok = 16 * tt + 4 * q4 + (r16 & 3);
+        if (tok < clen) {
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt)
+            store4<O>(oh + (size_t)tok * ro + 16 * nt + (r16 & ~3), y[nt][0], y[nt][1], y[nt][2], y[nt][3]);
         }
       }
     }
