@@ -1166,6 +1166,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 4
   const int seq = a.seq_order[unit / a.H], h = unit % a.H, H = a.H;   // longest sequences first
   const int n0 = sl * DVS;
   const int l = lane_id(), w = wave_id(), r16 = l & 15, q4 = l >> 4;
+  __builtin_assume(w < 8);   // 512 threads: every state tile t = w + 8 i < NST is then known in range
   const int c0 = a.seq_chunk0[seq], nch = a.seq_chunk0[seq + 1] - c0;
   // token range of the sequence, from its first and last chunk (read once, so
   // the only global loads inside the loop are the prefetch of the next chunk)
